@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of one block-sparse global-attention layer on one MI355X.
+
+A step is the whole hot path on one batch of resident synthetic input:
+pooled top-k block selection (mean-pool Q and K per block, pooled scores,
+per-frame special-token blocks forced, CSR emission) followed by the
+block-sparse flash-attention forward over the selected blocks. The workload is
+the 32-frame layer: 32 x 1408 padded tokens (1374 real), 16 heads, head_dim 64,
+bf16, blocks of 128, 75 % block sparsity.
+
+Prints one JSON line (see the keys below). `value` is the layer-effective
+throughput: algorithmic FLOP of the executed blocks (4 * 128^2 * 64 per
+executed block pair) divided by the measured time of the whole step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_vggt_layer_32f_s75_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_global_mean_amd", "csrc", "attn_bf16.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def cpu_baseline(w, data, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same layer: head by
+    head, pooled scores and top-k selection, then block-sparse attention per
+    query block, until about `budget_s` seconds have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lay = w.layout
+    keep = data["keep"]
+    forced = oracle.forced_blocks(lay, w.force_frame_first_block)
+    t0 = time.perf_counter()
+    pairs = rows = heads = 0
+    for h in range(lay.heads):
+        q, k, v = data["q"][:, h:h + 1], data["k"][:, h:h + 1], data["v"][:, h:h + 1]
+        qbar, kbar = oracle.pool(q, lay), oracle.pool(k, lay)
+        s = oracle.pooled_scores(qbar, kbar, lay.scale)[0, 0]
+        heads += 1
+        for i in range(lay.nblocks):
+            kept = oracle.select_topk_row(s[i], int(keep[h]), forced)
+            oracle.sparse_attention_row(q[0, 0], k[0, 0], v[0, 0], lay, i, kept)
+            pairs += len(kept)
+            rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = pairs * 4.0 * lay.block ** 2 * lay.head_dim
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"the 32-frame layer, head by head until the time budget: pooling and "
+                      f"pooled scores of {heads} head(s), then top-k selection + float64 "
+                      f"block-sparse attention for {rows} query blocks ({pairs} executed "
+                      f"block pairs, {flops / 1e9:.1f} GFLOP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, copy this many MiB once (counter calibration)")
+    ap.add_argument("--no-drift", action="store_true", help="skip the drift-layer side measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import block_sparse_global_mean_amd as bsgm
+    import workloads
+
+    dev = torch.device("cuda:0")
+    bsgm.library()
+    w = workloads.config("vggt_layer_32f_s75")
+    lay = w.layout
+    log(f"generating {w.name}")
+    data = workloads.generate(w)
+    q, k, v = (to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
+    keep = data["keep"]
+    nb, rows = lay.nblocks, lay.batch * lay.heads * lay.nblocks
+    cap = bsgm.col_capacity(lay, bsgm.TOPK, keep, force=True)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    ws = torch.empty(bsgm.workspace_bytes(lay, bsgm.TOPK), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def select():
+        bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=True, row_ptr=row_ptr,
+                           col_idx=col_idx, workspace=ws, want_stat=False)
+
+    def attend():
+        bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        select()
+        attend()
+    torch.cuda.synchronize()
+    executed = int(row_ptr[-1].item())
+    flops = executed * 4.0 * lay.block ** 2 * lay.head_dim
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_all[0].record(stream)
+    for s in range(K):
+        ev[s][0].record(stream)
+        select()
+        ev[s][1].record(stream)
+        attend()
+        ev[s][2].record(stream)
+    ev_all[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev_all[0].elapsed_time(ev_all[1])
+    sel_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]
+    att_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]
+    ms_per_step = max(total_ms, wall * 1e3) / K
+    attn_avg = float(np.mean(att_ms))
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms (select {np.mean(sel_ms):.3f}, attention {attn_avg:.3f})")
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+
+    traffic = traffic_per_launch()
+    detail = {
+        "select_ms": round(float(np.mean(sel_ms)), 4),
+        "attn_ms": round(attn_avg, 4),
+        "attn_ms_min": round(float(np.min(att_ms)), 4),
+        "executed_block_pairs": executed,
+        "measured_block_sparsity": round(1.0 - executed / (rows * nb), 6),
+        "executed_gflop": round(flops / 1e9, 3),
+        "attn_effective_tflops": round(achieved, 2),
+        "device": torch.cuda.get_device_name(0),
+    }
+
+    if not args.no_drift:
+        detail["drift_layer_16f"] = drift_side(bsgm, workloads, torch, dev)
+
+    out = {
+        "metric": "block-sparse global attn effective TFLOP/s + ms/layer, 32 frames, 75% sparse",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "vggt_layer_32f_s75: 32 frames x 1408 tokens (1374 real), "
+                               "16 heads, head_dim 64, block 128, top-88 of 352 key blocks "
+                               "per query block with 32 forced special-token blocks",
+                   "batch": lay.batch, "heads": lay.heads, "tokens": lay.tokens,
+                   "block": lay.block, "keep_per_query_block": int(keep[0])},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, data, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def drift_side(bsgm, workloads, torch, dev, steps=5):
+    """Side measurement: the 16-frame drift layer (drift scores + 3 swap rounds +
+    attention), not part of `value`."""
+    w = workloads.config("vggt_layer_16f_drift")
+    lay = w.layout
+    log(f"generating {w.name}")
+    data = workloads.generate(w)
+    q, k, v = (to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
+    keep = data["keep"]
+    nb, rows = lay.nblocks, lay.heads * lay.nblocks
+    contrib = torch.empty((1, lay.heads, nb, nb, 64), dtype=torch.float32, device=dev)
+    score = torch.empty((1, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsgm.workspace_bytes(lay, bsgm.DRIFT), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(bsgm.col_capacity(lay, bsgm.DRIFT, keep), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws)
+        e1.record(stream)
+        bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=w.swap_rounds,
+                           row_ptr=row_ptr, col_idx=col_idx, want_stat=False)
+        e2.record(stream)
+        bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o)
+
+    e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    step()
+    torch.cuda.synchronize()
+    t = np.zeros(3)
+    for _ in range(steps):
+        e0.record(stream)
+        step()
+        e3.record(stream)
+        torch.cuda.synchronize()
+        t += [e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3)]
+    t /= steps
+    executed = int(row_ptr[-1].item())
+    flops = executed * 4.0 * lay.block ** 2 * lay.head_dim
+    return {"drift_scores_ms": round(t[0], 4), "drift_select_ms": round(t[1], 4),
+            "attn_ms": round(t[2], 4), "ms_per_layer": round(float(t.sum()), 4),
+            "layer_effective_tflops": round(flops / (t.sum() * 1e-3) / 1e12, 2),
+            "attn_effective_tflops": round(flops / (t[2] * 1e-3) / 1e12, 2)}
+
+
+if __name__ == "__main__":
+    main()

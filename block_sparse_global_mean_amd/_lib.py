@@ -1,0 +1,230 @@
+"""ctypes binding of the bsgm C ABI (include/bsgm.h).
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+libbsgm.so. PyTorch supplies device memory and the current stream. If the
+library is missing, every entry point raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsgm.so")
+
+F32, BF16 = 0, 1
+TOPK, CDF, DRIFT = 0, 1, 2
+
+STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_CAPACITY",
+          -4: "BSGM_E_WORKSPACE", -5: "BSGM_E_HIP"}
+
+# Every symbol include/bsgm.h declares.
+EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_capacity",
+           "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd")
+
+
+class BsgmError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("frames", ctypes.c_int32), ("frame_len", ctypes.c_int32),
+                ("frame_valid", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class CSelectParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("keep_per_head", ctypes.POINTER(ctypes.c_int32)),
+                ("cdf_tau", ctypes.c_float), ("force_frame_first_block", ctypes.c_int32),
+                ("swap_rounds", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Loads libbsgm.so (built in-tree); raises if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_global_mean_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lp, pp = ctypes.POINTER(CLayout), ctypes.POINTER(CSelectParams)
+        lib.bsgm_version.restype = ctypes.c_int32
+        lib.bsgm_last_error.restype = ctypes.c_char_p
+        lib.bsgm_workspace_bytes.argtypes = [lp, ctypes.c_int32]
+        lib.bsgm_workspace_bytes.restype = sz
+        lib.bsgm_col_capacity.argtypes = [lp, pp]
+        lib.bsgm_col_capacity.restype = ctypes.c_int64
+        lib.bsgm_pool_blocks.argtypes = [lp, vp, vp, vp]
+        lib.bsgm_drift_scores.argtypes = [lp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
+                                           vp, sz, vp]
+        lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp]
+        for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
+                     "bsgm_sparse_attn_fwd"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def c_layout(layout) -> CLayout:
+    """Any object with batch, heads, head_dim, frames, frame_len, frame_valid,
+    block, dtype ('f32' / 'bf16' or 0 / 1) and scale."""
+    dt = layout.dtype
+    if isinstance(dt, str):
+        dt = {"f32": F32, "bf16": BF16}[dt]
+    return CLayout(layout.batch, layout.heads, layout.head_dim, layout.frames, layout.frame_len,
+                   layout.frame_valid, layout.block, dt, layout.scale)
+
+
+def c_params(mode: int, keep: Sequence[int], cdf_tau: float = 0.9, force: bool = False,
+             swap_rounds: int = 0) -> Tuple[CSelectParams, ctypes.Array]:
+    arr = (ctypes.c_int32 * len(keep))(*[int(x) for x in keep])
+    return CSelectParams(mode, arr, cdf_tau, 1 if force else 0, swap_rounds), arr
+
+
+def _check(code: int):
+    if code != 0:
+        raise BsgmError(code, library().bsgm_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+def _dims(layout):
+    n = layout.frames * layout.frame_len
+    nb = n // layout.block
+    return n, nb, layout.batch * layout.heads * nb
+
+
+def _tdtype(layout) -> torch.dtype:
+    return torch.bfloat16 if c_layout(layout).dtype == BF16 else torch.float32
+
+
+def version() -> int:
+    return library().bsgm_version()
+
+
+def workspace_bytes(layout, mode: int) -> int:
+    L = c_layout(layout)
+    n = library().bsgm_workspace_bytes(ctypes.byref(L), mode)
+    if n == 0:
+        raise BsgmError(-1, library().bsgm_last_error().decode())
+    return n
+
+
+def col_capacity(layout, mode: int, keep: Sequence[int], force: bool = False) -> int:
+    L = c_layout(layout)
+    P, _keep = c_params(mode, keep, force=force)
+    n = library().bsgm_col_capacity(ctypes.byref(L), ctypes.byref(P))
+    if n < 0:
+        raise BsgmError(-1, library().bsgm_last_error().decode())
+    return n
+
+
+def pool_blocks(layout, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """Block means of x over real tokens -> float32 [B,H,Nb,64]."""
+    n, nb, _ = _dims(layout)
+    _expect(x, "x", _tdtype(layout), (layout.batch, layout.heads, n, layout.head_dim))
+    if out is None:
+        out = torch.empty((layout.batch, layout.heads, nb, layout.head_dim), dtype=torch.float32,
+                          device=x.device)
+    L = c_layout(layout)
+    _check(library().bsgm_pool_blocks(ctypes.byref(L), _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stream=None):
+    """Drift contributions [B,H,Nb,Nb,64] and their norms [B,H,Nb,Nb] (float32)."""
+    n, nb, _ = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, _tdtype(layout), shape)
+    dev = q.device
+    if contrib is None:
+        contrib = torch.empty((layout.batch, layout.heads, nb, nb, layout.head_dim),
+                              dtype=torch.float32, device=dev)
+    if score is None:
+        score = torch.empty((layout.batch, layout.heads, nb, nb), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(layout, DRIFT), dtype=torch.uint8, device=dev)
+    L = c_layout(layout)
+    _check(library().bsgm_drift_scores(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), _ptr(contrib),
+                                       _ptr(score), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+    return contrib, score
+
+
+def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contrib=None,
+                  cdf_tau: float = 0.9, force: bool = False, swap_rounds: int = 0,
+                  row_ptr=None, col_idx=None, row_stat=None, scores_out=None, swap_log=None,
+                  workspace=None, want_stat: bool = True, stream=None):
+    """Selected key blocks as CSR (row_ptr, col_idx) plus the per-row statistic."""
+    n, nb, rows = _dims(layout)
+    dev = (q if q is not None else contrib).device
+    if mode in (TOPK, CDF):
+        shape = (layout.batch, layout.heads, n, layout.head_dim)
+        _expect(q, "q", _tdtype(layout), shape)
+        _expect(k, "k", _tdtype(layout), shape)
+    else:
+        _expect(contrib, "contrib", torch.float32,
+                (layout.batch, layout.heads, nb, nb, layout.head_dim))
+    cap = col_capacity(layout, mode, keep, force)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_stat is None and want_stat:
+        row_stat = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None and mode != DRIFT:
+        workspace = torch.empty(workspace_bytes(layout, mode), dtype=torch.uint8, device=dev)
+    L = c_layout(layout)
+    P, _keep = c_params(mode, keep, cdf_tau, force, swap_rounds)
+    _check(library().bsgm_select_blocks(
+        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(row_ptr),
+        _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return row_ptr, col_idx, row_stat
+
+
+def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_lse=False,
+                    stream=None):
+    """Block-sparse attention forward; returns (o, lse or None)."""
+    n, nb, rows = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, _tdtype(layout), shape)
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32 or row_ptr.numel() != rows + 1:
+        raise ValueError("row_ptr must be int32 [rows+1] and col_idx int32")
+    if o is None:
+        o = torch.empty(shape, dtype=_tdtype(layout), device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((layout.batch, layout.heads, n), dtype=torch.float32, device=q.device)
+    L = c_layout(layout)
+    _check(library().bsgm_sparse_attn_fwd(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
+                                          _stream(stream)))
+    return o, lse

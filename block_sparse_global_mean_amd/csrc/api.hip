@@ -1,0 +1,263 @@
+// C-ABI host layer: argument validation, workspace layout, dispatch to the
+// kernel launchers. Everything is enqueued on the caller's stream; nothing is
+// allocated and nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/bsgm.h"
+#include "internal.h"
+
+namespace bsgm {
+size_t drift_select_lds_bytes(int nb);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return BSGM_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(BSGM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Validates a layout and fills the kernel view. Returns BSGM_OK or an error.
+int check_layout(const bsgm_layout* L, bsgm::Dims* d) {
+  if (!L) return fail(BSGM_E_ARG, "layout is NULL");
+  if (L->batch < 1 || L->heads < 1 || L->frames < 1 || L->frame_len < 1)
+    return fail(BSGM_E_ARG, "batch, heads, frames and frame_len must be >= 1");
+  if (L->frame_valid < 1 || L->frame_valid > L->frame_len)
+    return fail(BSGM_E_ARG, "frame_valid must be in [1, frame_len]");
+  if (!(std::isfinite(L->scale) && L->scale > 0.f))
+    return fail(BSGM_E_ARG, "scale must be finite and > 0");
+  if (L->dtype != BSGM_F32 && L->dtype != BSGM_BF16)
+    return fail(BSGM_E_ARG, "dtype must be BSGM_F32 or BSGM_BF16");
+  if (L->head_dim != 64) return fail(BSGM_E_UNSUPPORTED, "head_dim must be 64 (got %d)", L->head_dim);
+  if (L->block != 64 && L->block != 128)
+    return fail(BSGM_E_UNSUPPORTED, "block must be 64 or 128 (got %d)", L->block);
+  if (L->frame_len % L->block != 0)
+    return fail(BSGM_E_UNSUPPORTED, "frame_len (%d) must be a multiple of block (%d)", L->frame_len,
+                L->block);
+  if (L->frame_len - L->frame_valid >= L->block)
+    return fail(BSGM_E_UNSUPPORTED,
+                "padding per frame (%d) must be shorter than a block (%d): no empty blocks",
+                L->frame_len - L->frame_valid, L->block);
+  if (L->heads > bsgm::kMaxHeads)
+    return fail(BSGM_E_UNSUPPORTED, "heads must be <= %d", bsgm::kMaxHeads);
+  const long long N = (long long)L->frames * L->frame_len;
+  const long long nb = N / L->block;
+  const long long rows = (long long)L->batch * L->heads * nb;
+  if (N > (1LL << 30) || rows >= (1LL << 31) - 1)
+    return fail(BSGM_E_UNSUPPORTED, "layout too large (tokens %lld, rows %lld)", N, rows);
+  d->B = L->batch;
+  d->H = L->heads;
+  d->D = L->head_dim;
+  d->F = L->frames;
+  d->L = L->frame_len;
+  d->Lv = L->frame_valid;
+  d->blk = L->block;
+  d->N = (int)N;
+  d->nb = (int)nb;
+  d->rows = (int)rows;
+  d->scale = L->scale;
+  return BSGM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t qbar, kbar, counts, bitmask, total;
+};
+
+WsLayout ws_layout(const bsgm::Dims& d, int mode) {
+  WsLayout w{};
+  const size_t pooled = (size_t)d.rows * 64 * sizeof(float);
+  size_t off = 0;
+  w.qbar = off;
+  off += align256(pooled);
+  if (mode == BSGM_SEL_TOPK || mode == BSGM_SEL_CDF) {
+    w.kbar = off;
+    off += align256(pooled);
+  }
+  if (mode == BSGM_SEL_CDF) {
+    w.counts = off;
+    off += align256((size_t)d.rows * sizeof(int32_t));
+    w.bitmask = off;
+    off += align256((size_t)d.rows * ((d.nb + 31) / 32) * sizeof(uint32_t));
+  }
+  w.total = off;
+  return w;
+}
+
+// Checks the per-head budgets and fills the closed-form CSR offsets.
+int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBudget* hb) {
+  if (!P) return fail(BSGM_E_ARG, "params is NULL");
+  if (!P->keep_per_head) return fail(BSGM_E_ARG, "keep_per_head is NULL");
+  const int nforced = P->force_frame_first_block ? d.F : 0;
+  long long off = 0;
+  for (int h = 0; h < d.H; ++h) {
+    const int k = P->keep_per_head[h];
+    if (k < 1 || k > d.nb)
+      return fail(BSGM_E_ARG, "keep_per_head[%d] = %d outside [1, %d]", h, k, d.nb);
+    if (k < nforced)
+      return fail(BSGM_E_ARG, "keep_per_head[%d] = %d is below the %d forced blocks", h, k, nforced);
+    hb->keep[h] = k;
+    hb->head_off[h] = off;
+    off += (long long)d.nb * k;
+  }
+  hb->per_batch = off;
+  return BSGM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsgm_version(void) { return 10000; }
+
+const char* bsgm_last_error(void) { return g_err.c_str(); }
+
+size_t bsgm_workspace_bytes(const bsgm_layout* layout, int32_t mode) {
+  bsgm::Dims d;
+  if (check_layout(layout, &d) != BSGM_OK) return 0;
+  if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF && mode != BSGM_SEL_DRIFT) {
+    fail(BSGM_E_ARG, "unknown selection mode %d", mode);
+    return 0;
+  }
+  ok();
+  return ws_layout(d, mode).total;
+}
+
+int64_t bsgm_col_capacity(const bsgm_layout* layout, const bsgm_select_params* params) {
+  bsgm::Dims d;
+  if (check_layout(layout, &d) != BSGM_OK) return -1;
+  bsgm::HeadBudget hb;
+  if (check_budget(d, params, &hb) != BSGM_OK) return -1;
+  ok();
+  return (int64_t)d.B * hb.per_batch;
+}
+
+int bsgm_pool_blocks(const bsgm_layout* layout, const void* x, float* mean, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  if (!x || !mean) return fail(BSGM_E_ARG, "x and mean must be non-NULL");
+  hipError_t e = bsgm::launch_pool(d, layout->dtype, x, mean, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  return ok();
+}
+
+int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, const void* v,
+                      float* contrib, float* score, void* ws, size_t ws_bytes, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  if (!q || !k || !v || !contrib || !score || !ws)
+    return fail(BSGM_E_ARG, "q, k, v, contrib, score and ws must be non-NULL");
+  const WsLayout w = ws_layout(d, BSGM_SEL_DRIFT);
+  if (ws_bytes < w.total)
+    return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  float* qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + w.qbar);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, s);
+  if (e != hipSuccess) return hip_fail(e, "drift launch");
+  return ok();
+}
+
+int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,
+                       const void* q, const void* k, const float* contrib, int32_t* row_ptr,
+                       int32_t* col_idx, int64_t col_capacity, float* row_stat,
+                       float* scores_out, int32_t* swap_log, void* ws, size_t ws_bytes,
+                       void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  bsgm::HeadBudget hb;
+  st = check_budget(d, params, &hb);
+  if (st != BSGM_OK) return st;
+  const int mode = params->mode;
+  if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF && mode != BSGM_SEL_DRIFT)
+    return fail(BSGM_E_ARG, "unknown selection mode %d", mode);
+  if (!row_ptr || !col_idx) return fail(BSGM_E_ARG, "row_ptr and col_idx must be non-NULL");
+  const long long need = (long long)d.B * hb.per_batch;
+  if (need > 0x7FFFFFFFLL)
+    return fail(BSGM_E_UNSUPPORTED, "worst-case nnz %lld does not fit int32 CSR", need);
+  if (col_capacity < need)
+    return fail(BSGM_E_CAPACITY, "col_capacity %lld below worst-case nnz %lld",
+                (long long)col_capacity, need);
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == BSGM_SEL_DRIFT) {
+    if (!contrib) return fail(BSGM_E_ARG, "DRIFT needs contrib");
+    if (params->swap_rounds < 0) return fail(BSGM_E_ARG, "swap_rounds must be >= 0");
+    if (d.nb > bsgm::kDriftMaxBlocks)
+      return fail(BSGM_E_UNSUPPORTED, "DRIFT supports at most %d blocks per row (got %d)",
+                  bsgm::kDriftMaxBlocks, d.nb);
+    if (swap_log && params->swap_rounds == 0) swap_log = nullptr;
+    hipError_t e = bsgm::launch_select_drift(d, hb, params->force_frame_first_block ? 1 : 0,
+                                             params->swap_rounds, contrib, row_ptr, col_idx,
+                                             row_stat, swap_log, s);
+    if (e != hipSuccess) return hip_fail(e, "drift select launch");
+    return ok();
+  }
+  if (!q || !k) return fail(BSGM_E_ARG, "TOPK and CDF need q and k");
+  if (mode == BSGM_SEL_CDF && !(params->cdf_tau > 0.f && params->cdf_tau <= 1.f))
+    return fail(BSGM_E_ARG, "cdf_tau must be in (0, 1]");
+  if (d.nb > bsgm::kSelectMaxBlocks)
+    return fail(BSGM_E_UNSUPPORTED, "pooled selection supports at most %d blocks per row",
+                bsgm::kSelectMaxBlocks);
+  if (!ws) return fail(BSGM_E_ARG, "ws must be non-NULL");
+  const WsLayout w = ws_layout(d, mode);
+  if (ws_bytes < w.total)
+    return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  char* base = static_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(base + w.qbar);
+  float* kbar = reinterpret_cast<float*>(base + w.kbar);
+  int32_t* counts = mode == BSGM_SEL_CDF ? reinterpret_cast<int32_t*>(base + w.counts) : nullptr;
+  uint32_t* bitmask =
+      mode == BSGM_SEL_CDF ? reinterpret_cast<uint32_t*>(base + w.bitmask) : nullptr;
+  hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
+  if (e == hipSuccess) e = bsgm::launch_pool(d, layout->dtype, k, kbar, s);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  e = bsgm::launch_select_pooled(d, hb, mode, params->cdf_tau,
+                                 params->force_frame_first_block ? 1 : 0, qbar, kbar, row_ptr,
+                                 col_idx, row_stat, scores_out, counts, bitmask, s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                         void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  if (!q || !k || !v || !row_ptr || !col_idx || !o)
+    return fail(BSGM_E_ARG, "q, k, v, row_ptr, col_idx and o must be non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = layout->dtype == BSGM_BF16
+                     ? bsgm::launch_attn_bf16(d, q, k, v, row_ptr, col_idx, o, lse, s)
+                     : bsgm::launch_attn_f32(d, q, k, v, row_ptr, col_idx, o, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI host layer (api.hip) and the kernel
+// launchers. Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsgm {
+
+// Layout as the kernels see it (validated on the host).
+struct Dims {
+  int B, H, D;         // batch, heads, head_dim (64)
+  int F, L, Lv;        // frames, padded frame length, real tokens per frame
+  int blk;             // block size (64 or 128)
+  int N;               // tokens per (b, h) = F * L
+  int nb;              // blocks per (b, h) = N / blk
+  int rows;            // B * H * nb
+  float scale;         // softmax scale
+};
+
+constexpr int kMaxHeads = 128;
+
+// Per-head budget and the CSR offset of each head's first row inside one
+// batch entry (closed form when every row of head h keeps exactly keep[h]).
+struct HeadBudget {
+  int keep[kMaxHeads];
+  long long head_off[kMaxHeads];   // sum_{h' < h} nb * keep[h']
+  long long per_batch;             // sum_h nb * keep[h]
+};
+
+// Pooling: mean over real tokens of each block. dtype: 0 f32, 1 bf16.
+hipError_t launch_pool(const Dims& d, int dtype, const void* x, float* mean, hipStream_t s);
+
+// Pooled selection (TOPK = 0, CDF = 1) from pooled Q and K.
+hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, float tau,
+                                int force, const float* qbar, const float* kbar,
+                                int32_t* row_ptr, int32_t* col_idx, float* row_stat,
+                                float* scores_out, int32_t* counts, uint32_t* bitmask,
+                                hipStream_t s);
+
+// Drift contributions and scores from pooled Q and K, V.
+hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, const void* k,
+                                const void* v, float* contrib, float* score, hipStream_t s);
+
+// Drift selection with swap restoration.
+hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, int rounds,
+                               const float* contrib, int32_t* row_ptr, int32_t* col_idx,
+                               float* row_stat, int32_t* swap_log, hipStream_t s);
+
+// Block-sparse attention forward.
+hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const void* v,
+                            const int32_t* row_ptr, const int32_t* col_idx, void* o,
+                            float* lse, hipStream_t s);
+hipError_t launch_attn_f32(const Dims& d, const void* q, const void* k, const void* v,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* o,
+                           float* lse, hipStream_t s);
+
+// Largest key-block count the drift selection keeps in LDS.
+constexpr int kDriftMaxBlocks = 512;
+// Largest block count a pooled selection row handles (16 per thread x 256).
+constexpr int kSelectMaxBlocks = 4096;
+
+}  // namespace bsgm

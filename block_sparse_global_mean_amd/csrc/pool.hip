@@ -1,0 +1,49 @@
+// Block mean pool: the mean of Q (or K) over the real tokens of every block,
+// accumulated in fp32. One workgroup per (block, b*h); HBM-bound stream.
+#include "device_util.h"
+
+namespace bsgm {
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, float* __restrict__ mean,
+                                              Dims d) {
+  constexpr int E = 16 / sizeof(T);       // elements per 16-byte chunk
+  constexpr int C = 64 / E;               // chunks per 64-wide row
+  constexpr int G = 256 / C;              // row groups
+  __shared__ float part[G][65];
+  const int j = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int c = t % C, g = t / C;
+  const int vlen = block_vlen(d, j);
+  const T* base = x + ((size_t)bh * d.N + (size_t)j * d.blk) * 64;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int r = g; r < vlen; r += G) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + (size_t)r * 64 + c * E);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += (float)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) part[g][c * E + e] = acc[e];
+  __syncthreads();
+  if (t < 64) {
+    float s = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < G; ++q) s += part[q][t];
+    mean[((size_t)bh * d.nb + j) * 64 + t] = s / (float)vlen;
+  }
+}
+
+hipError_t launch_pool(const Dims& d, int dtype, const void* x, float* mean, hipStream_t s) {
+  dim3 grid(d.nb, d.B * d.H);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_pool<__bf16>, grid, dim3(256), 0, s, (const __bf16*)x, mean, d);
+  else
+    hipLaunchKernelGGL(k_pool<float>, grid, dim3(256), 0, s, (const float*)x, mean, d);
+  return hipGetLastError();
+}
+
+}  // namespace bsgm

@@ -1,0 +1,180 @@
+/*
+ * bsgm.h - C ABI of the block-sparse global attention library for MI355X (gfx950).
+ *
+ * The library computes one global-attention layer of a multi-view geometry
+ * transformer with block sparsity, in two stages joined by a block list:
+ *
+ *   1. selection: for every (batch, head, query block) pick the key blocks to
+ *      execute, by pooled top-k, by a cumulative pooled-mass threshold under a
+ *      per-head cap, or by residual-drift score with swap restoration;
+ *   2. block-sparse attention forward over the selected blocks only.
+ *
+ * Sources (pages, by title):
+ *   [ReSS] "ReSS: Residual-Restoring Sparse Attention for 3D Vision
+ *          Transformers" (thelatestinai.com 2609.35593).
+ *   [VASC] "VASC: Value-Aware Sparse Attention with Cross-Layer Memory for
+ *          Efficient 3D Reconstruction" (paperlayer.ai 2610.01013v1 summary).
+ *
+ * Conventions shared by every entry point
+ *   - Q, K, V, O are device tensors [batch, heads, N, head_dim], row-major,
+ *     head_dim contiguous, N = frames * frame_len. Token f*frame_len + p is a
+ *     real token iff p < frame_valid; the others are padding and are ignored
+ *     by every pool, softmax and drift sum (their contents do not matter).
+ *   - Blocks: block j covers tokens [j*block, (j+1)*block); Nb = N / block.
+ *     Query and key blocks share the grid.
+ *   - Block lists are CSR: row r = (b*heads + h)*Nb + i, row_ptr int32
+ *     [batch*heads*Nb + 1], col_idx int32 key-block indices, strictly
+ *     ascending within a row.
+ *   - Ownership: the caller allocates every buffer (device memory for all
+ *     tensors and the workspace, host memory only where stated). The library
+ *     allocates nothing, keeps no state besides the per-thread error text,
+ *     and never synchronises: all work is enqueued on `stream` (a
+ *     hipStream_t; NULL means the default stream).
+ *   - Errors: arguments are checked on the host before any launch; on error
+ *     nothing is enqueued and a negative bsgm_status is returned, with text in
+ *     bsgm_last_error(). A launch failure reported by HIP returns
+ *     BSGM_E_HIP. Device-side contents (e.g. CSR indices passed to
+ *     bsgm_sparse_attn_fwd) are not validated.
+ *   - Supported: head_dim 64; block 64 or 128 dividing frame_len; at most one
+ *     partially padded block per frame (frame_len - frame_valid < block);
+ *     heads <= 128; dtype BSGM_BF16 (bf16 MFMA attention) or BSGM_F32.
+ */
+#ifndef BSGM_H
+#define BSGM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSGM_OK = 0,
+  BSGM_E_ARG = -1,          /* null pointer or out-of-range argument            */
+  BSGM_E_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, block, ...) */
+  BSGM_E_CAPACITY = -3,     /* col_capacity below the worst-case nnz            */
+  BSGM_E_WORKSPACE = -4,    /* ws_bytes below bsgm_workspace_bytes()            */
+  BSGM_E_HIP = -5           /* HIP reported an error at launch                  */
+} bsgm_status;
+
+typedef enum { BSGM_F32 = 0, BSGM_BF16 = 1 } bsgm_dtype;
+
+typedef enum {
+  BSGM_SEL_TOPK = 0,   /* fixed budget by pooled score                        */
+  BSGM_SEL_CDF = 1,    /* cumulative pooled mass >= tau, capped per head      */
+  BSGM_SEL_DRIFT = 2   /* drift score + swap restoration at a fixed budget    */
+} bsgm_sel_mode;
+
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t frames, frame_len, frame_valid;
+  int32_t block;
+  int32_t dtype;   /* bsgm_dtype of Q, K, V and O */
+  float scale;     /* softmax scale, normally 1/sqrt(head_dim) */
+} bsgm_layout;
+
+typedef struct {
+  int32_t mode;                   /* bsgm_sel_mode                                    */
+  const int32_t* keep_per_head;   /* HOST array [heads]: kept blocks per query block
+                                     (TOPK, DRIFT) or the cap (CDF); 1..Nb            */
+  float cdf_tau;                  /* CDF only: threshold in (0, 1]                    */
+  int32_t force_frame_first_block;/* keep the block holding token f*frame_len of every
+                                     frame in every row; forced blocks count toward
+                                     the budget                                       */
+  int32_t swap_rounds;            /* DRIFT only: restoration rounds, >= 0             */
+} bsgm_select_params;
+
+/* Version of this ABI (major*10000 + minor*100 + patch). */
+int32_t bsgm_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Valid until the
+ * next call of this library on the same thread. */
+const char* bsgm_last_error(void);
+
+/* Device workspace that bsgm_select_blocks (TOPK, CDF) or bsgm_drift_scores
+ * (mode = BSGM_SEL_DRIFT) needs for this layout; 0 if the layout is invalid
+ * (see bsgm_last_error). bsgm_select_blocks in DRIFT mode needs none. */
+size_t bsgm_workspace_bytes(const bsgm_layout* layout, int32_t mode);
+
+/* Worst-case number of CSR entries: batch * Nb * sum_h keep_per_head[h];
+ * -1 on invalid arguments. */
+int64_t bsgm_col_capacity(const bsgm_layout* layout, const bsgm_select_params* params);
+
+/* Block mean pool ([ReSS] Table S5, SpargeAttn row: selection on pooled
+ * query/key inner products; [VASC] A.1: pooled query blocks index key/value
+ * child blocks).
+ *   x    device [B,H,N,D] of layout->dtype
+ *   mean device float [B,H,Nb,D]: mean of x over the real tokens of each block.
+ */
+int bsgm_pool_blocks(const bsgm_layout* layout, const void* x, float* mean, void* stream);
+
+/* Drift contributions ([ReSS] abstract, Figs. 1-3: the shift that dropping a
+ * key block leaves in what attention writes into the residual stream).
+ * For pooled query block i (mean of Q over its real tokens) and every real key
+ * token u: l = scale*<qbar_i, k_u>, e_u = exp(l - max_u l);
+ *   contrib[b,h,i,j,:] = sum_{u in block j} e_u v_u / sum_u e_u   (float)
+ *   score[b,h,i,j]     = || contrib[b,h,i,j,:] ||_2                (float)
+ *   q, k, v  device [B,H,N,D] of layout->dtype
+ *   contrib  device float [B,H,Nb,Nb,D], required
+ *   score    device float [B,H,Nb,Nb], required
+ *   ws       device, >= bsgm_workspace_bytes(layout, BSGM_SEL_DRIFT) bytes
+ */
+int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, const void* v,
+                      float* contrib, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/* Block selection ([VASC] A.2: exact binary capacity per query; [ReSS]
+ * Fig. 3(b): per-head budget; [ReSS] Table 2: the cumulative-threshold rule;
+ * [VASC] 4.2: special-token key blocks always kept; selected lists go to the
+ * sparse kernel as they are).
+ * Priority order of a row: forced blocks (ascending), then the rest by score
+ * descending, ties to the lower block index.
+ *   TOPK : score = scale*<qbar_i, kbar_j>; keep the first keep_per_head[h].
+ *   CDF  : P = softmax_j(score); keep the shortest prefix whose mass reaches
+ *          cdf_tau (all blocks if it never does), at most keep_per_head[h],
+ *          at least one and at least the forced blocks.
+ *   DRIFT: score = ||contrib_ij||; start from the first keep_per_head[h]; then
+ *          up to swap_rounds rounds, each making the single swap (restore a
+ *          dropped block a, drop a kept non-forced block b) that minimises
+ *          J^2 = ||sum_{dropped} contrib - contrib_a + contrib_b||^2 (ties: lower
+ *          a, then lower b) if it lowers J, stopping otherwise.
+ *   q, k       device [B,H,N,D] (TOPK, CDF; may be NULL for DRIFT)
+ *   contrib    device float [B,H,Nb,Nb,D] from bsgm_drift_scores (DRIFT only)
+ *   row_ptr    device int32 [B*H*Nb + 1], written
+ *   col_idx    device int32 [col_capacity], first row_ptr[last] entries written
+ *   col_capacity >= bsgm_col_capacity(layout, params)
+ *   row_stat   device float [B*H*Nb] or NULL: kept pooled mass sum_{kept} P
+ *              (TOPK, CDF) or the final drift J = ||sum_{dropped} contrib|| (DRIFT)
+ *   scores_out device float [B,H,Nb,Nb] or NULL: the pooled logits (TOPK, CDF)
+ *   swap_log   device int32 [B*H*Nb, swap_rounds, 2] or NULL: the (a, b) of each
+ *              round, (-1, -1) once restoration has stopped (DRIFT)
+ *   ws         device, >= bsgm_workspace_bytes(layout, mode) bytes
+ */
+int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,
+                       const void* q, const void* k, const float* contrib,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                       float* row_stat, float* scores_out, int32_t* swap_log,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention forward ([VASC] section 3: retained weights are
+ * renormalised after dropping connections; [ReSS] Table S6: every selection
+ * rule drives the same block grid and sparse kernel). For each real query
+ * token t of query block i, over the real key tokens u of the listed blocks:
+ *   o_t = sum_u exp(scale <q_t,k_u> - m_t) v_u / sum_u exp(scale <q_t,k_u> - m_t),
+ *   lse_t = m_t + log(sum_u exp(scale <q_t,k_u> - m_t)),  m_t = max_u scale <q_t,k_u>.
+ * Padding query rows get o = 0 and lse = -inf; a row with no listed block
+ * gets the same.
+ *   q, k, v   device [B,H,N,D] of layout->dtype
+ *   row_ptr, col_idx  device CSR as above (strictly ascending indices < Nb)
+ *   o         device [B,H,N,D] of layout->dtype (bf16: rounded to nearest even)
+ *   lse       device float [B,H,N] or NULL
+ */
+int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         void* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSGM_H */

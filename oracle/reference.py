@@ -275,6 +275,8 @@ def sparse_attention_row(q_bh, k_bh, v_bh, layout, i: int, kept: Sequence[int]
     o = np.zeros((Bk, D))
     lse = np.full(Bk, -np.inf)
     rows = block_tokens(layout, i)
+    if not len(kept):
+        return o, lse          # no listed block: nothing to attend to
     keys = np.concatenate([block_tokens(layout, j) for j in sorted(kept)])
     if len(rows) and len(keys):
         orow, lrow = attention_rows(q_bh[rows], k_bh[keys], v_bh[keys], layout.scale)

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented codes (no device work involved)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_global_mean_amd as bsgm
+from block_sparse_global_mean_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "bsgm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsgm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(bsgm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsgm.library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert bsgm.version() == 10000
+
+
+class L:
+    def __init__(self, **kw):
+        base = dict(batch=1, heads=2, head_dim=64, frames=4, frame_len=256, frame_valid=250,
+                    block=128, dtype="bf16", scale=0.125)
+        base.update(kw)
+        self.__dict__.update(base)
+
+
+def ws(layout, mode):
+    lib = bsgm.library()
+    c = _lib.c_layout(layout)
+    return lib.bsgm_workspace_bytes(ctypes.byref(c), mode)
+
+
+def test_workspace_sizes():
+    lay = L()
+    rows = 2 * 8
+    assert ws(lay, bsgm.TOPK) == 2 * rows * 64 * 4
+    assert ws(lay, bsgm.DRIFT) == rows * 64 * 4
+    assert ws(lay, bsgm.CDF) == 2 * rows * 64 * 4 + 256 + 256
+    assert ws(lay, 7) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=128), -2), (dict(block=32), -2), (dict(frame_len=200, frame_valid=200), -2),
+    (dict(frame_valid=100), -2), (dict(frame_valid=0), -1), (dict(frame_valid=300), -1),
+    (dict(dtype=5), -1), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(heads=0), -1), (dict(heads=129), -2),
+])
+def test_bad_layouts_rejected(kw, code):
+    lib = bsgm.library()
+    c = _lib.c_layout(L(**kw))
+    fake = ctypes.c_void_p(16)
+    rc = lib.bsgm_sparse_attn_fwd(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, None)
+    assert rc == code, lib.bsgm_last_error()
+    assert lib.bsgm_last_error().decode() != ""
+
+
+def _select(lay, mode=0, keep=(2, 2), force=False, rounds=0, tau=0.9, cap=None, wsb=None,
+            q=16, k=16, contrib=None, rp=16, ci=16):
+    lib = bsgm.library()
+    c = _lib.c_layout(lay)
+    P, arr = _lib.c_params(mode, keep, tau, force, rounds)
+    need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
+    cap = need if cap is None else cap
+    wsb = ws(lay, mode) if wsb is None else wsb
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = lib.bsgm_select_blocks(ctypes.byref(c), ctypes.byref(P), v(q), v(k), v(contrib), v(rp),
+                                v(ci), cap, None, None, None, ctypes.c_void_p(16), wsb, None)
+    return rc, lib.bsgm_last_error().decode(), need
+
+
+def test_select_argument_errors():
+    lay = L()
+    assert _select(lay, keep=(0, 2))[0] == -1
+    assert _select(lay, keep=(2, 9))[0] == -1                  # Nb = 8
+    assert _select(lay, keep=(2, 2), force=True)[0] == -1      # 4 forced blocks > 2
+    rc, msg, need = _select(lay, keep=(3, 5))
+    assert need == 8 * 3 + 8 * 5
+    assert _select(lay, keep=(3, 5), cap=need - 1)[0] == -3
+    assert _select(lay, keep=(3, 5), wsb=100)[0] == -4
+    assert _select(lay, mode=1, tau=0.0)[0] == -1
+    assert _select(lay, mode=1, tau=1.5)[0] == -1
+    assert _select(lay, mode=9)[0] == -1
+    assert _select(lay, mode=2, contrib=None)[0] == -1
+    assert _select(lay, mode=2, contrib=16, rounds=-1)[0] == -1
+    assert _select(lay, q=None)[0] == -1
+    assert _select(lay, rp=None)[0] == -1
+    big = L(frames=2, frame_len=128 * 300, frame_valid=128 * 300)
+    assert _select(big, mode=2, keep=(5, 5), contrib=16)[0] == -2      # 600 blocks > 512
+
+
+def test_col_capacity_and_errors():
+    lay = L(batch=3)
+    assert bsgm.col_capacity(lay, bsgm.TOPK, [2, 5]) == 3 * 8 * 7
+    with pytest.raises(bsgm.BsgmError):
+        bsgm.col_capacity(lay, bsgm.TOPK, [0, 5])
+
+
+def test_pool_and_drift_null_arguments():
+    lib = bsgm.library()
+    c = _lib.c_layout(L())
+    assert lib.bsgm_pool_blocks(ctypes.byref(c), None, ctypes.c_void_p(16), None) == -1
+    one = ctypes.c_void_p(16)
+    assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, None, one, one, 1 << 20, None) == -1
+    assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, one, 10, None) == -4
+    assert lib.bsgm_pool_blocks(None, one, one, None) == -1

@@ -1,0 +1,524 @@
+"""HIP path against the oracle, through the C ABI (needs an MI355X).
+
+Small cases compare every element; the full-size presets run in the launch
+configuration that bench.py times and compare sampled rows the oracle computes
+one by one. Rules and tolerances are in tests/parity.py.
+"""
+import dataclasses
+import math
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_global_mean_amd as bsgm
+import oracle
+import workloads
+from workloads import synthetic
+import parity
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsgm.library()
+    return torch.device("cuda:0")
+
+
+def to_dev(arr_bits_or_f32, dev):
+    a = np.ascontiguousarray(arr_bits_or_f32)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a.astype(np.float32)).to(dev)
+
+
+def preset(idx, heads=None):
+    key = (idx, heads)
+    if key not in _CACHE:
+        w = workloads.config(idx)
+        if heads is not None:
+            w = synthetic.restrict(w, heads)
+        data = workloads.generate(workloads.config(idx), heads=heads)
+        _CACHE[key] = (w, data)
+    return _CACHE[key]
+
+
+def inputs(w, data, dev):
+    if w.layout.dtype == "bf16":
+        return tuple(to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
+    return tuple(to_dev(data[n], dev) for n in ("q", "k", "v"))
+
+
+def custom_layout(frames, frame_len, frame_valid, block, heads=1, dtype="bf16", batch=1):
+    return synthetic.Layout(batch, heads, 64, frames, frame_len, frame_valid, block, dtype, 0.125)
+
+
+def random_inputs(lay, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    shape = (lay.batch, lay.heads, lay.tokens, lay.head_dim)
+    arrs = [rng.standard_normal(shape, dtype=np.float32) * np.float32(scale) for _ in range(3)]
+    pad = (np.arange(lay.tokens) % lay.frame_len) >= lay.frame_valid
+    for a in arrs:
+        a[:, :, pad] = 0
+    if lay.dtype == "bf16":
+        bits = [workloads.bf16_bits_from_float(a) for a in arrs]
+        return bits, [workloads.float_from_bf16_bits(b) for b in bits]
+    return arrs, arrs
+
+
+def oracle_csr_rows(sets):
+    return [kept for per_b in sets for per_h in per_b for kept in per_h]
+
+
+def upload_csr(rows, dev):
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    ci = np.array([j for r in rows for j in r], dtype=np.int32)
+    if ci.size == 0:
+        ci = np.zeros(1, dtype=np.int32)
+    return torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+
+
+def assert_outputs(lay, o, o_ref, valid, label):
+    ok, worst, err = parity.output_check(o, o_ref, valid, lay.dtype)
+    say(f"{label}: max abs err {err:.3e}, worst error / allowance {worst:.3f}")
+    assert ok, (label, worst, err)
+
+
+# --------------------------------------------------------------------------
+# pooling
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["tiny_f32", "layer8_2heads", "ragged_bf16_b64", "ragged_f32_b128"])
+def test_pool_matches_oracle(dev, case):
+    say(f"pool {case}")
+    if case == "tiny_f32":
+        w, data = preset(0)
+        lay, host_in, vals = w.layout, [data["q"]], [data["q"]]
+    elif case == "layer8_2heads":
+        w, data = preset(1, heads=2)
+        lay, host_in, vals = w.layout, [data["q_bits"]], [data["q"]]
+    elif case == "ragged_bf16_b64":
+        lay = custom_layout(3, 192, 150, 64, heads=2)
+        host_in, vals = random_inputs(lay, 1)
+    else:
+        lay = custom_layout(2, 384, 300, 128, heads=1, dtype="f32")
+        host_in, vals = random_inputs(lay, 2)
+    x = to_dev(host_in[0], dev)
+    got = bsgm.pool_blocks(lay, x).cpu().numpy()
+    torch.cuda.synchronize()
+    ref = oracle.pool(vals[0], lay)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6 * max(1.0, np.abs(ref).max()))
+
+
+# --------------------------------------------------------------------------
+# pooled top-k selection
+# --------------------------------------------------------------------------
+def check_topk(lay, vals, keep, force, row_ptr, col_idx, scores_gpu, stat_gpu):
+    q, k, v = vals
+    nb = lay.nblocks
+    parity.check_csr_wellformed(row_ptr, col_idx, nb)
+    qbar, kbar = oracle.pool(q, lay), oracle.pool(k, lay)
+    s = oracle.pooled_scores(qbar, kbar, lay.scale)
+    p = oracle.row_softmax(s)
+    np.testing.assert_allclose(scores_gpu, s, rtol=0, atol=2e-5 * max(1.0, np.abs(s).max()))
+    forced = oracle.forced_blocks(lay, force)
+    rows = parity.csr_rows(row_ptr, col_idx)
+    mism = 0
+    for b in range(lay.batch):
+        for h in range(lay.heads):
+            for i in range(nb):
+                r = (b * lay.heads + h) * nb + i
+                exact = oracle.select_topk_row(s[b, h, i], int(keep[h]), forced)
+                if rows[r] != exact:
+                    mism += 1
+                    assert parity.topk_valid(rows[r], s[b, h, i], int(keep[h]), forced), \
+                        f"row {r}: {rows[r]} vs oracle {exact}"
+                else:
+                    assert abs(stat_gpu[r] - p[b, h, i, exact].sum()) < 1e-4
+    return mism
+
+
+@pytest.mark.parametrize("case", ["tiny_f32", "layer8_2heads", "layer32_forced_1head", "ragged_b64_2batch"])
+def test_topk_selection_matches_oracle(dev, case):
+    say(f"topk select {case}")
+    force = False
+    if case == "tiny_f32":
+        w, data = preset(0)
+        lay, dev_in, vals, keep = w.layout, inputs(w, data, dev), (data["q"], data["k"], data["v"]), data["keep"]
+    elif case == "layer8_2heads":
+        w, data = preset(1, heads=2)
+        lay, dev_in, vals, keep = w.layout, inputs(w, data, dev), (data["q"], data["k"], data["v"]), data["keep"]
+    elif case == "layer32_forced_1head":
+        w, data = preset(2, heads=1)
+        lay, dev_in, vals, keep = w.layout, inputs(w, data, dev), (data["q"], data["k"], data["v"]), data["keep"]
+        force = True
+    else:
+        lay = custom_layout(5, 192, 170, 64, heads=3, batch=2)
+        host_in, vals = random_inputs(lay, 3)
+        dev_in = tuple(to_dev(x, dev) for x in host_in)
+        keep = np.array([1, 7, 15], dtype=np.int32)
+        force = False
+    nb = lay.nblocks
+    scores = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=dev_in[0], k=dev_in[1], force=force,
+                                    scores_out=scores)
+    torch.cuda.synchronize()
+    mism = check_topk(lay, vals, keep, force, rp.cpu().numpy(), ci.cpu().numpy(),
+                      scores.cpu().numpy(), st.cpu().numpy())
+    say(f"topk {case}: rows differing from the oracle by near-ties: {mism}")
+
+
+def test_topk_deterministic(dev):
+    w, data = preset(1, heads=2)
+    q, k, _ = inputs(w, data, dev)
+    a = bsgm.select_blocks(w.layout, bsgm.TOPK, data["keep"], q=q, k=k)
+    b = bsgm.select_blocks(w.layout, bsgm.TOPK, data["keep"], q=q, k=k)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# --------------------------------------------------------------------------
+# attention on the oracle's CSR
+# --------------------------------------------------------------------------
+def run_attention_case(dev, lay, host_in, vals, rows, label):
+    say(f"attention {label}")
+    q, k, v = (to_dev(x, dev) for x in host_in)
+    rp, ci = upload_csr(rows, dev)
+    o, lse = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    col_idx = np.array([j for r in rows for j in r], dtype=np.int64)
+    o_ref, lse_ref = oracle.sparse_attention(vals[0], vals[1], vals[2], lay, row_ptr, col_idx)
+    valid = oracle.valid_mask(lay)
+    assert_outputs(lay, o, o_ref, valid, f"attention {label}")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    lse_tol = 1e-4 if lay.dtype == "f32" else 2e-3
+    assert np.abs(lse[fin] - lse_ref[fin]).max() <= lse_tol * max(1.0, np.abs(lse_ref[fin]).max())
+    assert np.all(o[..., ~valid, :] == 0)
+    return o, lse
+
+
+def test_attention_tiny_f32(dev):
+    w, data = preset(0)
+    vals = (data["q"], data["k"], data["v"])
+    sets, _ = oracle.select(*vals, w.layout, oracle.TOPK, data["keep"])
+    run_attention_case(dev, w.layout, vals, vals, oracle_csr_rows(sets), "tiny f32 top-4")
+
+
+def test_attention_layer8_2heads(dev):
+    w, data = preset(1, heads=2)
+    vals = (data["q"], data["k"], data["v"])
+    sets, _ = oracle.select(*vals, w.layout, oracle.TOPK, data["keep"])
+    host = (data["q_bits"], data["k_bits"], data["v_bits"])
+    run_attention_case(dev, w.layout, host, vals, oracle_csr_rows(sets), "8 frames, 2 heads, 50%")
+
+
+@pytest.mark.parametrize("dtype,block", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_attention_ragged_random_lists(dev, dtype, block):
+    """Random kept lists (including empty rows and the partial last block of
+    each frame) on a ragged layout with two batch entries."""
+    lay = custom_layout(3, 2 * block, 2 * block - 37, block, heads=2, dtype=dtype, batch=2)
+    host, vals = random_inputs(lay, 11 + block)
+    nb = lay.nblocks
+    rng = np.random.default_rng(5)
+    rows = []
+    for r in range(lay.batch * lay.heads * nb):
+        n = int(rng.integers(0, nb + 1)) if r % 7 else 0
+        rows.append(sorted(rng.choice(nb, size=n, replace=False).tolist()))
+    run_attention_case(dev, lay, host, vals, rows, f"ragged {dtype} block {block}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_all_kept_is_dense(dev, dtype):
+    lay = custom_layout(2, 256, 200, 128, heads=2, dtype=dtype)
+    host, vals = random_inputs(lay, 21)
+    nb = lay.nblocks
+    rows = [list(range(nb))] * (lay.heads * nb)
+    o, lse = run_attention_case(dev, lay, host, vals, rows, f"all kept {dtype}")
+    od, lsed = oracle.dense_attention(*vals, lay)
+    valid = oracle.valid_mask(lay)
+    assert_outputs(lay, o, od, valid, f"all kept vs dense {dtype}")
+
+
+def test_attention_constant_values_and_lse_merge(dev):
+    lay = custom_layout(2, 256, 230, 128, heads=1)
+    host, vals = random_inputs(lay, 31)
+    nb = lay.nblocks
+    q, k, _ = (to_dev(x, dev) for x in host)
+    ones = torch.ones_like(q)
+    rng = np.random.default_rng(6)
+    rows_s = [sorted(rng.choice(nb, size=2, replace=False).tolist()) for _ in range(nb)]
+    rows_d = [sorted(set(range(nb)) - set(s)) for s in rows_s]
+    rp, ci = upload_csr(rows_s, dev)
+    o1, _ = bsgm.sparse_attn_fwd(lay, q, k, ones, rp, ci)
+    valid = torch.from_numpy(oracle.valid_mask(lay)).to(dev)
+    assert torch.all((o1.float()[0, 0, valid] - 1).abs() <= 2 ** -7)
+    v = to_dev(host[2], dev)
+    os_, ls_ = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True)
+    rp2, ci2 = upload_csr(rows_d, dev)
+    od_, ld_ = bsgm.sparse_attn_fwd(lay, q, k, v, rp2, ci2, want_lse=True)
+    rp3, ci3 = upload_csr([list(range(nb))] * nb, dev)
+    oa_, la_ = bsgm.sparse_attn_fwd(lay, q, k, v, rp3, ci3, want_lse=True)
+    torch.cuda.synchronize()
+    ws, wd = ls_[0, 0, valid].exp()[:, None], ld_[0, 0, valid].exp()[:, None]
+    merged = (ws * os_.float()[0, 0, valid] + wd * od_.float()[0, 0, valid]) / (ws + wd)
+    ref = oa_.float()[0, 0, valid]
+    allow = 2 * 2e-2 * ref.pow(2).mean(dim=-1).sqrt()
+    assert bool(((merged - ref).abs().max(dim=-1).values <= allow).all())
+    assert float((torch.logaddexp(ls_, ld_)[0, 0, valid] - la_[0, 0, valid]).abs().max()) <= 2e-3
+
+
+# --------------------------------------------------------------------------
+# CDF selection
+# --------------------------------------------------------------------------
+def check_cdf(lay, vals, keep, tau, force, row_ptr, col_idx, stat_gpu, rows_to_check=None):
+    q, k, _ = vals
+    nb = lay.nblocks
+    parity.check_csr_wellformed(row_ptr, col_idx, nb)
+    rows = parity.csr_rows(row_ptr, col_idx)
+    forced = oracle.forced_blocks(lay, force)
+    bound_by_cdf = 0
+    mism = 0
+    for h in range(lay.heads):
+        qbar = oracle.pool(q[:, h:h + 1], lay)[0, 0]
+        kbar = oracle.pool(k[:, h:h + 1], lay)[0, 0]
+        for i in (range(nb) if rows_to_check is None else rows_to_check):
+            r = h * nb + i
+            s = lay.scale * (kbar @ qbar[i])
+            p = oracle.row_softmax(s)
+            exact = oracle.select_cdf_row(s, p, tau, int(keep[h]), forced)
+            if len(exact) < keep[h]:
+                bound_by_cdf += 1
+            if rows[r] != exact:
+                mism += 1
+                assert parity.cdf_valid(rows[r], s, p, tau, int(keep[h]), forced), \
+                    f"row {r}: {rows[r]} vs oracle {exact}"
+            else:
+                assert abs(stat_gpu[r] - p[exact].sum()) < 1e-4
+    return bound_by_cdf, mism
+
+
+def planted_peaked(lay, seed):
+    """Pooled scores with a few dominant key blocks per row, so that the
+    cumulative-mass rule stops before the cap."""
+    rng = np.random.default_rng(seed)
+    N, D = lay.tokens, lay.head_dim
+    u = rng.standard_normal(D).astype(np.float32)
+    u /= np.linalg.norm(u)
+    nb = lay.nblocks
+    qs = (rng.standard_normal((lay.heads, nb)) * 2).astype(np.float32)
+    ks = (rng.standard_normal((lay.heads, nb)) * 4).astype(np.float32)
+    q = np.zeros((1, lay.heads, N, D), np.float32)
+    k = np.zeros_like(q)
+    for h in range(lay.heads):
+        q[0, h] = np.repeat(qs[h], lay.block)[:, None] * u[None, :] * 4
+        k[0, h] = np.repeat(ks[h], lay.block)[:, None] * u[None, :] * 4
+    q += rng.standard_normal(q.shape).astype(np.float32) * 0.3
+    k += rng.standard_normal(k.shape).astype(np.float32) * 0.3
+    v = rng.standard_normal(q.shape).astype(np.float32)
+    pad = (np.arange(N) % lay.frame_len) >= lay.frame_valid
+    for a in (q, k, v):
+        a[:, :, pad] = 0
+    bits = [workloads.bf16_bits_from_float(a) for a in (q, k, v)]
+    return bits, [workloads.float_from_bf16_bits(b) for b in bits]
+
+
+@pytest.mark.parametrize("force", [False, True])
+def test_cdf_selection_planted(dev, force):
+    say(f"cdf planted force={force}")
+    lay = synthetic.restrict(workloads.config(1), 3).layout
+    host, vals = planted_peaked(lay, 41)
+    keep = np.array([44, 30, 12], dtype=np.int32)
+    q, k = to_dev(host[0], dev), to_dev(host[1], dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.CDF, keep, q=q, k=k, cdf_tau=0.9, force=force)
+    torch.cuda.synchronize()
+    bound, mism = check_cdf(lay, vals, keep, 0.9, force, rp.cpu().numpy(), ci.cpu().numpy(),
+                            st.cpu().numpy())
+    say(f"cdf planted: rows stopped by the threshold {bound}, near-tie rows {mism}")
+    assert bound > 0
+
+
+def test_cdf_selection_layer100_sampled(dev):
+    """100 frames, 16 heads, per-head caps: the bench launch; sampled rows."""
+    say("cdf 100 frames full size")
+    w, data = preset(3)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.CDF, data["keep"], q=q, k=k, cdf_tau=w.cdf_tau)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    sub = [0, 1, 10, 11, 545, 1099]
+    check_cdf(lay, (data["q"], data["k"], None), data["keep"], w.cdf_tau, False, rpn, cin,
+              st.cpu().numpy(), rows_to_check=sub)
+    # attention on the GPU's own lists: sampled rows whose lists equal the oracle's
+    o, _ = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci)
+    torch.cuda.synchronize()
+    check_sampled_attention(lay, data, o, rpn, cin, [(h, i) for h in (0, 7, 15) for i in (0, 10, 1099)],
+                            lambda h, i, s, p: oracle.select_cdf_row(s, p, w.cdf_tau, int(data["keep"][h])))
+
+
+def check_sampled_attention(lay, data, o_gpu, rpn, cin, samples, rule):
+    rows = parity.csr_rows(rpn, cin)
+    nb = lay.nblocks
+    checked = 0
+    for h, i in samples:
+        qh, kh, vh = data["q"][0, h], data["k"][0, h], data["v"][0, h]
+        qbar = oracle.pool(data["q"][:, h:h + 1], lay)[0, 0]
+        kbar = oracle.pool(data["k"][:, h:h + 1], lay)[0, 0]
+        s = lay.scale * (kbar @ qbar[i])
+        p = oracle.row_softmax(s)
+        exact = rule(h, i, s, p)
+        if rows[h * nb + i] != exact:
+            continue
+        o_ref, _ = oracle.sparse_attention_row(qh, kh, vh, lay, i, exact)
+        og = o_gpu[0, h, i * lay.block:(i + 1) * lay.block].float().cpu().numpy()
+        valid = oracle.valid_mask(lay)[i * lay.block:(i + 1) * lay.block]
+        assert_outputs(lay, og, o_ref, valid, f"sampled row (h={h}, i={i})")
+        checked += 1
+    assert checked >= len(samples) // 2, f"only {checked} sampled rows had oracle-equal lists"
+
+
+def test_topk_layer32_full_size_sampled(dev):
+    """32 frames, 16 heads, 75 % sparse with forced special blocks: the bench
+    launch (select + attention); sampled rows against the oracle."""
+    say("topk 32 frames full size")
+    w, data = preset(2)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.TOPK, data["keep"], q=q, k=k, force=True)
+    o, _ = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, lay.nblocks)
+    assert rpn[-1] == lay.heads * lay.nblocks * 88
+    rows = parity.csr_rows(rpn, cin)
+    forced = oracle.forced_blocks(lay, True)
+    nb = lay.nblocks
+    for h in (0, 5, 15):
+        qbar = oracle.pool(data["q"][:, h:h + 1], lay)[0, 0]
+        kbar = oracle.pool(data["k"][:, h:h + 1], lay)[0, 0]
+        for i in (0, 1, 11, 200, 351):
+            s = lay.scale * (kbar @ qbar[i])
+            assert parity.topk_valid(rows[h * nb + i], s, 88, forced), (h, i)
+    check_sampled_attention(lay, data, o, rpn, cin,
+                            [(h, i) for h in (0, 5, 15) for i in (0, 1, 11, 200, 351)],
+                            lambda h, i, s, p: oracle.select_topk_row(s, 88, forced))
+
+
+def test_topk_layer8_full_size(dev):
+    say("topk 8 frames full size")
+    w, data = preset(1)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    scores = torch.empty((1, lay.heads, lay.nblocks, lay.nblocks), dtype=torch.float32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.TOPK, data["keep"], q=q, k=k, scores_out=scores)
+    torch.cuda.synchronize()
+    mism = check_topk(lay, (data["q"], data["k"], data["v"]), data["keep"], False, rp.cpu().numpy(),
+                      ci.cpu().numpy(), scores.cpu().numpy(), st.cpu().numpy())
+    say(f"topk 8 frames: near-tie rows {mism}")
+
+
+# --------------------------------------------------------------------------
+# drift
+# --------------------------------------------------------------------------
+def check_drift(lay, vals, keep, rounds, force, contrib_g, score_g, rpn, cin, stat_g, log_g,
+                rows_to_check):
+    q, k, v = vals
+    nb = lay.nblocks
+    forced = oracle.forced_blocks(lay, force)
+    rows = parity.csr_rows(rpn, cin)
+    differ = 0
+    for (h, i) in rows_to_check:
+        qbar = oracle.pool(q[:, h:h + 1], lay)[0, 0]
+        chat, z, Z = oracle.drift_row(qbar[i], k[0, h], v[0, h], lay)
+        cg = contrib_g[0, h, i]
+        scale = np.sqrt((chat * chat).sum(axis=1)).max()
+        assert np.abs(cg - chat).max() <= 1e-4 * scale, (h, i)
+        dref = np.sqrt((chat * chat).sum(axis=1))
+        assert np.abs(score_g[0, h, i] - dref).max() <= 1e-4 * dref.max()
+        r = h * nb + i
+        swaps = log_g[r] if rounds > 0 else np.zeros((0, 2), np.int64)
+        ok, why, jrep = parity.drift_valid(rows[r], swaps, chat, int(keep[h]), forced)
+        assert ok, f"row {(h, i)}: {why}"
+        assert abs(stat_g[r] - jrep) <= 1e-4 * max(jrep, 1e-30), (h, i, stat_g[r], jrep)
+        kept_ref, j_ref, _ = oracle.restore_row(chat, int(keep[h]), rounds, forced)
+        if kept_ref != rows[r]:
+            differ += 1
+            assert jrep <= j_ref * (1 + 1e-3)
+    return differ
+
+
+@pytest.mark.parametrize("rounds,force", [(3, False), (0, False), (5, True)])
+def test_drift_layer16_two_heads(dev, rounds, force):
+    say(f"drift 16 frames, 2 heads, rounds {rounds}, force {force}")
+    w, data = preset(4, heads=2)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v)
+    nb = lay.nblocks
+    log = torch.full((lay.heads * nb, max(rounds, 1), 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, data["keep"], contrib=contrib,
+                                    swap_rounds=rounds, force=force, swap_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    assert rpn[-1] == lay.heads * nb * int(data["keep"][0])
+    logn = log.cpu().numpy()
+    if rounds > 0:
+        assert np.all(logn >= -1)
+    sample = [(h, i) for h in range(2) for i in range(0, nb, 5)]
+    differ = check_drift(lay, (data["q"], data["k"], data["v"]), data["keep"], rounds, force,
+                         contrib.cpu().numpy(), score.cpu().numpy(), rpn, cin, st.cpu().numpy(),
+                         logn, sample)
+    say(f"drift: sampled rows whose final set differs from the oracle's own run: {differ}")
+
+
+def test_drift_layer16_full_size_sampled(dev):
+    say("drift 16 frames full size")
+    w, data = preset(4)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v)
+    nb = lay.nblocks
+    log = torch.empty((lay.heads * nb, 3, 2), dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, data["keep"], contrib=contrib, swap_rounds=3,
+                                    swap_log=log)
+    o, _ = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    sample = [(h, i) for h in (0, 9, 15) for i in (0, 77, 175)]
+    check_drift(lay, (data["q"], data["k"], data["v"]), data["keep"], 3, False,
+                contrib.cpu().numpy(), score.cpu().numpy(), rpn, cin, st.cpu().numpy(),
+                log.cpu().numpy(), sample)
+    rows = parity.csr_rows(rpn, cin)
+    compared = 0
+    for h, i in sample:
+        # the oracle's attention on the list its own drift run keeps, compared
+        # where the GPU kept the same list
+        qbar = oracle.pool(data["q"][:, h:h + 1], lay)[0, 0]
+        chat, _, _ = oracle.drift_row(qbar[i], data["k"][0, h], data["v"][0, h], lay)
+        kept_ref, _, _ = oracle.restore_row(chat, 35, 3)
+        if kept_ref != rows[h * nb + i]:
+            continue
+        o_ref, _ = oracle.sparse_attention_row(data["q"][0, h], data["k"][0, h], data["v"][0, h],
+                                               lay, i, kept_ref)
+        og = o[0, h, i * 128:(i + 1) * 128].float().cpu().numpy()
+        valid = oracle.valid_mask(lay)[i * 128:(i + 1) * 128]
+        assert_outputs(lay, og, o_ref, valid, f"drift sampled row (h={h}, i={i})")
+        compared += 1
+    say(f"drift full size: sampled rows with oracle-equal lists compared: {compared}")

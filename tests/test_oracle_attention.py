@@ -177,3 +177,12 @@ def test_frame_permutation_equivariance():
     o2, l2 = oracle.sparse_attention(q, k2, v2, lay, *kept_to_csr(kept2))
     np.testing.assert_allclose(o1, o2, atol=1e-13)
     np.testing.assert_allclose(l1, l2, atol=1e-13)
+
+
+def test_empty_block_list_gives_zero_output():
+    """A query block with no listed key block attends to nothing: o = 0 and
+    lse = -inf, as for padding rows."""
+    lay = layout()
+    q, k, v = rand_qkv(lay, 9)
+    o, lse = oracle.sparse_attention_row(q[0, 0], k[0, 0], v[0, 0], lay, 1, [])
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
