@@ -4,8 +4,17 @@
 // Work split: one workgroup per (b, h, query block) with BLK/32 waves; each
 // wave owns 32 query rows. The workgroup walks the CSR list of its row in
 // ascending key-block order; K and V tiles (BLK x 64 bf16) are staged in LDS,
-// double-buffered, with the next tile's global loads issued before the
-// current tile's math.
+// double-buffered: right after the barrier that opens a tile, the waves issue
+// direct global->LDS copies of the next tile into the other buffer, which land
+// while the current tile's math runs. The row's column list, each entry packed
+// with the number of real keys of its block, is kept in an LDS ring so that
+// the loop reads no global memory besides the tiles.
+//
+// Softmax uses a lazy reference maximum: the running maximum m of a query row
+// moves (and O, l are rescaled) only when a tile's maximum exceeds it by more
+// than 8 in log2 units, so P = exp2((s - m) c) stays below 2^8 and most tiles
+// skip the rescale. The row sum is taken from the bf16-rounded P, the values
+// that enter the second MFMA.
 //
 // Math per key tile, per wave (online softmax, exp2 with the scale folded in):
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q in VGPRs
@@ -35,12 +44,32 @@ struct AttnArgs {
   float* lse;
 };
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+// 16-byte chunk swizzle of a 128-byte key row. gfx950 LDS serves 256 bytes per
+// cycle: a b128 read is served 16 lanes at a time and a b64 read 32 lanes at a
+// time, and rows r and r+1 fall in different 128-byte halves. The K-operand read
+// (16 rows, one logical chunk per 16 lanes) needs distinct swizzles among the even
+// rows and among the odd rows of each 16-row group; the transposing V read (4
+// consecutive rows x 4 chunks per 32 lanes) needs rows r and r+2 to land in
+// opposite 4-chunk halves. f(r) = ((r & 2) << 1) | ((r >> 2) & 3) meets both.
+__device__ __forceinline__ int swz(int row) { return ((row & 2) << 1) | ((row >> 2) & 3); }
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
   typedef bf16x4 __attribute__((address_space(3))) * lds_ptr;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(p));
 }
+
+// One 16-byte-per-lane global->LDS copy: lane l's 16 bytes at `src` land at LDS
+// byte address lds + 16*l (lds is wave-uniform; it goes to M0). Issued as an
+// instruction the compiler does not see as an LDS write, so that it does not
+// wait for the copy before every later LDS read; the tile ring orders it
+// instead (wait_dma() and a barrier before the first read of a slot, a barrier
+// between the last read of a slot and the copy that refills it).
+__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Waits until this wave's global->LDS copies have landed.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
@@ -48,7 +77,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   constexpr int KT = BLK / 32;         // 32-key sub-tiles per key block
   constexpr int TB = BLK * 128;        // bytes of one K or V tile
   constexpr int CPT = (BLK * 8) / NT;  // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];
+  constexpr int CB = 1024;
+  __shared__ int colbuf[CB];
 
   const Dims& d = a.d;
   const int r = xcd_remap(blockIdx.x, d.rows);
@@ -73,43 +104,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   // 16(x/8) + 8(l/32) + x%8 of the 32-key sub-tile.
   const int pim = ((n >> 4) << 4) | (((n >> 2) & 1) << 3) | (((n >> 3) & 1) << 2) | (n & 3);
 
-  // Tile chunk c of this thread: key row cid/8, 16-byte column cid%8, with
-  // cid = tid + NT*s; the LDS offset applies the chunk swizzle.
-  int goff[CPT], soff[CPT];
+  int goff[CPT];
 #pragma unroll
-  for (int s = 0; s < CPT; ++s) {
-    const int cid = tid + NT * s;
-    const int row = cid >> 3, c = cid & 7;
-    goff[s] = cid * 8;
-    soff[s] = row * 128 + ((c ^ swz(row)) << 4);
+  for (int s2 = 0; s2 < CPT; ++s2) {
+    const int q = NT * s2 + tid;
+    const int row = q >> 3, pc = q & 7;
+    goff[s2] = row * 64 + ((pc ^ swz(row)) << 3);
   }
-  uint4 kreg0, kreg1, kreg2, kreg3, vreg0, vreg1, vreg2, vreg3;
-  static_assert(CPT == 4, "four chunks per thread per tile");
-#define BSGM_GLOAD(J)                                                   \
-  do {                                                                  \
-    const __bf16* kt_ = K + (size_t)(J) * BLK * 64;                     \
-    const __bf16* vt_ = V + (size_t)(J) * BLK * 64;                     \
-    kreg0 = *reinterpret_cast<const uint4*>(kt_ + goff[0]);             \
-    kreg1 = *reinterpret_cast<const uint4*>(kt_ + goff[1]);             \
-    kreg2 = *reinterpret_cast<const uint4*>(kt_ + goff[2]);             \
-    kreg3 = *reinterpret_cast<const uint4*>(kt_ + goff[3]);             \
-    vreg0 = *reinterpret_cast<const uint4*>(vt_ + goff[0]);             \
-    vreg1 = *reinterpret_cast<const uint4*>(vt_ + goff[1]);             \
-    vreg2 = *reinterpret_cast<const uint4*>(vt_ + goff[2]);             \
-    vreg3 = *reinterpret_cast<const uint4*>(vt_ + goff[3]);             \
-  } while (0)
-#define BSGM_SWRITE(BUF)                                                \
-  do {                                                                  \
-    unsigned char* kb_ = smem + (BUF) * 2 * TB;                         \
-    unsigned char* vb_ = kb_ + TB;                                      \
-    *reinterpret_cast<uint4*>(kb_ + soff[0]) = kreg0;                   \
-    *reinterpret_cast<uint4*>(kb_ + soff[1]) = kreg1;                   \
-    *reinterpret_cast<uint4*>(kb_ + soff[2]) = kreg2;                   \
-    *reinterpret_cast<uint4*>(kb_ + soff[3]) = kreg3;                   \
-    *reinterpret_cast<uint4*>(vb_ + soff[0]) = vreg0;                   \
-    *reinterpret_cast<uint4*>(vb_ + soff[1]) = vreg1;                   \
-    *reinterpret_cast<uint4*>(vb_ + soff[2]) = vreg2;                   \
-    *reinterpret_cast<uint4*>(vb_ + soff[3]) = vreg3;                   \
+  const int wv = tid >> 6;
+#define BSGM_DMA(BUF, J)                                                         \
+  do {                                                                             \
+    const __bf16* kt_ = K + (size_t)(J) * BLK * 64;                                \
+    const __bf16* vt_ = V + (size_t)(J) * BLK * 64;                                \
+    const unsigned kb_ = (unsigned)(uintptr_t)(smem + (BUF) * 2 * TB) + wv * 1024; \
+    _Pragma("unroll") for (int s3 = 0; s3 < CPT; ++s3) {                           \
+      dma16(kt_ + goff[s3], kb_ + s3 * NT * 16);                                 \
+      dma16(vt_ + goff[s3], kb_ + TB + s3 * NT * 16);                            \
+    }                                                                              \
   } while (0)
 
   // Lane-constant parts of the transposing V read: within each 16-lane group g,
@@ -126,17 +137,29 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = d.scale * 1.4426950408889634f;
 
-  if (beg < end) {
-    BSGM_GLOAD(a.col_idx[beg]);
-    BSGM_SWRITE(0);
+  const int nt = end - beg;
+  for (int x = tid; x < min(nt, CB); x += NT) {
+    const int c = a.col_idx[beg + x];
+    colbuf[x] = (c << 7) | (block_vlen(d, c) - 1);
   }
-  __syncthreads();
+  if (nt > 0) BSGM_DMA(0, a.col_idx[beg]);
 
   for (int it = beg; it < end; ++it) {
-    const int buf = (it - beg) & 1;
-    const int j = a.col_idx[it];
+    const int jt = it - beg;
+    const int buf = jt & 1;
+    wait_dma();
+    __syncthreads();
+    if ((jt & (CB / 2 - 1)) == 0 && jt > 0 && jt + CB / 2 < nt)
+      for (int x = jt + CB / 2 + tid; x < min(nt, jt + CB); x += NT) {
+        const int c = a.col_idx[beg + x];
+        colbuf[x & (CB - 1)] = (c << 7) | (block_vlen(d, c) - 1);
+      }
+    const int ecur = __builtin_amdgcn_readfirstlane(colbuf[jt & (CB - 1)]);
     const bool has_next = it + 1 < end;
-    if (has_next) BSGM_GLOAD(a.col_idx[it + 1]);
+    if (has_next) {
+      const int en = __builtin_amdgcn_readfirstlane(colbuf[(jt + 1) & (CB - 1)]);
+      BSGM_DMA(buf ^ 1, en >> 7);
+    }
     const unsigned char* kb = smem + buf * 2 * TB;
     const unsigned char* vb = kb + TB;
 
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
       }
     }
 
-    const int vlen = block_vlen(d, j);
+    const int vlen = (ecur & 127) + 1;
     if (vlen < BLK) {
 #pragma unroll
       for (int t = 0; t < KT; ++t)
@@ -175,33 +198,43 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
                                                        false, false);
       mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
     }
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-    const float mb = m_new * c2;
-
+    const bool grow = (mx - m_run) * c2 > 8.f;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) oacc[mt][x] *= alpha;
+      m_run = m_new;
+    }
+    const float mb = m_run * c2;
     bf16x8 pb[KT][2];
     float psum = 0.f;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int t = 0; t < KT; ++t)
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
+      for (int e = 0; e < 2; ++e) {
+        float pf[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[t][8 * e + x], c2, -mb));
-          psum += p;
-          pb[t][e][x] = (__bf16)p;
-        }
+        for (int x = 0; x < 8; ++x) pf[x] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * e + x], c2, -mb));
+        const bf16x8 pv = {(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3],
+                           (__bf16)pf[4], (__bf16)pf[5], (__bf16)pf[6], (__bf16)pf[7]};
+        pb[t][e] = pv;
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, psum, false);
+      }
     {
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum),
                                                        false, false);
       psum = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) oacc[mt][x] *= alpha;
+    l_run += psum;
 
 #pragma unroll
     for (int t = 0; t < KT; ++t)
@@ -220,9 +253,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
         }
       }
 
-    if (has_next) BSGM_SWRITE(buf ^ 1);
-    __syncthreads();
   }
+  wait_dma();
 
   // Output: lane holds query qrow and head dims 32mt + 8(x/4) + 4hh + x%4.
   const bool real_q = (qrow % d.L) < d.Lv;

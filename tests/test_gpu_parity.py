@@ -243,6 +243,41 @@ def test_attention_ragged_random_lists(dev, dtype, block):
     run_attention_case(dev, lay, host, vals, rows, f"ragged {dtype} block {block}")
 
 
+@pytest.mark.parametrize("dtype,block", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_attention_long_rows(dev, dtype, block):
+    """Kept lists longer than 512, 1024 and 1536 blocks (the kernels buffer a
+    row's column list in pieces), checked row by row against the oracle."""
+    lay = custom_layout(85 * block // 64, 20 * 64, 20 * 64 - 30, block, heads=1, dtype=dtype)
+    host, vals = random_inputs(lay, 41 + block)
+    nb = lay.nblocks
+    rng = np.random.default_rng(8)
+    lengths = {3: min(nb, 1100), 7: min(nb, 1600), nb // 2: nb, nb - 1: 513, 11: 1025}
+    rows = []
+    for i in range(nb):
+        n = lengths.get(i, 2)
+        rows.append(sorted(rng.choice(nb, size=n, replace=False).tolist()))
+    say(f"attention long rows {dtype} block {block}: nb {nb}, lengths {sorted(lengths.values())}")
+    q, k, v = (to_dev(x, dev) for x in host)
+    rp, ci = upload_csr(rows, dev)
+    o, lse = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()[0, 0]
+    lse = lse.cpu().numpy()[0, 0]
+    for i in sorted(set(lengths) | {0, 1}):
+        ob, lb = oracle.sparse_attention_row(vals[0][0, 0], vals[1][0, 0], vals[2][0, 0], lay, i,
+                                             rows[i])
+        sl = slice(i * block, (i + 1) * block)
+        valid = np.isfinite(lb)
+        assert valid.any()
+        full_valid = oracle.valid_mask(lay)[sl]
+        assert np.array_equal(valid, full_valid)
+        ok, worst, err = parity.output_check(o[sl], ob, valid, lay.dtype)
+        say(f"  row {i} ({len(rows[i])} blocks): max abs err {err:.3e}, worst/allowance {worst:.3f}")
+        assert ok, (i, worst, err)
+        lse_tol = 1e-4 if dtype == "f32" else 2e-3
+        assert np.abs(lse[sl][valid] - lb[valid]).max() <= lse_tol * max(1.0, np.abs(lb[valid]).max())
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_attention_all_kept_is_dense(dev, dtype):
     lay = custom_layout(2, 256, 200, 128, heads=2, dtype=dtype)
