@@ -83,7 +83,7 @@ int check_layout(const bsgm_layout* L, bsgm::Dims* d) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qbar, kbar, counts, bitmask, total;
+  size_t qbar, kbar, counts, bitmask, stats, mz, total;
 };
 
 WsLayout ws_layout(const bsgm::Dims& d, int mode) {
@@ -95,6 +95,12 @@ WsLayout ws_layout(const bsgm::Dims& d, int mode) {
   if (mode == BSGM_SEL_TOPK || mode == BSGM_SEL_CDF) {
     w.kbar = off;
     off += align256(pooled);
+  }
+  if (mode == BSGM_SEL_DRIFT) {
+    w.stats = off;
+    off += align256((size_t)d.rows * d.nb * 2 * sizeof(float));
+    w.mz = off;
+    off += align256((size_t)d.rows * 2 * sizeof(float));
   }
   if (mode == BSGM_SEL_CDF) {
     w.counts = off;
@@ -178,7 +184,13 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
-  e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, s);
+  if (layout->dtype == BSGM_BF16) {
+    char* base = static_cast<char*>(ws);
+    e = bsgm::launch_drift_contrib_bf16(d, qbar, k, v, reinterpret_cast<float2*>(base + w.stats),
+                                        reinterpret_cast<float2*>(base + w.mz), contrib, score, s);
+  } else {
+    e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "drift launch");
   return ok();
 }

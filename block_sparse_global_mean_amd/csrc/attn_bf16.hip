@@ -44,20 +44,6 @@ struct AttnArgs {
   float* lse;
 };
 
-// 16-byte chunk swizzle of a 128-byte key row. gfx950 LDS serves 256 bytes per
-// cycle: a b128 read is served 16 lanes at a time and a b64 read 32 lanes at a
-// time, and rows r and r+1 fall in different 128-byte halves. The K-operand read
-// (16 rows, one logical chunk per 16 lanes) needs distinct swizzles among the even
-// rows and among the odd rows of each 16-row group; the transposing V read (4
-// consecutive rows x 4 chunks per 32 lanes) needs rows r and r+2 to land in
-// opposite 4-chunk halves. f(r) = ((r & 2) << 1) | ((r >> 2) & 3) meets both.
-__device__ __forceinline__ int swz(int row) { return ((row & 2) << 1) | ((row >> 2) & 3); }
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
-  typedef bf16x4 __attribute__((address_space(3))) * lds_ptr;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(p));
-}
-
 // One 16-byte-per-lane global->LDS copy: lane l's 16 bytes at `src` land at LDS
 // byte address lds + 16*l (lds is wave-uniform; it goes to M0). Issued as an
 // instruction the compiler does not see as an LDS write, so that it does not

@@ -93,6 +93,57 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
   return __popcll(below);
 }
 
+// LDS tiles of 64-wide bf16 rows (K or V, 128 bytes per key row): the
+// 16-byte chunk index within a row is XOR-swizzled by swz(row).
+//
+// Chunk swizzle of a 128-byte key row. gfx950 LDS serves 256 bytes per
+// cycle: a b128 read is served 16 lanes at a time and a b64 read 32 lanes at a
+// time, and rows r and r+1 fall in different 128-byte halves. The K-operand read
+// (16 rows, one logical chunk per 16 lanes) needs distinct swizzles among the even
+// rows and among the odd rows of each 16-row group; the transposing V read (4
+// consecutive rows x 4 chunks per 32 lanes) needs rows r and r+2 to land in
+// opposite 4-chunk halves. f(r) = ((r & 2) << 1) | ((r >> 2) & 3) meets both.
+__device__ __forceinline__ int swz(int row) { return ((row & 2) << 1) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
+  typedef bf16x4 __attribute__((address_space(3))) * lds_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(p));
+}
+
+// Fragments for v_mfma_f32_32x32x16_bf16 on such tiles. Both operands give
+// lane l the row or column l % 32 and the k-slots 8 (l / 32) .. +7.
+//
+// K fragment (operand of S^T = K X^T over head dims 16 ks .. 16 ks + 15): A-row m
+// of the 32-key sub-tile t reads key row 32 t + key_perm(m), where
+// m = 8a + 4h + j maps to 16 (a / 2) + 8h + 4 (a % 2) + j. Accumulator register x
+// of lane l then holds key 16 (x / 8) + 8 (l / 32) + x % 8 of the sub-tile, so the
+// 8 registers x = 8e .. 8e + 7 are 8 consecutive keys: exactly the k-slots that a
+// lane supplies when the same keys are the contraction index of a second MFMA.
+__device__ __forceinline__ int key_perm(int m) {
+  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+__device__ __forceinline__ bf16x8 k_frag(const unsigned char* kb, int t, int ks, int lane) {
+  const int row = 32 * t + key_perm(lane & 31);
+  return *reinterpret_cast<const bf16x8*>(kb + row * 128 +
+                                          (((2 * ks + (lane >> 5)) ^ swz(row)) << 4));
+}
+
+// V fragment for a contraction over keys kbase .. kbase + 15: lane l gets head
+// dim 32 mt + l % 32 of keys kbase + 8 (l / 32) + s, s = 0..7 (the A operand of
+// O^T += V^T P^T, or equally the B operand of O += P V). Two transposing 8-byte
+// reads: within each 16-lane group g, lane jj fetches 4 head dims of key row
+// 8 (g / 2) + jj / 4 and of the row 4 below it.
+__device__ __forceinline__ bf16x8 v_frag(const unsigned char* vb, int kbase, int mt, int lane) {
+  const int g16 = lane >> 4, jj = lane & 15;
+  const int row_lo = kbase + 8 * (g16 >> 1) + (jj >> 2), row_hi = row_lo + 4;
+  const int byte = 64 * mt + 32 * (g16 & 1) + 8 * (jj & 3);
+  const int c = byte >> 4, sub = byte & 15;
+  const bf16x4 lo = lds_read_tr(vb + row_lo * 128 + ((c ^ swz(row_lo)) << 4) + sub);
+  const bf16x4 hi = lds_read_tr(vb + row_hi * 128 + ((c ^ swz(row_hi)) << 4) + sub);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Maps a dispatch index to a work index so that the workgroups that one XCD
 // (dispatch index mod 8) runs take consecutive work items: neighbouring rows
 // of one head then share that XCD's L2. Bijective on [0, n).

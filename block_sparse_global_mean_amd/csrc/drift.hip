@@ -1,5 +1,6 @@
-// Drift contributions of every key block to every pooled query block, and the
-// drift selection with swap restoration.
+// Drift contributions of every key block to every pooled query block for fp32
+// inputs (vector ALU; bf16 inputs take the matrix-core kernels of
+// drift_mfma.hip), and the drift selection with swap restoration.
 //
 // Contributions: for pooled query i and real key token u,
 //   e_u = exp(scale <qbar_i, k_u> - M_i),  M_i = max_u scale <qbar_i, k_u>,

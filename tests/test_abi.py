@@ -47,7 +47,9 @@ def test_workspace_sizes():
     lay = L()
     rows = 2 * 8
     assert ws(lay, bsgm.TOPK) == 2 * rows * 64 * 4
-    assert ws(lay, bsgm.DRIFT) == rows * 64 * 4
+    nb = 8
+    al = lambda x: (x + 255) // 256 * 256
+    assert ws(lay, bsgm.DRIFT) == rows * 64 * 4 + al(rows * nb * 8) + al(rows * 8)
     assert ws(lay, bsgm.CDF) == 2 * rows * 64 * 4 + 256 + 256
     assert ws(lay, 7) == 0
 

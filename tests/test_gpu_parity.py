@@ -523,6 +523,34 @@ def test_drift_layer16_two_heads(dev, rounds, force):
     say(f"drift: sampled rows whose final set differs from the oracle's own run: {differ}")
 
 
+@pytest.mark.parametrize("dtype,block,force", [("bf16", 64, False), ("bf16", 128, True),
+                                               ("f32", 64, True), ("f32", 128, False)])
+def test_drift_small_layouts(dev, dtype, block, force):
+    """Every row of ragged layouts with 40 (block 64) or 33 (block 128) key
+    blocks per head: two 32-row query tiles, the second partial, and for 33 an
+    odd block count (the kernels pair key blocks)."""
+    frames, per = (10, 4) if block == 64 else (11, 3)
+    lay = custom_layout(frames, per * block, per * block - 37, block, heads=2, dtype=dtype)
+    host, vals = random_inputs(lay, 51 + block)
+    nb = lay.nblocks
+    nf = frames if force else 0
+    keep = np.array([max(10, nf + 3), max(7, nf + 1)], dtype=np.int32)
+    rounds = 3
+    say(f"drift small {dtype} block {block} force {force}: nb {nb}")
+    q, k, v = (to_dev(x, dev) for x in host)
+    contrib, score = bsgm.drift_scores(lay, q, k, v)
+    log = torch.full((lay.heads * nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    force=force, swap_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    rows = [(h, i) for h in range(lay.heads) for i in range(nb)]
+    differ = check_drift(lay, vals, keep, rounds, force, contrib.cpu().numpy(), score.cpu().numpy(),
+                         rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows)
+    say(f"drift small: rows whose final set differs from the oracle's own run: {differ}")
+
+
 def test_drift_layer16_full_size_sampled(dev):
     say("drift 16 frames full size")
     w, data = preset(4)
