@@ -11,10 +11,6 @@
 #include "../../include/bsgm.h"
 #include "internal.h"
 
-namespace bsgm {
-size_t drift_select_lds_bytes(int nb);
-}
-
 namespace {
 
 thread_local std::string g_err;

@@ -7,6 +7,8 @@
 //   contrib_ij = sum_{u in j} e_u v_u / Z_i,  Z_i = sum_u e_u,  score_ij = ||contrib_ij||.
 // Pass 1 finds (M_i, Z_i) with an online log-sum-exp; pass 2 walks the key
 // blocks and writes contrib and score. All arithmetic is fp32.
+#include <algorithm>
+
 #include "device_util.h"
 
 namespace bsgm {
@@ -149,18 +151,28 @@ __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__
 
 hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, const void* k,
                                 const void* v, float* contrib, float* score, hipStream_t s) {
+  if (dtype != 0) return hipErrorInvalidValue;   // bf16 takes launch_drift_contrib_bf16
   dim3 grid((d.nb + kDriftRows - 1) / kDriftRows, d.B * d.H);
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_drift_contrib<__bf16>, grid, dim3(256), 0, s, qbar, (const __bf16*)k,
-                       (const __bf16*)v, contrib, score, d);
-  else
-    hipLaunchKernelGGL(k_drift_contrib<float>, grid, dim3(256), 0, s, qbar, (const float*)k,
-                       (const float*)v, contrib, score, d);
+  hipLaunchKernelGGL(k_drift_contrib<float>, grid, dim3(256), 0, s, qbar, (const float*)k,
+                     (const float*)v, contrib, score, d);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Drift selection: one workgroup per row, the row's contributions in LDS.
+// Drift selection: one workgroup per row.
+//
+// With D the dropped blocks, S the kept non-forced blocks, r = sum_{j in D} c_j,
+// g_j = <r, c_j> and G_ab = <c_a, c_b>, restoring a in D and dropping b in S gives
+//   J^2(a, b) = ||r - c_a + c_b||^2 = ||r||^2 + delta(a, b),
+//   delta(a, b) = (|c_a|^2 - 2 g_a) + (|c_b|^2 + 2 g_b) - 2 G_ab.
+// A round takes the pair of least delta (ties: lower a, then lower b) and swaps
+// it if delta < 0.
+//
+// LDS holds the contributions of D and S in slot order (D slots first, then S
+// slots; forced blocks never move and are not needed). A swap exchanges the two
+// slots' rows and updates r by -c_a + c_b. G over D x S does not depend on r:
+// when it fits it is computed once per row into LDS and a swap refreshes one
+// row and one column of it; otherwise every round recomputes the dot products.
 // ---------------------------------------------------------------------------
 struct DriftSelArgs {
   Dims d;
@@ -174,167 +186,295 @@ struct DriftSelArgs {
   int32_t* swap_log;
 };
 
-constexpr int kCs = 65;   // padded LDS row stride (floats) of a contribution vector
+constexpr int kCs = 68;          // LDS row stride (floats): 16-byte aligned, rows 4 banks apart
+constexpr int kTa = 3, kTb = 4;  // register tile of dot products: kTa D slots x kTb S slots
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+// float4 registers per thread that hold a whole row of contributions: RR = 8
+// for rows of up to 256 blocks, 16 up to kDriftMaxBlocks
+// Dynamic LDS a selection workgroup may take (the static arrays need < 4 KB).
+constexpr size_t kDriftSelLdsCap = 160 * 1024 - 6144;
 
-__device__ __forceinline__ bool better(float j2, int a, int b, float bj2, int ba, int bb) {
-  return j2 < bj2 || (j2 == bj2 && (a < ba || (a == ba && b < bb)));
+template <typename P>
+__device__ __forceinline__ float dot64(const P* x, const float* y) {
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  const float4* y4 = reinterpret_cast<const float4*>(y);
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; c += 2) {
+    const float4 a0 = x4[c], b0 = y4[c], a1 = x4[c + 1], b1 = y4[c + 1];
+    s0 = fmaf(a0.x, b0.x, s0); s0 = fmaf(a0.y, b0.y, s0);
+    s0 = fmaf(a0.z, b0.z, s0); s0 = fmaf(a0.w, b0.w, s0);
+    s1 = fmaf(a1.x, b1.x, s1); s1 = fmaf(a1.y, b1.y, s1);
+    s1 = fmaf(a1.z, b1.z, s1); s1 = fmaf(a1.w, b1.w, s1);
+  }
+  return s0 + s1;
 }
 
-__global__ __launch_bounds__(256) void k_select_drift(DriftSelArgs a) {
-  extern __shared__ float smem[];
+// LDS carve-up of one row (byte offsets).
+struct DriftSelLds {
+  size_t cs, slot, keys, slot_of, G, total;
+};
+
+__host__ __device__ inline DriftSelLds drift_sel_lds(int nb, int nslots, size_t gfloats) {
+  DriftSelLds L;
+  size_t o = 0;
+  L.cs = o;      o += (size_t)nslots * kCs * 4;  // slot rows
+  L.slot = o;    o += (size_t)nslots * 16;       // per slot: |c|^2, weight, block, -
+  L.keys = o;    o += (size_t)nb * 8;            // priority keys by block
+  L.slot_of = o; o += (size_t)nb * 4;            // slot of each block (-1: forced)
+  o = (o + 15) & ~(size_t)15;
+  L.G = o;       o += gfloats * 4;               // G[D slot][S slot]
+  L.total = o;
+  return L;
+}
+
+struct SlotRec {
+  float cc;    // |c|^2
+  float wgt;   // |c|^2 - 2 g (D slot) or |c|^2 + 2 g (S slot)
+  int blk;     // key block in this slot
+  int pad;
+};
+
+template <bool CACHE, int RR>
+__global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
   const Dims& d = a.d;
   const int nb = d.nb;
-  float* cs = smem;                                  // [nb][kCs]
-  float* cc = cs + (size_t)nb * kCs;                 // [nb] squared norms
-  int* kept = reinterpret_cast<int*>(cc + nb);       // [nb]
-  int* dl = kept + nb;                               // [nb] dropped list
-  int* sl = dl + nb;                                 // [nb] kept non-forced list
-  __shared__ float rv[64];
-  __shared__ float part[4][64];
-  __shared__ float redf[4];
-  __shared__ int redi[4];
-  __shared__ int wtot[4];
-  __shared__ float bj2s[4];
-  __shared__ int bas[4], bbs[4];
-  __shared__ int nd_s, ns_s;
-
   const int r = blockIdx.x;
   const int bh = r / nb, i = r - bh * nb;
   const int h = bh % d.H, b = bh / d.H;
+  const int k = a.hb.keep[h];
+  const int nd = nb - k, ns = k - (a.force ? d.F : 0), nsl = nd + ns;
+  const DriftSelLds L = drift_sel_lds(nb, nsl, CACHE ? (size_t)nd * ns : 0);
+  float* cs = reinterpret_cast<float*>(dsm + L.cs);
+  SlotRec* slot = reinterpret_cast<SlotRec*>(dsm + L.slot);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(dsm + L.keys);
+  int* slot_of = reinterpret_cast<int*>(dsm + L.slot_of);
+  float* G = reinterpret_cast<float*>(dsm + L.G);
+  __shared__ __attribute__((aligned(16))) float rv[64];
+  __shared__ float part[kSelWaves][64];
+  __shared__ int bks[kSelWaves];
+  __shared__ unsigned long long bkey[kSelWaves];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const float* src = a.contrib + ((size_t)bh * nb + i) * (size_t)nb * 64;
-  for (int x = t; x < nb * 64; x += 256) cs[(x >> 6) * kCs + (x & 63)] = src[x];
-  __syncthreads();
 
-  // squared norms and keys (nb <= 512: two slots per thread)
-  constexpr int PER = kDriftMaxBlocks / 256;
-  unsigned long long key[PER];
-  bool valid[PER];
+  // the row, coalesced into registers: thread t holds chunk (t + 512 m) & 15 of
+  // block (t + 512 m) >> 4; squared norms reduce over the 16 lanes of a block
+  const float4* src = reinterpret_cast<const float4*>(
+      a.contrib + ((size_t)bh * nb + i) * (size_t)nb * 64);
+  float4 row[RR];
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int j = t + 256 * p;
-    valid[p] = j < nb;
-    key[p] = 0ull;
-    if (valid[p]) {
-      float s = 0.f;
-      for (int c = 0; c < 64; ++c) s = fmaf(cs[j * kCs + c], cs[j * kCs + c], s);
-      cc[j] = s;
-      const bool f = a.force && block_forced(d, j);
-      const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(sqrtf(s));
-      key[p] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
+  for (int m = 0; m < RR; ++m) {
+    const int x = t + kSelThreads * m;
+    row[m] = x < nb * 16 ? src[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int m = 0; m < RR; ++m) {
+    const int x = t + kSelThreads * m;
+    if (kSelThreads * m < nb * 16) {
+      float ss = row[m].x * row[m].x + row[m].y * row[m].y + row[m].z * row[m].z +
+                 row[m].w * row[m].w;
+      ss += __shfl_xor(ss, 8, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 1, 64);
+      const int j = x >> 4;
+      if ((x & 15) == 0 && j < nb) {
+        const bool f = a.force && block_forced(d, j);
+        const unsigned long long hi =
+            f ? 0xFFFFFFFFull : (unsigned long long)orderable(sqrtf(ss));
+        keys[j] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
+        slot_of[j] = __float_as_int(ss);   // the norm, until slots are known
+      }
     }
   }
-  const int k = a.hb.keep[h];
-  unsigned long long T = 0ull;
-  for (int bit = 63; bit >= 0; --bit) {
-    const unsigned long long cand = T | (1ull << bit);
-    int c = 0;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) c += (valid[p] && key[p] >= cand) ? 1 : 0;
-    if (block_sum_i<256>(c, redi) >= k) T = cand;
+  __syncthreads();
+  // initial kept set: the k keys of highest priority (keys are distinct)
+  bool kept_j = false, forced_j = false;
+  float cc_j = 0.f;
+  if (t < nb) {
+    const unsigned long long kj = keys[t];
+    int rank = 0;
+#pragma unroll 8
+    for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
+    kept_j = rank < k;
+    forced_j = a.force && block_forced(d, t);
+    cc_j = __int_as_float(slot_of[t]);
   }
+  // slots: dropped blocks ascending, then kept non-forced blocks ascending
+  {
+    const bool isd = t < nb && !kept_j, iss = t < nb && kept_j && !forced_j;
+    const unsigned long long md = __ballot(isd), ms = __ballot(iss);
+    if (lane == 0) bkey[w] = ((unsigned long long)__popcll(md) << 32) | __popcll(ms);
+    __syncthreads();
+    int bd0 = 0, bs0 = 0;
+    for (int q = 0; q < w; ++q) { bd0 += (int)(bkey[q] >> 32); bs0 += (int)(uint32_t)bkey[q]; }
+    int sl = -1;
+    if (isd) sl = bd0 + lanes_below(md);
+    if (iss) sl = nd + bs0 + lanes_below(ms);
+    if (t < nb) {
+      slot_of[t] = sl;
+      if (sl >= 0) slot[sl] = SlotRec{cc_j, 0.f, t, 0};
+    }
+  }
+  __syncthreads();
 #pragma unroll
-  for (int p = 0; p < PER; ++p)
-    if (valid[p]) kept[t + 256 * p] = key[p] >= T ? 1 : 0;
+  for (int m = 0; m < RR; ++m) {
+    const int x = t + kSelThreads * m;
+    if (x < nb * 16) {
+      const int sl = slot_of[x >> 4];
+      if (sl >= 0) *reinterpret_cast<float4*>(cs + sl * kCs + 4 * (x & 15)) = row[m];
+    }
+  }
+  __syncthreads();
+
+  // kTa x kTb tiles of <c_a, c_b>. Tile (ta, tb) takes D slots ta + x NTA and S
+  // slots tb + y NTB, so that neighbouring lanes read neighbouring LDS rows.
+  const int NTA = (nd + kTa - 1) / kTa, NTB = (ns + kTb - 1) / kTb, ntiles = NTA * NTB;
+  auto tiles = [&](auto&& consume) {
+    for (int tile = t; tile < ntiles; tile += kSelThreads) {
+      const int ta = tile / NTB, tb = tile - ta * NTB;
+      float acc[kTa][kTb];
+#pragma unroll
+      for (int x = 0; x < kTa; ++x)
+#pragma unroll
+        for (int y = 0; y < kTb; ++y) acc[x][y] = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < 64; c += 4) {
+        float4 av[kTa], bv[kTb];
+#pragma unroll
+        for (int x = 0; x < kTa; ++x)
+          av[x] = *reinterpret_cast<const float4*>(cs + min(ta + x * NTA, nd - 1) * kCs + c);
+#pragma unroll
+        for (int y = 0; y < kTb; ++y)
+          bv[y] = *reinterpret_cast<const float4*>(cs + (nd + min(tb + y * NTB, ns - 1)) * kCs + c);
+#pragma unroll
+        for (int x = 0; x < kTa; ++x)
+#pragma unroll
+          for (int y = 0; y < kTb; ++y) {
+            acc[x][y] = fmaf(av[x].x, bv[y].x, acc[x][y]);
+            acc[x][y] = fmaf(av[x].y, bv[y].y, acc[x][y]);
+            acc[x][y] = fmaf(av[x].z, bv[y].z, acc[x][y]);
+            acc[x][y] = fmaf(av[x].w, bv[y].w, acc[x][y]);
+          }
+      }
+#pragma unroll
+      for (int x = 0; x < kTa; ++x)
+#pragma unroll
+        for (int y = 0; y < kTb; ++y) {
+          const int ai = ta + x * NTA, bi = tb + y * NTB;
+          if (ai < nd && bi < ns) consume(ai, bi, acc[x][y]);
+        }
+    }
+  };
+
+  // r = sum of the dropped contributions; G once per row when cached
+  {
+    float s = 0.f;
+    for (int x = w; x < nd; x += kSelWaves) s += cs[x * kCs + lane];
+    part[w][lane] = s;
+  }
+  if (CACHE) tiles([&](int ai, int bi, float v) { G[ai * ns + bi] = v; });
+  __syncthreads();
+  if (t < 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kSelWaves; ++q) s += part[q][t];
+    rv[t] = s;
+  }
   __syncthreads();
 
   float rr = 0.f;
-  bool stopped = false;
-  for (int round = 0; round <= a.rounds; ++round) {
-    // residual of the drop set: r = sum over dropped j of contrib_j
+  for (int round = 0;; ++round) {
     {
-      const int dd = t & 63, g = t >> 6;
-      float s = 0.f;
-      for (int j = g; j < nb; j += 4)
-        if (!kept[j]) s += cs[j * kCs + dd];
-      part[g][dd] = s;
+      const float x = rv[lane];
+      rr = wave_sum(x * x);
     }
-    __syncthreads();
-    if (t < 64) rv[t] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
-    __syncthreads();
-    {
-      const float x = t < 64 ? rv[t] * rv[t] : 0.f;
-      rr = block_sum<256>(x, redf);
-    }
-    if (round == a.rounds || stopped) break;
+    if (round == a.rounds) break;
 
-    // candidate lists, ascending: dropped blocks (to restore) and kept
-    // non-forced blocks (to drop)
-    {
-      int nd = 0, ns = 0;
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int j = t + 256 * p;
-        const bool isd = valid[p] && !kept[j];
-        const bool iss = valid[p] && kept[j] && !(a.force && block_forced(d, j));
-        const unsigned long long md = __ballot(isd), ms = __ballot(iss);
-        __syncthreads();
-        if (lane == 0) wtot[w] = __popcll(md) | (__popcll(ms) << 16);
-        __syncthreads();
-        int bd = 0, bs = 0, td = 0, ts = 0;
-        for (int q = 0; q < 4; ++q) {
-          const int vd = wtot[q] & 0xFFFF, vs = wtot[q] >> 16;
-          if (q < w) { bd += vd; bs += vs; }
-          td += vd; ts += vs;
-        }
-        if (isd) dl[nd + bd + lanes_below(md)] = j;
-        if (iss) sl[ns + bs + lanes_below(ms)] = j;
-        nd += td;
-        ns += ts;
-      }
-      if (t == 0) { nd_s = nd; ns_s = ns; }
+    for (int sl = t; sl < nsl; sl += kSelThreads) {
+      const float g = dot64(rv, cs + sl * kCs);
+      slot[sl].wgt = sl < nd ? slot[sl].cc - 2.f * g : slot[sl].cc + 2.f * g;
     }
     __syncthreads();
-    const int nd = nd_s, ns = ns_s;
-    float best = INFINITY;
-    int ba = 0x7FFFFFFF, bb = 0x7FFFFFFF;
-    for (int ai = t; ai < nd; ai += 256) {
-      const int aa = dl[ai];
-      float u[64];
-      float uu = 0.f;
-#pragma unroll
-      for (int c = 0; c < 64; ++c) {
-        u[c] = rv[c] - cs[aa * kCs + c];
-        uu = fmaf(u[c], u[c], uu);
+
+    // candidates ordered by (delta, a, b) as one 64-bit key
+    unsigned long long best = ~0ull;
+    if (CACHE) {
+      // thread t takes S slot bi = t % ns and D slots ai = t / ns + m * (512 / ns)
+      const int per = kSelThreads / max(ns, 1);
+      if (ns > 0 && t < per * ns) {
+        const int bi = t % ns;
+        const SlotRec sb = slot[nd + bi];
+        const uint32_t blo = (uint32_t)sb.blk;
+#pragma unroll 4
+        for (int ai = t / ns; ai < nd; ai += per) {
+          const SlotRec sa = slot[ai];
+          const float dlt = (sa.wgt + sb.wgt) - 2.f * G[ai * ns + bi];
+          const unsigned long long key = ((unsigned long long)orderable(dlt) << 32) |
+                                         ((uint32_t)sa.blk << 16) | blo;
+          best = key < best ? key : best;
+        }
       }
-      for (int bi = 0; bi < ns; ++bi) {
-        const int bbk = sl[bi];
-        float dot = 0.f;
-#pragma unroll
-        for (int c = 0; c < 64; ++c) dot = fmaf(u[c], cs[bbk * kCs + c], dot);
-        const float j2 = uu + 2.f * dot + cc[bbk];
-        if (better(j2, aa, bbk, best, ba, bb)) { best = j2; ba = aa; bb = bbk; }
-      }
+    } else {
+      tiles([&](int ai, int bi, float v) {
+        const SlotRec sa = slot[ai], sb = slot[nd + bi];
+        const float dlt = (sa.wgt + sb.wgt) - 2.f * v;
+        const unsigned long long key = ((unsigned long long)orderable(dlt) << 32) |
+                                       ((uint32_t)sa.blk << 16) | (uint32_t)sb.blk;
+        best = key < best ? key : best;
+      });
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      const float ob = __shfl_xor(best, o, 64);
-      const int oa = __shfl_xor(ba, o, 64), obb = __shfl_xor(bb, o, 64);
-      if (better(ob, oa, obb, best, ba, bb)) { best = ob; ba = oa; bb = obb; }
+      const unsigned long long ob = __shfl_xor(best, o, 64);
+      best = ob < best ? ob : best;
     }
-    if (lane == 0) { bj2s[w] = best; bas[w] = ba; bbs[w] = bb; }
+    if (lane == 0) bkey[w] = best;
     __syncthreads();
-    best = bj2s[0]; ba = bas[0]; bb = bbs[0];
-    for (int q = 1; q < 4; ++q)
-      if (better(bj2s[q], bas[q], bbs[q], best, ba, bb)) { best = bj2s[q]; ba = bas[q]; bb = bbs[q]; }
-    const bool do_swap = nd > 0 && ns > 0 && best < rr;
+    best = bkey[0];
+#pragma unroll
+    for (int q = 1; q < kSelWaves; ++q) best = bkey[q] < best ? bkey[q] : best;
+    const uint32_t hi = (uint32_t)(best >> 32);
+    // delta < 0 (strictly) exactly when its orderable key is below that of -0
+    const float bd = best == ~0ull ? INFINITY : (hi < 0x7FFFFFFFu ? -1.f : 1.f);
+    const uint32_t bab = (uint32_t)best;
+    const bool do_swap = nd > 0 && ns > 0 && bd < 0.f;
+    const int ba = (int)(bab >> 16), bb = (int)(bab & 0xFFFFu);
     if (t == 0 && a.swap_log) {
       int32_t* lg = a.swap_log + ((size_t)r * a.rounds + round) * 2;
       lg[0] = do_swap ? ba : -1;
       lg[1] = do_swap ? bb : -1;
     }
-    __syncthreads();
-    if (do_swap) {
-      if (t == 0) { kept[ba] = 1; kept[bb] = 0; }
-    } else {
-      stopped = true;
+    if (!do_swap) {
       if (a.swap_log)
-        for (int q = round + 1 + t; q < a.rounds; q += 256) {
+        for (int q = round + 1 + t; q < a.rounds; q += kSelThreads) {
           a.swap_log[((size_t)r * a.rounds + q) * 2] = -1;
           a.swap_log[((size_t)r * a.rounds + q) * 2 + 1] = -1;
         }
+      break;   // r and rr describe the final drop set
+    }
+    // restore ba (D slot pa) and drop bb (S slot sb): exchange the slots' rows
+    const int pa = slot_of[ba], sb = slot_of[bb], pb = sb - nd;
+    __syncthreads();   // every wave is done with bkey, slot weights and G of this round
+    if (t < 64) {
+      const float ra = cs[pa * kCs + t], rb = cs[sb * kCs + t];
+      rv[t] = (rv[t] - ra) + rb;
+      cs[pa * kCs + t] = rb;
+      cs[sb * kCs + t] = ra;
+    } else if (t == 64) {
+      const SlotRec x = slot[pa];
+      slot[pa] = slot[sb];
+      slot[sb] = x;
+      slot_of[ba] = sb;
+      slot_of[bb] = pa;
     }
     __syncthreads();
+    if (CACHE)
+      for (int x = t; x < ns + nd; x += kSelThreads) {
+        if (x < ns) G[pa * ns + x] = dot64(cs + pa * kCs, cs + (nd + x) * kCs);
+        else if (x - ns != pa) G[(x - ns) * ns + pb] = dot64(cs + (x - ns) * kCs, cs + sb * kCs);
+      }
   }
   if (t == 0 && a.row_stat) a.row_stat[r] = sqrtf(rr);
 
@@ -343,38 +483,40 @@ __global__ __launch_bounds__(256) void k_select_drift(DriftSelArgs a) {
     a.row_ptr[r] = (int32_t)base;
     if (r == d.rows - 1) a.row_ptr[d.rows] = (int32_t)(base + k);
   }
-  long long running = base;
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int j = t + 256 * p;
-    const bool f = valid[p] && kept[j];
+  // kept blocks in ascending order: a block is kept iff it sits in an S slot or is forced
+  {
+    const bool f = t < nb && (slot_of[t] >= nd || slot_of[t] < 0);
     const unsigned long long m = __ballot(f);
     __syncthreads();
-    if (lane == 0) wtot[w] = __popcll(m);
+    if (lane == 0) bks[w] = __popcll(m);
     __syncthreads();
-    int before = 0, total = 0;
-    for (int q = 0; q < 4; ++q) {
-      before += (q < w) ? wtot[q] : 0;
-      total += wtot[q];
-    }
-    if (f) a.col_idx[running + before + lanes_below(m)] = j;
-    running += total;
+    int before = 0;
+    for (int q = 0; q < w; ++q) before += bks[q];
+    if (f) a.col_idx[base + before + lanes_below(m)] = t;
   }
-}
-
-size_t drift_select_lds_bytes(int nb) {
-  return (size_t)nb * kCs * sizeof(float) + (size_t)nb * sizeof(float) + 3 * (size_t)nb * sizeof(int);
 }
 
 hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, int rounds,
                                const float* contrib, int32_t* row_ptr, int32_t* col_idx,
                                float* row_stat, int32_t* swap_log, hipStream_t s) {
   DriftSelArgs a{d, hb, force, rounds, contrib, row_ptr, col_idx, row_stat, swap_log};
-  const size_t lds = drift_select_lds_bytes(d.nb);
-  hipError_t e = hipFuncSetAttribute((const void*)k_select_drift,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int nforced = force ? d.F : 0;
+  size_t gmax = 0;
+  int smax = 0;
+  for (int h = 0; h < d.H; ++h) {
+    gmax = std::max(gmax, (size_t)(d.nb - hb.keep[h]) * (size_t)(hb.keep[h] - nforced));
+    smax = std::max(smax, d.nb - nforced);
+  }
+  const size_t lds_cache = drift_sel_lds(d.nb, smax, gmax).total;
+  const bool cache = rounds > 0 && lds_cache <= kDriftSelLdsCap;
+  const size_t lds = cache ? lds_cache : drift_sel_lds(d.nb, smax, 0).total;
+  const bool small = d.nb * 16 <= 8 * kSelThreads;
+  const void* fn = cache ? (small ? (const void*)k_select_drift<true, 8> : (const void*)k_select_drift<true, 16>)
+                         : (small ? (const void*)k_select_drift<false, 8> : (const void*)k_select_drift<false, 16>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select_drift, dim3(d.rows), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(reinterpret_cast<void (*)(DriftSelArgs)>(const_cast<void*>(fn))),
+                     dim3(d.rows), dim3(kSelThreads), lds, s, a);
   return hipGetLastError();
 }
 

@@ -551,6 +551,30 @@ def test_drift_small_layouts(dev, dtype, block, force):
     say(f"drift small: rows whose final set differs from the oracle's own run: {differ}")
 
 
+def test_drift_512_blocks_uncached_search(dev):
+    """512 key blocks (the largest drift row) with half of them kept: the pair
+    inner products D x S no longer fit in LDS, so every round recomputes them."""
+    lay = custom_layout(32, 1024, 1000, 64, heads=1, dtype="bf16")
+    host, vals = random_inputs(lay, 61)
+    nb = lay.nblocks
+    assert nb == 512
+    keep = np.array([256], dtype=np.int32)
+    rounds = 2
+    say("drift 512 blocks, keep 256, 2 rounds")
+    q, k, v = (to_dev(x, dev) for x in host)
+    contrib, score = bsgm.drift_scores(lay, q, k, v)
+    log = torch.full((nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    swap_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    rows = [(0, i) for i in (0, 1, 255, 511)]
+    differ = check_drift(lay, vals, keep, rounds, False, contrib.cpu().numpy(),
+                         score.cpu().numpy(), rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows)
+    say(f"drift 512: sampled rows whose final set differs from the oracle's own run: {differ}")
+
+
 def test_drift_layer16_full_size_sampled(dev):
     say("drift 16 frames full size")
     w, data = preset(4)
