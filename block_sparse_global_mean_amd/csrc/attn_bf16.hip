@@ -54,6 +54,11 @@ __device__ __forceinline__ void dma16(const void* src, unsigned lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// The same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // Waits until this wave's global->LDS copies have landed.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -98,14 +103,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
     goff[s2] = row * 64 + ((pc ^ swz(row)) << 3);
   }
   const int wv = tid >> 6;
+  unsigned voff[CPT];
+#pragma unroll
+  for (int s3 = 0; s3 < CPT; ++s3) voff[s3] = (unsigned)goff[s3] * 2u;
+  const unsigned lds0 = (unsigned)(uintptr_t)smem + __builtin_amdgcn_readfirstlane(wv) * 1024;
 #define BSGM_DMA(BUF, J)                                                         \
   do {                                                                             \
     const __bf16* kt_ = K + (size_t)(J) * BLK * 64;                                \
     const __bf16* vt_ = V + (size_t)(J) * BLK * 64;                                \
-    const unsigned kb_ = (unsigned)(uintptr_t)(smem + (BUF) * 2 * TB) + wv * 1024; \
+    const unsigned kb_ = lds0 + (BUF) * 2 * TB;                                    \
     _Pragma("unroll") for (int s3 = 0; s3 < CPT; ++s3) {                           \
-      dma16(kt_ + goff[s3], kb_ + s3 * NT * 16);                                 \
-      dma16(vt_ + goff[s3], kb_ + TB + s3 * NT * 16);                            \
+      dma16s(kt_, voff[s3], kb_ + s3 * NT * 16);                                 \
+      dma16s(vt_, voff[s3], kb_ + TB + s3 * NT * 16);                            \
     }                                                                              \
   } while (0)
 
