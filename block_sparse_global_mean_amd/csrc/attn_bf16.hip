@@ -44,18 +44,14 @@ struct AttnArgs {
   float* lse;
 };
 
-// One 16-byte-per-lane global->LDS copy: lane l's 16 bytes at `src` land at LDS
+// One 16-byte-per-lane global->LDS copy: lane l's 16 bytes at sbase + voff (sbase a
+// wave-uniform 64-bit base in SGPRs, voff the lane's byte offset) land at LDS
 // byte address lds + 16*l (lds is wave-uniform; it goes to M0). Issued as an
 // instruction the compiler does not see as an LDS write, so that it does not
 // wait for the copy before every later LDS read; the tile ring orders it
 // instead (wait_dma() and a barrier before the first read of a slot, a barrier
 // between the last read of a slot and the copy that refills it).
-__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-
-// The same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset.
-__device__ __forceinline__ void dma16s(const void* sbase, unsigned voff, unsigned lds) {
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, unsigned lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
@@ -113,8 +109,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
     const __bf16* vt_ = V + (size_t)(J) * BLK * 64;                                \
     const unsigned kb_ = lds0 + (BUF) * 2 * TB;                                    \
     _Pragma("unroll") for (int s3 = 0; s3 < CPT; ++s3) {                           \
-      dma16s(kt_, voff[s3], kb_ + s3 * NT * 16);                                 \
-      dma16s(vt_, voff[s3], kb_ + TB + s3 * NT * 16);                            \
+      dma16(kt_, voff[s3], kb_ + s3 * NT * 16);                                 \
+      dma16(vt_, voff[s3], kb_ + TB + s3 * NT * 16);                            \
     }                                                                              \
   } while (0)
 
