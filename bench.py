@@ -11,6 +11,10 @@ bf16, blocks of 128, 75 % block sparsity.
 Prints one JSON line (see the keys below). `value` is the layer-effective
 throughput: algorithmic FLOP of the executed blocks (4 * 128^2 * 64 per
 executed block pair) divided by the measured time of the whole step.
+`detail.other_layers` gives the per-layer times of the other presets (8 frames
+at 50 %, 100 frames with the cumulative-mass rule and per-head caps, 16 frames
+with drift selection and three restoration rounds), each phase timed over
+back-to-back launches; they are side measurements, not part of `value`.
 """
 from __future__ import annotations
 
@@ -29,7 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_vggt_layer_32f_s75_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_global_mean_amd", "csrc", "attn_bf16.hip")
+CSRC = os.path.join(ROOT, "block_sparse_global_mean_amd", "csrc")
+# the translation unit of the attention kernel
+ATTN_SRCS = [os.path.join(CSRC, f) for f in ("attn_bf16.hip", "device_util.h", "internal.h")]
 
 
 def log(msg):
@@ -37,8 +43,11 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in ATTN_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_per_launch():
@@ -106,7 +115,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB once (counter calibration)")
-    ap.add_argument("--no-drift", action="store_true", help="skip the drift-layer side measurement")
+    ap.add_argument("--no-side", "--no-drift", dest="no_side", action="store_true",
+                    help="skip the per-layer side measurements of the other presets")
+    ap.add_argument("--layer", default=None,
+                    help="time only this other preset (e.g. vggt_layer_16f_drift) and print "
+                         "its per-layer JSON; for profiling its kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -118,6 +131,11 @@ def main():
 
     dev = torch.device("cuda:0")
     bsgm.library()
+    if args.layer:
+        res = side_config(bsgm, workloads, torch, dev, args.layer, args.steps)
+        calibration_copy(torch, dev, args.calib_copy_mib)
+        print(json.dumps({"layer": args.layer, **res}), flush=True)
+        return
     w = workloads.config("vggt_layer_32f_s75")
     lay = w.layout
     log(f"generating {w.name}")
@@ -171,14 +189,7 @@ def main():
     achieved = flops / (attn_avg * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms (select {np.mean(sel_ms):.3f}, attention {attn_avg:.3f})")
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+    calibration_copy(torch, dev, args.calib_copy_mib)
 
     traffic = traffic_per_launch()
     detail = {
@@ -192,8 +203,10 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
 
-    if not args.no_drift:
-        detail["drift_layer_16f"] = drift_side(bsgm, workloads, torch, dev)
+    if not args.no_side:
+        detail["other_layers"] = {
+            name: side_config(bsgm, workloads, torch, dev, name)
+            for name in ("vggt_layer_8f_s50", "vggt_layer_100f_cdf", "vggt_layer_16f_drift")}
 
     out = {
         "metric": "block-sparse global attn effective TFLOP/s + ms/layer, 32 frames, 75% sparse",
@@ -224,49 +237,88 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def drift_side(bsgm, workloads, torch, dev, steps=5):
-    """Side measurement: the 16-frame drift layer (drift scores + 3 swap rounds +
-    attention), not part of `value`."""
-    w = workloads.config("vggt_layer_16f_drift")
+def calibration_copy(torch, dev, mib: int):
+    """One device copy of `mib` MiB: a transfer of known size for scaling the
+    HBM byte counters."""
+    if mib <= 0:
+        return
+    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy of {mib} MiB done")
+
+
+def gpu_ms(torch, fn, reps: int) -> float:
+    """Average GPU time of fn over `reps` back-to-back launches on the current
+    stream (HIP events), after one untimed call."""
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5):
+    """Per-layer times of another preset: selection (drift scores + restoration
+    for the drift preset) and attention, each timed over back-to-back launches."""
+    w = workloads.config(name)
     lay = w.layout
     log(f"generating {w.name}")
     data = workloads.generate(w)
     q, k, v = (to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
     keep = data["keep"]
-    nb, rows = lay.nblocks, lay.heads * lay.nblocks
-    contrib = torch.empty((1, lay.heads, nb, nb, 64), dtype=torch.float32, device=dev)
-    score = torch.empty((1, lay.heads, nb, nb), dtype=torch.float32, device=dev)
-    ws = torch.empty(bsgm.workspace_bytes(lay, bsgm.DRIFT), dtype=torch.uint8, device=dev)
+    nb, rows = lay.nblocks, lay.batch * lay.heads * lay.nblocks
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
-    col_idx = torch.empty(bsgm.col_capacity(lay, bsgm.DRIFT, keep), dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(bsgm.col_capacity(lay, w.mode, keep, w.force_frame_first_block), 1),
+                          dtype=torch.int32, device=dev)
+    ws = torch.empty(bsgm.workspace_bytes(lay, w.mode), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
-    stream = torch.cuda.current_stream()
+    out = {}
+    if w.mode == bsgm.DRIFT:
+        contrib = torch.empty((lay.batch, lay.heads, nb, nb, 64), dtype=torch.float32, device=dev)
+        score = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
 
-    def step():
-        bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws)
-        e1.record(stream)
-        bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=w.swap_rounds,
-                           row_ptr=row_ptr, col_idx=col_idx, want_stat=False)
-        e2.record(stream)
+        def scores():
+            bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws)
+
+        def select():
+            bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=w.swap_rounds,
+                               force=w.force_frame_first_block, row_ptr=row_ptr,
+                               col_idx=col_idx, want_stat=False)
+        out["drift_scores_ms"] = round(gpu_ms(torch, scores, reps), 4)
+        out["drift_select_ms"] = round(gpu_ms(torch, select, reps), 4)
+        sel = out["drift_scores_ms"] + out["drift_select_ms"]
+    else:
+        def select():
+            bsgm.select_blocks(lay, w.mode, keep, q=q, k=k, cdf_tau=w.cdf_tau,
+                               force=w.force_frame_first_block, row_ptr=row_ptr,
+                               col_idx=col_idx, workspace=ws, want_stat=False)
+        out["select_ms"] = round(gpu_ms(torch, select, reps), 4)
+        sel = out["select_ms"]
+
+    def attend():
         bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o)
-
-    e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-    step()
-    torch.cuda.synchronize()
-    t = np.zeros(3)
-    for _ in range(steps):
-        e0.record(stream)
-        step()
-        e3.record(stream)
-        torch.cuda.synchronize()
-        t += [e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3)]
-    t /= steps
+    attn = gpu_ms(torch, attend, reps)
     executed = int(row_ptr[-1].item())
     flops = executed * 4.0 * lay.block ** 2 * lay.head_dim
-    return {"drift_scores_ms": round(t[0], 4), "drift_select_ms": round(t[1], 4),
-            "attn_ms": round(t[2], 4), "ms_per_layer": round(float(t.sum()), 4),
-            "layer_effective_tflops": round(flops / (t.sum() * 1e-3) / 1e12, 2),
-            "attn_effective_tflops": round(flops / (t[2] * 1e-3) / 1e12, 2)}
+    out.update({
+        "attn_ms": round(attn, 4),
+        "ms_per_layer": round(sel + attn, 4),
+        "executed_block_pairs": executed,
+        "measured_block_sparsity": round(1.0 - executed / (rows * nb), 6),
+        "attn_effective_tflops": round(flops / (attn * 1e-3) / 1e12, 2),
+        "layer_effective_tflops": round(flops / ((sel + attn) * 1e-3) / 1e12, 2),
+    })
+    del q, k, v, o, data
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
