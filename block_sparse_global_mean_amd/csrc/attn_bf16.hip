@@ -52,7 +52,12 @@ struct AttnArgs {
 // instead (wait_dma() and a barrier before the first read of a slot, a barrier
 // between the last read of a slot and the copy that refills it).
 __device__ __forceinline__ void dma16(const void* sbase, unsigned voff, unsigned lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(bs)),
+               "{m0}"(lds)
+               : "memory");
 }
 
 // Waits until this wave's global->LDS copies have landed.
