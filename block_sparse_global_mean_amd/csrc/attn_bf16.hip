@@ -74,7 +74,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   __shared__ int colbuf[CB];
 
   const Dims& d = a.d;
-  const int r = xcd_remap(blockIdx.x, d.rows);
+  const int r = head_sync_row(blockIdx.x, d.nb);
+  if (r < 0) return;
   const int bh = r / d.nb, i = r - bh * d.nb;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -276,9 +277,9 @@ hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const v
   AttnArgs a{d, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
              (__bf16*)o, lse};
   if (d.blk == 128)
-    hipLaunchKernelGGL(k_attn_bf16<128>, dim3(d.rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16<128>, dim3(head_sync_grid(d)), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16<64>, dim3(d.rows), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16<64>, dim3(head_sync_grid(d)), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

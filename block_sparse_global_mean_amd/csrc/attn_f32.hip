@@ -24,7 +24,8 @@ __global__ __launch_bounds__(BLK) void k_attn_f32(AttnF32Args a) {
   __shared__ float4 Ks[BLK * 16];
   __shared__ float4 Vs[BLK * 16];
   const Dims& d = a.d;
-  const int r = xcd_remap(blockIdx.x, d.rows);
+  const int r = head_sync_row(blockIdx.x, d.nb);
+  if (r < 0) return;
   const int bh = r / d.nb, i = r - bh * d.nb;
   const int t = threadIdx.x;
   const size_t hoff = (size_t)bh * d.N * 64;
@@ -117,9 +118,9 @@ hipError_t launch_attn_f32(const Dims& d, const void* q, const void* k, const vo
   AttnF32Args a{d, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
                 (float*)o, lse};
   if (d.blk == 128)
-    hipLaunchKernelGGL(k_attn_f32<128>, dim3(d.rows), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn_f32<128>, dim3(head_sync_grid(d)), dim3(128), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_f32<64>, dim3(d.rows), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_attn_f32<64>, dim3(head_sync_grid(d)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

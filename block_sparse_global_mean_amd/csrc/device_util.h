@@ -144,13 +144,21 @@ __device__ __forceinline__ bf16x8 v_frag(const unsigned char* vb, int kbase, int
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Maps a dispatch index to a work index so that the workgroups that one XCD
-// (dispatch index mod 8) runs take consecutive work items: neighbouring rows
-// of one head then share that XCD's L2. Bijective on [0, n).
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = n >> 3;
-  if (bid >= per * 8) return bid;
-  return (bid & 7) * per + (bid >> 3);
+// Dispatch order of the per-(b, h, query block) attention grids. Workgroups
+// are dispatched to the 8 XCDs round-robin (dispatch index mod 8). The k-th
+// workgroup of XCD x takes query block x*c + k % c of head k / c, c = ceil(nb/8):
+// all XCDs work on the same head at once, so one head's K and V (not eight) is
+// the working set of the shared Infinity Cache, and each XCD sweeps a
+// contiguous eighth of that head's query blocks, whose kept lists overlap,
+// through its own L2. Returns the row (b*H + h)*nb + i, or -1 for the padding
+// indices of a head (i >= nb). The grid has head_sync_grid(d) workgroups.
+__device__ __forceinline__ int head_sync_row(int bid, int nb) {
+  const int c = (nb + 7) >> 3;
+  const int x = bid & 7, k = bid >> 3;
+  const int bh = k / c, i = x * c + (k - bh * c);
+  return i < nb ? bh * nb + i : -1;
 }
+
+inline int head_sync_grid(const Dims& d) { return d.B * d.H * 8 * ((d.nb + 7) / 8); }
 
 }  // namespace bsgm
