@@ -317,5 +317,27 @@ def dense_attention(q, k, v, layout) -> Tuple[np.ndarray, np.ndarray]:
     return o, lse
 
 
+def special_rows_dense(q, k, v, layout, o, lse, n_special: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Camera and register query rows keep dense attention (VASC section 4.2 and
+    A.5): in every frame the first n_special tokens (the special tokens, at the
+    start of the frame) attend over all real keys of their (b, h); every other
+    row keeps the given output. Returns new (o, lse) arrays.
+    """
+    B, H, N, D = q.shape
+    o2 = np.array(o, dtype=np.float64, copy=True)
+    l2 = np.array(lse, dtype=np.float64, copy=True)
+    keys = np.nonzero(valid_mask(layout))[0]
+    rows = np.array([f * layout.frame_len + p for f in range(layout.frames) for p in range(n_special)],
+                    dtype=np.int64)
+    if not len(rows):
+        return o2, l2
+    for b in range(B):
+        for h in range(H):
+            ob, lb = attention_rows(q[b, h, rows], k[b, h, keys], v[b, h, keys], layout.scale)
+            o2[b, h, rows] = ob
+            l2[b, h, rows] = lb
+    return o2, l2
+
+
 def executed_block_pairs(row_ptr) -> int:
     return int(row_ptr[-1])

@@ -186,3 +186,45 @@ def test_empty_block_list_gives_zero_output():
     q, k, v = rand_qkv(lay, 9)
     o, lse = oracle.sparse_attention_row(q[0, 0], k[0, 0], v[0, 0], lay, 1, [])
     assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+@pytest.mark.parametrize("n_special", [1, 2])
+def test_special_rows_dense_brute_force(n_special):
+    """Camera/register rows (the first n_special tokens of every frame) attend
+    over every real key; all other rows keep the sparse output unchanged."""
+    lay = layout(frames=3)
+    q, k, v = rand_qkv(lay, 12)
+    nb = oracle.num_blocks(lay)
+    rng = np.random.default_rng(13)
+    kept = [sorted(rng.choice(nb, size=2, replace=False).tolist()) for _ in range(nb)]
+    rp, ci = kept_to_csr(kept)
+    o, lse = oracle.sparse_attention(q, k, v, lay, rp, ci)
+    o2, l2 = oracle.special_rows_dense(q, k, v, lay, o, lse, n_special)
+    dense_ref = brute_force(q, k, v, lay, [list(range(nb))] * nb)
+    N = lay.frames * lay.frame_len
+    special = np.array([(t % lay.frame_len) < n_special for t in range(N)])
+    np.testing.assert_allclose(o2[0, 0, special], dense_ref[special], rtol=0, atol=1e-13)
+    assert np.array_equal(o2[0, 0, ~special], o[0, 0, ~special])
+    assert np.array_equal(l2[0, 0, ~special], lse[0, 0, ~special])
+    # lse of a special row: log of the sum of exp over all real keys, written out
+    t = lay.frame_len + n_special - 1
+    keys = [u for u in range(N) if u % lay.frame_len < lay.frame_valid]
+    s = [lay.scale * sum(q[0, 0, t, d] * k[0, 0, u, d] for d in range(lay.head_dim)) for u in keys]
+    m = max(s)
+    assert abs(l2[0, 0, t] - (m + math.log(sum(math.exp(x - m) for x in s)))) <= 1e-12
+
+
+def test_special_rows_dense_limits():
+    """n_special = 0 changes nothing; n_special = frame_valid makes every real
+    row dense, which is the oracle's dense attention (itself pinned to SDPA)."""
+    lay = layout(frames=2)
+    q, k, v = rand_qkv(lay, 14)
+    nb = oracle.num_blocks(lay)
+    kept = [[i] for i in range(nb)]
+    o, lse = oracle.sparse_attention(q, k, v, lay, *kept_to_csr(kept))
+    o0, l0 = oracle.special_rows_dense(q, k, v, lay, o, lse, 0)
+    assert np.array_equal(o0, o) and np.array_equal(l0, lse)
+    oa, la = oracle.special_rows_dense(q, k, v, lay, o, lse, lay.frame_valid)
+    od, ld = oracle.dense_attention(q, k, v, lay)
+    np.testing.assert_allclose(oa, od, atol=1e-13)
+    np.testing.assert_allclose(la, ld, atol=1e-13)
