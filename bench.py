@@ -203,6 +203,18 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
 
+    # dense camera/register rows (5 per frame) on the same layer, after the sparse pass
+    ns = 5
+    sws = torch.empty(bsgm.special_rows_workspace_bytes(lay, ns), dtype=torch.uint8, device=dev)
+    sp_ms = gpu_ms(torch, lambda: bsgm.special_rows_dense_fwd(lay, q, k, v, ns, o, workspace=sws),
+                   10)
+    real_keys = lay.frames * lay.frame_valid
+    sp_flops = 4.0 * lay.batch * lay.heads * lay.frames * ns * real_keys * lay.head_dim
+    detail["special_rows_dense"] = {
+        "rows_per_frame": ns, "ms": round(sp_ms, 4),
+        "gflop": round(sp_flops / 1e9, 3),
+        "tflops": round(sp_flops / (sp_ms * 1e-3) / 1e12, 2)}
+
     if not args.no_side:
         detail["other_layers"] = {
             name: side_config(bsgm, workloads, torch, dev, name)

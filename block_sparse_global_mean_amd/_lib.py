@@ -23,7 +23,8 @@ STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_
 
 # Every symbol include/bsgm.h declares.
 EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_capacity",
-           "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd")
+           "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
+           "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd")
 
 
 class BsgmError(RuntimeError):
@@ -69,6 +70,9 @@ def library() -> ctypes.CDLL:
         lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                            vp, sz, vp]
         lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.bsgm_special_rows_workspace_bytes.argtypes = [lp, ctypes.c_int32]
+        lib.bsgm_special_rows_workspace_bytes.restype = sz
+        lib.bsgm_special_rows_dense_fwd.argtypes = [lp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
         for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
                      "bsgm_sparse_attn_fwd"):
             getattr(lib, name).restype = ctypes.c_int
@@ -227,4 +231,30 @@ def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_ls
     _check(library().bsgm_sparse_attn_fwd(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
                                           _stream(stream)))
+    return o, lse
+
+
+def special_rows_workspace_bytes(layout, n_special: int) -> int:
+    L = c_layout(layout)
+    nbytes = library().bsgm_special_rows_workspace_bytes(ctypes.byref(L), int(n_special))
+    if nbytes == 0:
+        raise BsgmError(-1, library().bsgm_last_error().decode())
+    return nbytes
+
+
+def special_rows_dense_fwd(layout, q, k, v, n_special: int, o, lse=None, workspace=None,
+                           stream=None):
+    """Dense attention of the first n_special tokens of every frame, written into
+    the matching rows of o (and lse); returns (o, lse)."""
+    n, nb, rows = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, name, _tdtype(layout), shape)
+    if workspace is None:
+        workspace = torch.empty(special_rows_workspace_bytes(layout, n_special), dtype=torch.uint8,
+                                device=q.device)
+    L = c_layout(layout)
+    _check(library().bsgm_special_rows_dense_fwd(
+        ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), int(n_special), _ptr(o), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, lse

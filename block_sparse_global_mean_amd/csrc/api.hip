@@ -76,7 +76,7 @@ int check_layout(const bsgm_layout* L, bsgm::Dims* d) {
   return BSGM_OK;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+using bsgm::align256;
 
 struct WsLayout {
   size_t qbar, kbar, counts, bitmask, stats, mz, total;
@@ -188,6 +188,37 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
     e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, s);
   }
   if (e != hipSuccess) return hip_fail(e, "drift launch");
+  return ok();
+}
+
+size_t bsgm_special_rows_workspace_bytes(const bsgm_layout* layout, int32_t n_special) {
+  bsgm::Dims d;
+  if (check_layout(layout, &d) != BSGM_OK) return 0;
+  if (n_special < 1 || n_special > d.Lv) {
+    fail(BSGM_E_ARG, "n_special = %d outside [1, frame_valid = %d]", n_special, d.Lv);
+    return 0;
+  }
+  ok();
+  const bsgm::DenseRowsPlan p = bsgm::dense_rows_plan(d, n_special);
+  return align256(p.po_bytes) + align256(p.pml_bytes);
+}
+
+int bsgm_special_rows_dense_fwd(const bsgm_layout* layout, const void* q, const void* k,
+                                const void* v, int32_t n_special, void* o, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  if (layout->dtype != BSGM_BF16)
+    return fail(BSGM_E_UNSUPPORTED, "special rows: dtype must be BSGM_BF16");
+  if (!q || !k || !v || !o || !ws) return fail(BSGM_E_ARG, "q, k, v, o and ws must be non-NULL");
+  if (n_special < 1 || n_special > d.Lv)
+    return fail(BSGM_E_ARG, "n_special = %d outside [1, frame_valid = %d]", n_special, d.Lv);
+  const bsgm::DenseRowsPlan p = bsgm::dense_rows_plan(d, n_special);
+  const size_t need = align256(p.po_bytes) + align256(p.pml_bytes);
+  if (ws_bytes < need) return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  hipError_t e = bsgm::launch_dense_rows(d, n_special, q, k, v, o, lse, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "special rows launch");
   return ok();
 }
 

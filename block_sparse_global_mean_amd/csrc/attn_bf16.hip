@@ -44,25 +44,6 @@ struct AttnArgs {
   float* lse;
 };
 
-// One 16-byte-per-lane global->LDS copy: lane l's 16 bytes at sbase + voff (sbase a
-// wave-uniform 64-bit base in SGPRs, voff the lane's byte offset) land at LDS
-// byte address lds + 16*l (lds is wave-uniform; it goes to M0). Issued as an
-// instruction the compiler does not see as an LDS write, so that it does not
-// wait for the copy before every later LDS read; the tile ring orders it
-// instead (wait_dma() and a barrier before the first read of a slot, a barrier
-// between the last read of a slot and the copy that refills it).
-__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, unsigned lds) {
-  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-  const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(bs)),
-               "{m0}"(lds)
-               : "memory");
-}
-
-// Waits until this wave's global->LDS copies have landed.
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   constexpr int NT = BLK * 2;          // threads (BLK/32 waves)

@@ -61,6 +61,17 @@ hipError_t launch_attn_f32(const Dims& d, const void* q, const void* k, const vo
                            const int32_t* row_ptr, const int32_t* col_idx, void* o,
                            float* lse, hipStream_t s);
 
+// Dense attention of the camera/register rows: work split and scratch sizes.
+struct DenseRowsPlan {
+  int nrows, ngroups, cpc, nchunks;
+  size_t po_bytes, pml_bytes;
+};
+DenseRowsPlan dense_rows_plan(const Dims& d, int ns);
+hipError_t launch_dense_rows(const Dims& d, int ns, const void* q, const void* k, const void* v,
+                             void* o, float* lse, void* ws, hipStream_t s);
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 // Largest key-block count the drift selection keeps in LDS.
 constexpr int kDriftMaxBlocks = 512;
 // Largest block count a pooled selection row handles (16 per thread x 256).

@@ -173,6 +173,26 @@ int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k
                          const int32_t* row_ptr, const int32_t* col_idx,
                          void* o, float* lse, void* stream);
 
+/* Dense attention of the camera and register query rows ([VASC] 4.2 and A.5:
+ * camera and register queries keep dense attention while patch queries use the
+ * selected blocks). In every frame the first n_special tokens (the special
+ * tokens, which open each frame) attend over all real keys of their (b, h):
+ *   o_t = sum_u exp(scale <q_t,k_u> - m_t) v_u / sum_u exp(scale <q_t,k_u> - m_t),
+ *   lse_t = m_t + log(sum_u exp(scale <q_t,k_u> - m_t)), over every real key u.
+ * Only those rows of o and lse are written; run it after bsgm_sparse_attn_fwd
+ * to replace their sparse result. bf16 only (BSGM_E_UNSUPPORTED otherwise).
+ *   n_special  1..frame_valid special tokens per frame (VGGT: camera + 4 registers = 5)
+ *   q, k, v    device [B,H,N,D] bf16
+ *   o          device [B,H,N,D] bf16, rows f*frame_len + p (p < n_special) written
+ *   lse        device float [B,H,N] or NULL, the same rows written
+ *   ws         device, >= bsgm_special_rows_workspace_bytes(layout, n_special) bytes
+ *              (per-chunk partial results of the split over key blocks)
+ */
+size_t bsgm_special_rows_workspace_bytes(const bsgm_layout* layout, int32_t n_special);
+int bsgm_special_rows_dense_fwd(const bsgm_layout* layout, const void* q, const void* k,
+                                const void* v, int32_t n_special, void* o, float* lse,
+                                void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -118,3 +118,23 @@ def test_pool_and_drift_null_arguments():
     assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, None, one, one, 1 << 20, None) == -1
     assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, one, 10, None) == -4
     assert lib.bsgm_pool_blocks(None, one, one, None) == -1
+
+
+def test_special_rows_workspace_and_errors():
+    lib = bsgm.library()
+    lay = L()                                  # 2 heads, 4 frames x 256 (250 real), block 128
+    c = _lib.c_layout(lay)
+    nbytes = lib.bsgm_special_rows_workspace_bytes(ctypes.byref(c), 5)
+    # 4 frames x 5 rows = 20 rows -> one group of 128; chunks of >= 4 of the 8 key blocks
+    assert nbytes == 2 * 128 * 64 * 4 * 2 + 2 * 128 * 2 * 4 * 2
+    assert lib.bsgm_special_rows_workspace_bytes(ctypes.byref(c), 0) == 0
+    assert lib.bsgm_special_rows_workspace_bytes(ctypes.byref(c), 251) == 0
+    one = ctypes.c_void_p(16)
+    f = lib.bsgm_special_rows_dense_fwd
+    assert f(ctypes.byref(c), one, one, one, 5, one, None, one, nbytes - 1, None) == -4
+    assert f(ctypes.byref(c), one, one, one, 0, one, None, one, nbytes, None) == -1
+    assert f(ctypes.byref(c), None, one, one, 5, one, None, one, nbytes, None) == -1
+    assert f(ctypes.byref(c), one, one, one, 5, None, None, one, nbytes, None) == -1
+    c32 = _lib.c_layout(L(dtype="f32"))
+    assert f(ctypes.byref(c32), one, one, one, 5, one, None, one, nbytes, None) == -2
+    assert lib.bsgm_last_error().decode() != ""

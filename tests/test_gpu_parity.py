@@ -609,3 +609,76 @@ def test_drift_layer16_full_size_sampled(dev):
         assert_outputs(lay, og, o_ref, valid, f"drift sampled row (h={h}, i={i})")
         compared += 1
     say(f"drift full size: sampled rows with oracle-equal lists compared: {compared}")
+
+
+# --------------------------------------------------------------------------
+# dense camera/register query rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("block,ns", [(128, 5), (64, 5), (128, 50)])
+def test_special_rows_dense_on_sparse_output(dev, block, ns):
+    """Sparse attention on random kept lists, then the first ns tokens of every
+    frame recomputed densely; the whole output against the oracle's composite."""
+    lay = custom_layout(6, 4 * block, 4 * block - 37, block, heads=2, batch=2)
+    host, vals = random_inputs(lay, 71 + block + ns)
+    nb = lay.nblocks
+    rng = np.random.default_rng(9)
+    rows = [sorted(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+            for _ in range(lay.batch * lay.heads * nb)]
+    say(f"special rows {ns} per frame, block {block}")
+    q, k, v = (to_dev(x, dev) for x in host)
+    rp, ci = upload_csr(rows, dev)
+    o, lse = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True)
+    bsgm.special_rows_dense_fwd(lay, q, k, v, ns, o, lse)
+    torch.cuda.synchronize()
+    row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    col_idx = np.array([j for r in rows for j in r], dtype=np.int64)
+    o_s, l_s = oracle.sparse_attention(vals[0], vals[1], vals[2], lay, row_ptr, col_idx)
+    o_ref, l_ref = oracle.special_rows_dense(vals[0], vals[1], vals[2], lay, o_s, l_s, ns)
+    valid = oracle.valid_mask(lay)
+    assert_outputs(lay, o.float().cpu().numpy(), o_ref, valid, f"special rows ns={ns} block {block}")
+    lse_g = lse.cpu().numpy()
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(lse_g), fin)
+    assert np.abs(lse_g[fin] - l_ref[fin]).max() <= 2e-3 * max(1.0, np.abs(l_ref[fin]).max())
+
+
+def test_special_rows_all_rows_is_dense(dev):
+    """n_special = frame_valid: every real row dense, i.e. dense attention."""
+    lay = custom_layout(3, 256, 230, 128, heads=2)
+    host, vals = random_inputs(lay, 81)
+    q, k, v = (to_dev(x, dev) for x in host)
+    o = torch.zeros_like(q)
+    lse = torch.full((lay.batch, lay.heads, lay.tokens), -float("inf"), device=dev)
+    bsgm.special_rows_dense_fwd(lay, q, k, v, lay.frame_valid, o, lse)
+    torch.cuda.synchronize()
+    od, ld = oracle.dense_attention(*vals, lay)
+    valid = oracle.valid_mask(lay)
+    assert_outputs(lay, o.float().cpu().numpy(), od, valid, "all rows special vs dense")
+    assert np.abs(lse.cpu().numpy()[..., valid] - ld[..., valid]).max() <= 2e-3 * np.abs(ld[..., valid]).max()
+    assert torch.all(o[..., torch.from_numpy(~valid).to(dev), :] == 0)
+
+
+def test_special_rows_full_size_sampled(dev):
+    """32-frame layer at full size: special rows of two heads, sampled, against
+    the oracle's softmax over all real keys."""
+    w, data = preset(2)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((lay.batch, lay.heads, lay.tokens), dtype=torch.float32, device=dev)
+    say("special rows 32 frames full size")
+    bsgm.special_rows_dense_fwd(lay, q, k, v, 5, o, lse)
+    torch.cuda.synchronize()
+    og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    keys = np.nonzero(oracle.valid_mask(lay))[0]
+    for h in (0, 15):
+        toks = np.array([f * lay.frame_len + p for f in (0, 13, 31) for p in (0, 4)])
+        orf, lrf = oracle.attention_rows(data["q"][0, h, toks], data["k"][0, h, keys],
+                                         data["v"][0, h, keys], lay.scale)
+        for n, t in enumerate(toks):
+            err = np.abs(og[0, h, t] - orf[n]).max()
+            allow = 2e-2 * np.sqrt((orf[n] ** 2).mean())
+            assert err <= allow, (h, t, err, allow)
+            assert abs(lg[0, h, t] - lrf[n]) <= 2e-3 * max(1.0, abs(lrf[n]))
+        # rows that are not special are left alone
+        assert float(np.abs(og[0, h, 5:lay.frame_len]).max()) == 0.0
