@@ -196,17 +196,78 @@ def drift_j(chat: np.ndarray, kept: Sequence[int]) -> float:
     return float(math.sqrt(float(r @ r)))
 
 
+# Drift objectives: RAW is the norm of the summed dropped contributions (the
+# objective the restoration above minimises); RENORM is the shift of the pooled
+# query's attention output once the dropped blocks are removed and the kept
+# weights renormalised, (C - C_D)/(Z - Z_D) - C/Z (ReSS Fig. 3(a): masking a
+# block shifts what attention writes into the residual stream).
+RAW, RENORM = 0, 1
+
+
+def drift_j_renorm(chat: np.ndarray, zhat: np.ndarray, kept: Sequence[int]) -> float:
+    """|| sum_{j in S} chat_j / sum_{j in S} zhat_j - sum_j chat_j || for the kept set S,
+    with chat_j = c_j / Z and zhat_j = z_j / Z (so sum_j zhat_j = 1)."""
+    S = sorted(set(kept))
+    obar = chat.sum(axis=0)
+    zs = float(zhat[S].sum()) if S else 0.0
+    if zs <= 0.0:
+        return math.inf
+    u = chat[S].sum(axis=0) / zs - obar
+    return float(math.sqrt(float(u @ u)))
+
+
+def restore_row_renorm(chat: np.ndarray, zhat: np.ndarray, k: int, rounds: int,
+                       forced: Sequence[int] = ()) -> Tuple[List[int], float, List[Tuple[int, int]]]:
+    """Drift selection at budget k under the RENORM objective.
+
+    The initial kept set is that of restore_row (forced blocks, then the highest
+    ||chat_j||). Each round evaluates every swap (restore a dropped block a, drop
+    a kept non-forced block b) by the renormalised drift of the resulting set,
+    J^2 = || (C_S + chat_a - chat_b) / (Z_S + zhat_a - zhat_b) - sum_j chat_j ||^2,
+    takes the least (ties: lower a, then lower b) and makes it only if it lowers
+    J; otherwise the procedure stops. Returns (kept ascending, final J, swaps).
+    """
+    nb = chat.shape[0]
+    d = np.sqrt((chat * chat).sum(axis=1))
+    kept = set(priority_order(d, forced)[:k])
+    fset = set(forced)
+    obar = chat.sum(axis=0)
+    swaps: List[Tuple[int, int]] = []
+    for _ in range(rounds):
+        drop = sorted(set(range(nb)) - kept)
+        cand_b = sorted(kept - fset)
+        if not drop or not cand_b:
+            break
+        S = sorted(kept)
+        cs, zs = chat[S].sum(axis=0), float(zhat[S].sum())
+        cur = drift_j_renorm(chat, zhat, S) ** 2
+        c2 = cs[None, None, :] + chat[drop][:, None, :] - chat[cand_b][None, :, :]
+        z2 = zs + zhat[drop][:, None] - zhat[cand_b][None, :]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            u = c2 / z2[:, :, None] - obar[None, None, :]
+            j2 = np.where(z2 > 0, (u * u).sum(axis=-1), np.inf)
+        flat = int(np.argmin(j2))
+        ia, ib = divmod(flat, len(cand_b))
+        if not j2[ia, ib] < cur:
+            break
+        a, b = drop[ia], cand_b[ib]
+        kept.remove(b)
+        kept.add(a)
+        swaps.append((a, b))
+    return sorted(kept), drift_j_renorm(chat, zhat, sorted(kept)), swaps
+
+
 # --------------------------------------------------------------------------
 # Whole-layer selection and CSR emission.
 # --------------------------------------------------------------------------
 def select(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout, mode: int,
            keep: Sequence[int], tau: float = 0.9, force: bool = False,
-           rounds: int = 0):
+           rounds: int = 0, objective: int = RAW):
     """Kept key blocks for every (b, h, query block).
 
     Returns (sets, row_stat) where sets[b][h][i] is an ascending list and
     row_stat[b,h,i] is the kept pooled mass (TOPK, CDF) or the final drift J
-    (DRIFT).
+    (DRIFT, under the given objective).
     """
     B, H = q.shape[0], q.shape[1]
     nb = num_blocks(layout)
@@ -231,8 +292,11 @@ def select(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout, mode: int,
         for b in range(B):
             for h in range(H):
                 for i in range(nb):
-                    chat, _, _ = drift_row(qbar[b, h, i], k[b, h], v[b, h], layout)
-                    kept, j, _ = restore_row(chat, int(keep[h]), rounds, forced)
+                    chat, z, Z = drift_row(qbar[b, h, i], k[b, h], v[b, h], layout)
+                    if objective == RENORM:
+                        kept, j, _ = restore_row_renorm(chat, z / Z, int(keep[h]), rounds, forced)
+                    else:
+                        kept, j, _ = restore_row(chat, int(keep[h]), rounds, forced)
                     sets[b][h][i] = kept
                     stat[b, h, i] = j
     else:

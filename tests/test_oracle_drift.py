@@ -138,3 +138,65 @@ def test_drift_selection_planted_block():
     k[0, 0, 8:12, 2] += 3.0
     sets, stat = oracle.select(q, k, v, lay, oracle.DRIFT, [1], rounds=3)
     assert sets[0][0][0] == [2]
+
+
+def _output_shift_by_attention(qbar, k, v, lay, kept):
+    """The renormalised drift written as two attention computations: the pooled
+    query attending to the real keys of the kept blocks only, minus the same
+    query attending densely (oracle.attention_rows, a separate code path)."""
+    valid = oracle.valid_mask(lay)
+    keys = np.concatenate([oracle.block_tokens(lay, j) for j in sorted(kept)])
+    o_s, _ = oracle.attention_rows(qbar[None], k[keys], v[keys], lay.scale)
+    o_d, _ = oracle.attention_rows(qbar[None], k[valid], v[valid], lay.scale)
+    return float(np.sqrt(((o_s[0] - o_d[0]) ** 2).sum()))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_renormalised_drift_is_the_output_shift(seed):
+    lay = layout(frames=3, frame_len=8, frame_valid=6, block=4, D=5, scale=0.8)
+    k, v = rand_kv(lay, 20 + seed)
+    qbar = np.random.default_rng(30 + seed).standard_normal(5)
+    chat, z, Z = oracle.drift_row(qbar, k, v, lay)
+    nb = oracle.num_blocks(lay)
+    rng = np.random.default_rng(40 + seed)
+    for _ in range(5):
+        kept = sorted(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+        assert oracle.drift_j_renorm(chat, z / Z, kept) == pytest.approx(
+            _output_shift_by_attention(qbar, k, v, lay, kept), rel=1e-10, abs=1e-13)
+    assert oracle.drift_j_renorm(chat, z / Z, list(range(nb))) == pytest.approx(0.0, abs=1e-14)
+
+
+@pytest.mark.parametrize("seed,force,swapped", [(1, False, True), (3, True, True), (6, False, True),
+                                               (0, False, False)])
+def test_renormalised_restoration_takes_the_best_swap(seed, force, swapped):
+    """Every round's swap is the best single swap by the output shift computed
+    with attention_rows, every stop is justified, and J never rises."""
+    lay = layout(frames=3, frame_len=8, frame_valid=6, block=2, D=4, scale=0.9)
+    k, v = rand_kv(lay, 50 + seed)
+    qbar = np.random.default_rng(60 + seed).standard_normal(4) * 1.5
+    chat, z, Z = oracle.drift_row(qbar, k, v, lay)
+    nb = oracle.num_blocks(lay)
+    forced = oracle.forced_blocks(lay, force)
+    kbudget = 5
+    kept, j_final, swaps = oracle.restore_row_renorm(chat, z / Z, kbudget, 6, forced)
+    d = np.sqrt((chat * chat).sum(axis=1))
+    # replay: each logged swap is the best one and lowers J; the stop is justified
+    cur = set(oracle.priority_order(d, forced)[:kbudget])
+    j_cur = _output_shift_by_attention(qbar, k, v, lay, cur)
+    for a, b in swaps:
+        cands = [(aa, bb) for aa in sorted(set(range(nb)) - cur) for bb in sorted(cur - set(forced))]
+        scored = sorted((_output_shift_by_attention(qbar, k, v, lay, (cur - {bb}) | {aa}), aa, bb)
+                        for aa, bb in cands)
+        assert (scored[0][1], scored[0][2]) == (a, b) or scored[0][0] == pytest.approx(
+            _output_shift_by_attention(qbar, k, v, lay, (cur - {b}) | {a}), rel=1e-12)
+        j_new = _output_shift_by_attention(qbar, k, v, lay, (cur - {b}) | {a})
+        assert j_new < j_cur
+        cur = (cur - {b}) | {a}
+        j_cur = j_new
+    if len(swaps) < 6:
+        cands = [(aa, bb) for aa in sorted(set(range(nb)) - cur) for bb in sorted(cur - set(forced))]
+        assert all(_output_shift_by_attention(qbar, k, v, lay, (cur - {bb}) | {aa}) >= j_cur * (1 - 1e-12)
+                   for aa, bb in cands)
+    assert sorted(cur) == kept
+    assert j_final == pytest.approx(j_cur, rel=1e-10)
+    assert (len(swaps) >= 1) == swapped
