@@ -304,6 +304,20 @@ def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5):
             bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=w.swap_rounds,
                                force=w.force_frame_first_block, row_ptr=row_ptr,
                                col_idx=col_idx, want_stat=False)
+        # the renormalised objective on the same layer (scores with block masses)
+        zmass = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+
+        def scores_z():
+            bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws,
+                              zmass=zmass)
+
+        def select_z():
+            bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=w.swap_rounds,
+                               force=w.force_frame_first_block, row_ptr=row_ptr,
+                               col_idx=col_idx, want_stat=False,
+                               objective=bsgm.RENORMALISED, zmass=zmass)
+        out["renorm_drift_scores_ms"] = round(gpu_ms(torch, scores_z, reps), 4)
+        out["renorm_drift_select_ms"] = round(gpu_ms(torch, select_z, reps), 4)
         out["drift_scores_ms"] = round(gpu_ms(torch, scores, reps), 4)
         out["drift_select_ms"] = round(gpu_ms(torch, select, reps), 4)
         sel = out["drift_scores_ms"] + out["drift_select_ms"]

@@ -7,7 +7,7 @@ libbsgm.so; this package is the thin ctypes binding to its C ABI
 (include/bsgm.h).
 """
 from ._lib import (  # noqa: F401
-    BF16, CDF, DRIFT, F32, TOPK, BsgmError, EXPORTS, LIB_PATH, col_capacity, drift_scores,
+    BF16, CDF, DRIFT, DROPPED_SUM, F32, RENORMALISED, TOPK, BsgmError, EXPORTS, LIB_PATH, col_capacity, drift_scores,
     library, pool_blocks, select_blocks, sparse_attn_fwd, special_rows_dense_fwd,
     special_rows_workspace_bytes, version, workspace_bytes,
 )

@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(HERE, "libbsgm.so")
 
 F32, BF16 = 0, 1
 TOPK, CDF, DRIFT = 0, 1, 2
+# Drift objectives: the norm of the dropped blocks' summed contribution, or the
+# output shift after the kept blocks are renormalised.
+DROPPED_SUM, RENORMALISED = 0, 1
 
 STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_CAPACITY",
           -4: "BSGM_E_WORKSPACE", -5: "BSGM_E_HIP"}
@@ -43,7 +46,7 @@ class CLayout(ctypes.Structure):
 class CSelectParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("keep_per_head", ctypes.POINTER(ctypes.c_int32)),
                 ("cdf_tau", ctypes.c_float), ("force_frame_first_block", ctypes.c_int32),
-                ("swap_rounds", ctypes.c_int32)]
+                ("swap_rounds", ctypes.c_int32), ("drift_objective", ctypes.c_int32)]
 
 
 _lib = None
@@ -66,8 +69,8 @@ def library() -> ctypes.CDLL:
         lib.bsgm_col_capacity.argtypes = [lp, pp]
         lib.bsgm_col_capacity.restype = ctypes.c_int64
         lib.bsgm_pool_blocks.argtypes = [lp, vp, vp, vp]
-        lib.bsgm_drift_scores.argtypes = [lp, vp, vp, vp, vp, vp, vp, sz, vp]
-        lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
+        lib.bsgm_drift_scores.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                            vp, sz, vp]
         lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.bsgm_special_rows_workspace_bytes.argtypes = [lp, ctypes.c_int32]
@@ -91,9 +94,9 @@ def c_layout(layout) -> CLayout:
 
 
 def c_params(mode: int, keep: Sequence[int], cdf_tau: float = 0.9, force: bool = False,
-             swap_rounds: int = 0) -> Tuple[CSelectParams, ctypes.Array]:
+             swap_rounds: int = 0, objective: int = 0) -> Tuple[CSelectParams, ctypes.Array]:
     arr = (ctypes.c_int32 * len(keep))(*[int(x) for x in keep])
-    return CSelectParams(mode, arr, cdf_tau, 1 if force else 0, swap_rounds), arr
+    return CSelectParams(mode, arr, cdf_tau, 1 if force else 0, swap_rounds, objective), arr
 
 
 def _check(code: int):
@@ -161,8 +164,12 @@ def pool_blocks(layout, x: torch.Tensor, out: Optional[torch.Tensor] = None, str
     return out
 
 
-def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stream=None):
-    """Drift contributions [B,H,Nb,Nb,64] and their norms [B,H,Nb,Nb] (float32)."""
+def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stream=None,
+                 zmass=None):
+    """Drift contributions [B,H,Nb,Nb,64] and their norms [B,H,Nb,Nb] (float32).
+
+    If `zmass` (float32 [B,H,Nb,Nb]) is given it receives each block's normalised
+    softmax mass, which the renormalised drift objective needs."""
     n, nb, _ = _dims(layout)
     shape = (layout.batch, layout.heads, n, layout.head_dim)
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -176,14 +183,17 @@ def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stre
     if workspace is None:
         workspace = torch.empty(workspace_bytes(layout, DRIFT), dtype=torch.uint8, device=dev)
     L = c_layout(layout)
+    if zmass is not None:
+        _expect(zmass, "zmass", torch.float32, (layout.batch, layout.heads, nb, nb))
     _check(library().bsgm_drift_scores(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), _ptr(contrib),
-                                       _ptr(score), _ptr(workspace), workspace.numel(),
+                                       _ptr(score), _ptr(zmass), _ptr(workspace), workspace.numel(),
                                        _stream(stream)))
     return contrib, score
 
 
 def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contrib=None,
                   cdf_tau: float = 0.9, force: bool = False, swap_rounds: int = 0,
+                  objective: int = 0, zmass=None,
                   row_ptr=None, col_idx=None, row_stat=None, scores_out=None, swap_log=None,
                   workspace=None, want_stat: bool = True, stream=None):
     """Selected key blocks as CSR (row_ptr, col_idx) plus the per-row statistic."""
@@ -196,6 +206,8 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
     else:
         _expect(contrib, "contrib", torch.float32,
                 (layout.batch, layout.heads, nb, nb, layout.head_dim))
+        if zmass is not None:
+            _expect(zmass, "zmass", torch.float32, (layout.batch, layout.heads, nb, nb))
     cap = col_capacity(layout, mode, keep, force)
     if row_ptr is None:
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
@@ -206,9 +218,9 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
     if workspace is None and mode != DRIFT:
         workspace = torch.empty(workspace_bytes(layout, mode), dtype=torch.uint8, device=dev)
     L = c_layout(layout)
-    P, _keep = c_params(mode, keep, cdf_tau, force, swap_rounds)
+    P, _keep = c_params(mode, keep, cdf_tau, force, swap_rounds, objective)
     _check(library().bsgm_select_blocks(
-        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(row_ptr),
+        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
     return row_ptr, col_idx, row_stat

@@ -132,7 +132,7 @@ int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBud
 
 extern "C" {
 
-int32_t bsgm_version(void) { return 10000; }
+int32_t bsgm_version(void) { return 10100; }
 
 const char* bsgm_last_error(void) { return g_err.c_str(); }
 
@@ -167,7 +167,8 @@ int bsgm_pool_blocks(const bsgm_layout* layout, const void* x, float* mean, void
 }
 
 int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, const void* v,
-                      float* contrib, float* score, void* ws, size_t ws_bytes, void* stream) {
+                      float* contrib, float* score, float* zmass, void* ws, size_t ws_bytes,
+                      void* stream) {
   bsgm::Dims d;
   int st = check_layout(layout, &d);
   if (st != BSGM_OK) return st;
@@ -183,9 +184,10 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
   if (layout->dtype == BSGM_BF16) {
     char* base = static_cast<char*>(ws);
     e = bsgm::launch_drift_contrib_bf16(d, qbar, k, v, reinterpret_cast<float2*>(base + w.stats),
-                                        reinterpret_cast<float2*>(base + w.mz), contrib, score, s);
+                                        reinterpret_cast<float2*>(base + w.mz), contrib, score,
+                                        zmass, s);
   } else {
-    e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, s);
+    e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, zmass, s);
   }
   if (e != hipSuccess) return hip_fail(e, "drift launch");
   return ok();
@@ -223,7 +225,8 @@ int bsgm_special_rows_dense_fwd(const bsgm_layout* layout, const void* q, const 
 }
 
 int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,
-                       const void* q, const void* k, const float* contrib, int32_t* row_ptr,
+                       const void* q, const void* k, const float* contrib, const float* zmass,
+                       int32_t* row_ptr,
                        int32_t* col_idx, int64_t col_capacity, float* row_stat,
                        float* scores_out, int32_t* swap_log, void* ws, size_t ws_bytes,
                        void* stream) {
@@ -247,13 +250,18 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
   if (mode == BSGM_SEL_DRIFT) {
     if (!contrib) return fail(BSGM_E_ARG, "DRIFT needs contrib");
     if (params->swap_rounds < 0) return fail(BSGM_E_ARG, "swap_rounds must be >= 0");
+    if (params->drift_objective != BSGM_DRIFT_DROPPED_SUM &&
+        params->drift_objective != BSGM_DRIFT_RENORMALISED)
+      return fail(BSGM_E_ARG, "unknown drift objective %d", params->drift_objective);
+    if (params->drift_objective == BSGM_DRIFT_RENORMALISED && !zmass)
+      return fail(BSGM_E_ARG, "the renormalised drift objective needs zmass");
     if (d.nb > bsgm::kDriftMaxBlocks)
       return fail(BSGM_E_UNSUPPORTED, "DRIFT supports at most %d blocks per row (got %d)",
                   bsgm::kDriftMaxBlocks, d.nb);
     if (swap_log && params->swap_rounds == 0) swap_log = nullptr;
     hipError_t e = bsgm::launch_select_drift(d, hb, params->force_frame_first_block ? 1 : 0,
-                                             params->swap_rounds, contrib, row_ptr, col_idx,
-                                             row_stat, swap_log, s);
+                                             params->swap_rounds, params->drift_objective, contrib,
+                                             zmass, row_ptr, col_idx, row_stat, swap_log, s);
     if (e != hipSuccess) return hip_fail(e, "drift select launch");
     return ok();
   }

@@ -4,7 +4,8 @@
 //
 // Contributions: for pooled query i and real key token u,
 //   e_u = exp(scale <qbar_i, k_u> - M_i),  M_i = max_u scale <qbar_i, k_u>,
-//   contrib_ij = sum_{u in j} e_u v_u / Z_i,  Z_i = sum_u e_u,  score_ij = ||contrib_ij||.
+//   contrib_ij = sum_{u in j} e_u v_u / Z_i,  Z_i = sum_u e_u,  score_ij = ||contrib_ij||,
+//   zmass_ij = sum_{u in j} e_u / Z_i (optional).
 // Pass 1 finds (M_i, Z_i) with an online log-sum-exp; pass 2 walks the key
 // blocks and writes contrib and score. All arithmetic is fp32.
 #include <algorithm>
@@ -32,7 +33,8 @@ __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__
                                                        const T* __restrict__ K,
                                                        const T* __restrict__ V,
                                                        float* __restrict__ contrib,
-                                                       float* __restrict__ score, Dims d) {
+                                                       float* __restrict__ score,
+                                                       float* __restrict__ zmass, Dims d) {
   __shared__ float qs[kDriftRows][64];
   __shared__ float E[kDriftRows][128];
   __shared__ float Vs[128][65];
@@ -130,11 +132,12 @@ __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__
       for (int e = 0; e < EL; ++e) Vs[row][c * EL + e] = row < vlen ? (float)v[e] : 0.f;
     }
     __syncthreads();
-    float a0 = 0.f, a1 = 0.f;
+    float a0 = 0.f, a1 = 0.f, zs = 0.f;
     for (int u = 0; u < vlen; ++u) {
       const float e = E[ri][u];
       a0 = fmaf(e, Vs[u][dp], a0);
       a1 = fmaf(e, Vs[u][dp + 1], a1);
+      zs += e;
     }
     const int ii = i0 + ri;
     float sq = a0 * a0 + a1 * a1;
@@ -144,22 +147,34 @@ __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__
       float2* dst = reinterpret_cast<float2*>(contrib + (((size_t)bh * d.nb + ii) * d.nb + j) * 64 + dp);
       *dst = make_float2(a0, a1);
       if ((t & 31) == 0) score[((size_t)bh * d.nb + ii) * d.nb + j] = sqrtf(sq);
+      if ((t & 31) == 0 && zmass) zmass[((size_t)bh * d.nb + ii) * d.nb + j] = zs;
     }
     __syncthreads();
   }
 }
 
 hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, const void* k,
-                                const void* v, float* contrib, float* score, hipStream_t s) {
+                                const void* v, float* contrib, float* score, float* zmass,
+                                hipStream_t s) {
   if (dtype != 0) return hipErrorInvalidValue;   // bf16 takes launch_drift_contrib_bf16
   dim3 grid((d.nb + kDriftRows - 1) / kDriftRows, d.B * d.H);
   hipLaunchKernelGGL(k_drift_contrib<float>, grid, dim3(256), 0, s, qbar, (const float*)k,
-                     (const float*)v, contrib, score, d);
+                     (const float*)v, contrib, score, zmass, d);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Drift selection: one workgroup per row.
+//
+// Two objectives share the swap machinery. Dropped-sum drift: rows x_j = c_j,
+// residual r = sum_{j in D} x_j, J = ||r||. Renormalised output shift (the
+// pooled query's attention output over the kept blocks, renormalised, minus its
+// dense output o = sum_j c_j): with z_j the block's normalised mass and S the
+// kept set, J = ||sum_S c_j / sum_S z_j - o|| = ||u|| / Z_S where u = sum_S (c_j
+// - z_j o); with rows x_j = z_j o - c_j, u = sum_D x_j + (1 - sum_j z_j) o, and
+// a swap moves u exactly like r: u' = u - x_a + x_b, Z_S' = Z_S + z_a - z_b.
+// The first objective ranks swaps by delta below, the second by
+// (||u||^2 + delta) / Z_S'^2.
 //
 // With D the dropped blocks, S the kept non-forced blocks, r = sum_{j in D} c_j,
 // g_j = <r, c_j> and G_ab = <c_a, c_b>, restoring a in D and dropping b in S gives
@@ -179,7 +194,9 @@ struct DriftSelArgs {
   HeadBudget hb;
   int force;
   int rounds;
+  int renorm;            // objective: 0 dropped-sum drift, 1 renormalised output shift
   const float* contrib;
+  const float* zmass;    // renorm only: [rows, nb] normalised block masses
   int32_t* row_ptr;
   int32_t* col_idx;
   float* row_stat;
@@ -213,7 +230,7 @@ __device__ __forceinline__ float dot64(const P* x, const float* y) {
 
 // LDS carve-up of one row (byte offsets).
 struct DriftSelLds {
-  size_t cs, slot, keys, slot_of, G, total;
+  size_t cs, slot, keys, slot_of, zb, G, total;
 };
 
 __host__ __device__ inline DriftSelLds drift_sel_lds(int nb, int nslots, size_t gfloats) {
@@ -223,6 +240,7 @@ __host__ __device__ inline DriftSelLds drift_sel_lds(int nb, int nslots, size_t 
   L.slot = o;    o += (size_t)nslots * 16;       // per slot: |c|^2, weight, block, -
   L.keys = o;    o += (size_t)nb * 8;            // priority keys by block
   L.slot_of = o; o += (size_t)nb * 4;            // slot of each block (-1: forced)
+  L.zb = o;      o += (size_t)nb * 4;            // normalised block mass (renorm)
   o = (o + 15) & ~(size_t)15;
   L.G = o;       o += gfloats * 4;               // G[D slot][S slot]
   L.total = o;
@@ -230,11 +248,16 @@ __host__ __device__ inline DriftSelLds drift_sel_lds(int nb, int nslots, size_t 
 }
 
 struct SlotRec {
-  float cc;    // |c|^2
-  float wgt;   // |c|^2 - 2 g (D slot) or |c|^2 + 2 g (S slot)
+  float cc;    // |x|^2
+  float wgt;   // |x|^2 - 2 g (D slot) or |x|^2 + 2 g (S slot)
   int blk;     // key block in this slot
-  int pad;
+  float z;     // normalised block mass (renorm)
 };
+
+// Renormalised objective of a candidate: (||u||^2 + delta) / Z'^2 (never negative).
+__device__ __forceinline__ float renorm_j2(float rr, float dlt, float zs) {
+  return zs > 0.f ? fmaxf(rr + dlt, 0.f) / (zs * zs) : INFINITY;
+}
 
 template <bool CACHE, int RR>
 __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a) {
@@ -251,8 +274,12 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
   SlotRec* slot = reinterpret_cast<SlotRec*>(dsm + L.slot);
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(dsm + L.keys);
   int* slot_of = reinterpret_cast<int*>(dsm + L.slot_of);
+  float* zb = reinterpret_cast<float*>(dsm + L.zb);
   float* G = reinterpret_cast<float*>(dsm + L.G);
+  const bool renorm = a.renorm != 0;
   __shared__ __attribute__((aligned(16))) float rv[64];
+  __shared__ __attribute__((aligned(16))) float ob[64];
+  __shared__ float redz[kSelWaves];
   __shared__ float part[kSelWaves][64];
   __shared__ int bks[kSelWaves];
   __shared__ unsigned long long bkey[kSelWaves];
@@ -314,19 +341,76 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
     if (iss) sl = nd + bs0 + lanes_below(ms);
     if (t < nb) {
       slot_of[t] = sl;
-      if (sl >= 0) slot[sl] = SlotRec{cc_j, 0.f, t, 0};
+      if (sl >= 0) slot[sl] = SlotRec{cc_j, 0.f, t, 0.f};
     }
   }
   __syncthreads();
+  float ztot = 0.f;
+  if (renorm) {
+    // o = sum_j c_j (chunk c4 = t % 16 of every block this thread holds), z_j, sum_j z_j
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < RR; ++m) {
+      acc.x += row[m].x; acc.y += row[m].y; acc.z += row[m].z; acc.w += row[m].w;
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      acc.x += __shfl_xor(acc.x, o, 64); acc.y += __shfl_xor(acc.y, o, 64);
+      acc.z += __shfl_xor(acc.z, o, 64); acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    if (lane < 16) *reinterpret_cast<float4*>(&part[w][4 * lane]) = acc;
+    float zt = 0.f;
+    if (t < nb) {
+      zt = a.zmass[((size_t)bh * nb + i) * nb + t];
+      zb[t] = zt;
+    }
+    zt = wave_sum(zt);
+    if (lane == 0) redz[w] = zt;
+    __syncthreads();
+    if (t < 64) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int q = 0; q < kSelWaves; ++q) sacc += part[q][t];
+      ob[t] = sacc;
+    }
+#pragma unroll
+    for (int q = 0; q < kSelWaves; ++q) ztot += redz[q];
+    __syncthreads();
+  }
 #pragma unroll
   for (int m = 0; m < RR; ++m) {
     const int x = t + kSelThreads * m;
     if (x < nb * 16) {
       const int sl = slot_of[x >> 4];
-      if (sl >= 0) *reinterpret_cast<float4*>(cs + sl * kCs + 4 * (x & 15)) = row[m];
+      if (sl >= 0) {
+        float4 xv = row[m];
+        if (renorm) {
+          const float zj = zb[x >> 4];
+          const float4 o4 = *reinterpret_cast<const float4*>(&ob[4 * (x & 15)]);
+          xv = make_float4(zj * o4.x - xv.x, zj * o4.y - xv.y, zj * o4.z - xv.z, zj * o4.w - xv.w);
+        }
+        *reinterpret_cast<float4*>(cs + sl * kCs + 4 * (x & 15)) = xv;
+      }
     }
   }
   __syncthreads();
+  float z_s = 0.f;   // renorm: mass of the kept set
+  if (renorm) {
+    float zd = 0.f;
+    for (int sl = t; sl < nsl; sl += kSelThreads) {
+      const float zj = zb[slot[sl].blk];
+      slot[sl].cc = dot64(cs + sl * kCs, cs + sl * kCs);
+      slot[sl].z = zj;
+      if (sl < nd) zd += zj;
+    }
+    zd = wave_sum(zd);
+    if (lane == 0) redz[w] = zd;
+    __syncthreads();
+    zd = 0.f;
+#pragma unroll
+    for (int q = 0; q < kSelWaves; ++q) zd += redz[q];
+    z_s = ztot - zd;
+  }
 
   // kTa x kTb tiles of <c_a, c_b>. Tile (ta, tb) takes D slots ta + x NTA and S
   // slots tb + y NTB, so that neighbouring lanes read neighbouring LDS rows.
@@ -380,7 +464,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < kSelWaves; ++q) s += part[q][t];
-    rv[t] = s;
+    rv[t] = renorm ? fmaf(1.f - ztot, ob[t], s) : s;
   }
   __syncthreads();
 
@@ -411,7 +495,8 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
         for (int ai = t / ns; ai < nd; ai += per) {
           const SlotRec sa = slot[ai];
           const float dlt = (sa.wgt + sb.wgt) - 2.f * G[ai * ns + bi];
-          const unsigned long long key = ((unsigned long long)orderable(dlt) << 32) |
+          const float crit = renorm ? renorm_j2(rr, dlt, z_s + sa.z - sb.z) : dlt;
+          const unsigned long long key = ((unsigned long long)orderable(crit) << 32) |
                                          ((uint32_t)sa.blk << 16) | blo;
           best = key < best ? key : best;
         }
@@ -420,15 +505,16 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
       tiles([&](int ai, int bi, float v) {
         const SlotRec sa = slot[ai], sb = slot[nd + bi];
         const float dlt = (sa.wgt + sb.wgt) - 2.f * v;
-        const unsigned long long key = ((unsigned long long)orderable(dlt) << 32) |
+        const float crit = renorm ? renorm_j2(rr, dlt, z_s + sa.z - sb.z) : dlt;
+        const unsigned long long key = ((unsigned long long)orderable(crit) << 32) |
                                        ((uint32_t)sa.blk << 16) | (uint32_t)sb.blk;
         best = key < best ? key : best;
       });
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned long long ob = __shfl_xor(best, o, 64);
-      best = ob < best ? ob : best;
+      const unsigned long long other = __shfl_xor(best, o, 64);
+      best = other < best ? other : best;
     }
     if (lane == 0) bkey[w] = best;
     __syncthreads();
@@ -436,10 +522,17 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
 #pragma unroll
     for (int q = 1; q < kSelWaves; ++q) best = bkey[q] < best ? bkey[q] : best;
     const uint32_t hi = (uint32_t)(best >> 32);
-    // delta < 0 (strictly) exactly when its orderable key is below that of -0
-    const float bd = best == ~0ull ? INFINITY : (hi < 0x7FFFFFFFu ? -1.f : 1.f);
+    bool improves;
+    if (renorm) {
+      // criteria are >= 0, whose orderable keys are the float bits with the sign bit set
+      const float jb = __uint_as_float(hi & 0x7FFFFFFFu);
+      improves = best != ~0ull && hi >= 0x80000000u && jb < rr / (z_s * z_s);
+    } else {
+      // delta < 0 (strictly) exactly when its orderable key is below that of -0
+      improves = best != ~0ull && hi < 0x7FFFFFFFu;
+    }
     const uint32_t bab = (uint32_t)best;
-    const bool do_swap = nd > 0 && ns > 0 && bd < 0.f;
+    const bool do_swap = nd > 0 && ns > 0 && improves;
     const int ba = (int)(bab >> 16), bb = (int)(bab & 0xFFFFu);
     if (t == 0 && a.swap_log) {
       int32_t* lg = a.swap_log + ((size_t)r * a.rounds + round) * 2;
@@ -456,6 +549,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
     }
     // restore ba (D slot pa) and drop bb (S slot sb): exchange the slots' rows
     const int pa = slot_of[ba], sb = slot_of[bb], pb = sb - nd;
+    if (renorm) z_s += slot[pa].z - slot[sb].z;
     __syncthreads();   // every wave is done with bkey, slot weights and G of this round
     if (t < 64) {
       const float ra = cs[pa * kCs + t], rb = cs[sb * kCs + t];
@@ -476,7 +570,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
         else if (x - ns != pa) G[(x - ns) * ns + pb] = dot64(cs + (x - ns) * kCs, cs + sb * kCs);
       }
   }
-  if (t == 0 && a.row_stat) a.row_stat[r] = sqrtf(rr);
+  if (t == 0 && a.row_stat) a.row_stat[r] = renorm ? sqrtf(rr) / z_s : sqrtf(rr);
 
   const long long base = (long long)b * a.hb.per_batch + a.hb.head_off[h] + (long long)i * k;
   if (t == 0) {
@@ -497,9 +591,11 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
 }
 
 hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, int rounds,
-                               const float* contrib, int32_t* row_ptr, int32_t* col_idx,
-                               float* row_stat, int32_t* swap_log, hipStream_t s) {
-  DriftSelArgs a{d, hb, force, rounds, contrib, row_ptr, col_idx, row_stat, swap_log};
+                               int objective, const float* contrib, const float* zmass,
+                               int32_t* row_ptr, int32_t* col_idx, float* row_stat,
+                               int32_t* swap_log, hipStream_t s) {
+  DriftSelArgs a{d, hb, force, rounds, objective, contrib, zmass, row_ptr, col_idx, row_stat,
+                 swap_log};
   const int nforced = force ? d.F : 0;
   size_t gmax = 0;
   int smax = 0;

@@ -3,7 +3,8 @@
 // For pooled query i (fp32 mean of Q over the real tokens of block i) and real
 // key token u: l_iu = scale <qbar_i, k_u>; with M_i = max_u l_iu and
 // Z_i = sum_u exp(l_iu - M_i),
-//   contrib_ij = sum_{u in j} exp(l_iu - M_i) v_u / Z_i,   score_ij = ||contrib_ij||.
+//   contrib_ij = sum_{u in j} exp(l_iu - M_i) v_u / Z_i,   score_ij = ||contrib_ij||,
+//   zmass_ij = sum_{u in j} exp(l_iu - M_i) / Z_i (optional).
 //
 // Both contractions run as v_mfma_f32_32x32x16_bf16 with fp32 accuracy: the
 // fp32 operand (qbar in the logits, the weights in the value sum) is split into
@@ -30,6 +31,7 @@ struct DriftMfmaArgs {
   float2* mz;            // [B*H*nb]: (M_i * log2(e), 1 / Z_i)
   float* contrib;        // [B*H*nb, nb, 64]
   float* score;          // [B*H*nb, nb]
+  float* zmass;          // [B*H*nb, nb] or null: sum over the block of exp(l - M) / Z
 };
 
 constexpr int kDriftBlocksPerWg = 2;
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a) 
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
+    float wsum = 0.f;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const f32x16 s = qk_tile(kb, t, lane, qh, qm, ql);
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a) 
         for (int x = 0; x < 8; ++x) {
           const float wgt = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mz.x)) * mz.y;
           p[x] = tile_key(t, 8 * e + x, lane) < vlen ? wgt : 0.f;
+          wsum += p[x];
         }
         bf16x8 ph, pm, pl;
         split3(p, ph, pm, pl);
@@ -270,13 +274,19 @@ __global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a) 
     const int qi = 32 * rt + 8 * (xr >> 2) + 4 * hh + (xr & 3);
     if ((n & 1) == 0 && qi < d.nb)
       a.score[((size_t)bh * d.nb + qi) * d.nb + j] = sqrtf(v[0]);
+    if (a.zmass) {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsum), __float_as_uint(wsum),
+                                                       false, false);
+      const float zt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      if (hh == 0 && i < d.nb) a.zmass[((size_t)bh * d.nb + i) * d.nb + j] = zt;
+    }
   }
 }
 
 hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, const void* k,
                                      const void* v, float2* stats, float2* mz, float* contrib,
-                                     float* score, hipStream_t s) {
-  DriftMfmaArgs a{d, qbar, (const __bf16*)k, (const __bf16*)v, stats, mz, contrib, score};
+                                     float* score, float* zmass, hipStream_t s) {
+  DriftMfmaArgs a{d, qbar, (const __bf16*)k, (const __bf16*)v, stats, mz, contrib, score, zmass};
   const dim3 grid((d.nb + kDriftBlocksPerWg - 1) / kDriftBlocksPerWg, d.B * d.H);
   if (d.blk == 128)
     hipLaunchKernelGGL(k_drift_stats<128>, grid, dim3(256), 0, s, a);

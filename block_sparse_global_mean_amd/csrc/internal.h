@@ -40,18 +40,20 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
 
 // Drift contributions and scores from pooled Q and K, V.
 hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, const void* k,
-                                const void* v, float* contrib, float* score, hipStream_t s);
+                                const void* v, float* contrib, float* score, float* zmass,
+                                hipStream_t s);
 
 // The same on the matrix cores for bf16 K and V (fp32-accurate via split
 // operands). stats: [rows, nb] float2 scratch; mz: [rows] float2 scratch.
 hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, const void* k,
                                      const void* v, float2* stats, float2* mz, float* contrib,
-                                     float* score, hipStream_t s);
+                                     float* score, float* zmass, hipStream_t s);
 
 // Drift selection with swap restoration.
 hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, int rounds,
-                               const float* contrib, int32_t* row_ptr, int32_t* col_idx,
-                               float* row_stat, int32_t* swap_log, hipStream_t s);
+                               int objective, const float* contrib, const float* zmass,
+                               int32_t* row_ptr, int32_t* col_idx, float* row_stat,
+                               int32_t* swap_log, hipStream_t s);
 
 // Block-sparse attention forward.
 hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const void* v,

@@ -74,6 +74,12 @@ typedef struct {
   float scale;     /* softmax scale, normally 1/sqrt(head_dim) */
 } bsgm_layout;
 
+typedef enum {
+  BSGM_DRIFT_DROPPED_SUM = 0,     /* J = || sum_{dropped} contrib ||                  */
+  BSGM_DRIFT_RENORMALISED = 1     /* J = || sum_{kept} contrib / sum_{kept} zmass
+                                         - sum_{all} contrib || (output shift)        */
+} bsgm_drift_objective;
+
 typedef struct {
   int32_t mode;                   /* bsgm_sel_mode                                    */
   const int32_t* keep_per_head;   /* HOST array [heads]: kept blocks per query block
@@ -83,6 +89,7 @@ typedef struct {
                                      frame in every row; forced blocks count toward
                                      the budget                                       */
   int32_t swap_rounds;            /* DRIFT only: restoration rounds, >= 0             */
+  int32_t drift_objective;        /* DRIFT only: bsgm_drift_objective                 */
 } bsgm_select_params;
 
 /* Version of this ABI (major*10000 + minor*100 + patch). */
@@ -115,13 +122,17 @@ int bsgm_pool_blocks(const bsgm_layout* layout, const void* x, float* mean, void
  * token u: l = scale*<qbar_i, k_u>, e_u = exp(l - max_u l);
  *   contrib[b,h,i,j,:] = sum_{u in block j} e_u v_u / sum_u e_u   (float)
  *   score[b,h,i,j]     = || contrib[b,h,i,j,:] ||_2                (float)
+ *   zmass[b,h,i,j]     = sum_{u in block j} e_u / sum_u e_u         (float)
  *   q, k, v  device [B,H,N,D] of layout->dtype
  *   contrib  device float [B,H,Nb,Nb,D], required
  *   score    device float [B,H,Nb,Nb], required
+ *   zmass    device float [B,H,Nb,Nb] or NULL (needed by the renormalised
+ *            drift objective of bsgm_select_blocks)
  *   ws       device, >= bsgm_workspace_bytes(layout, BSGM_SEL_DRIFT) bytes
  */
 int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, const void* v,
-                      float* contrib, float* score, void* ws, size_t ws_bytes, void* stream);
+                      float* contrib, float* score, float* zmass, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* Block selection ([VASC] A.2: exact binary capacity per query; [ReSS]
  * Fig. 3(b): per-head budget; [ReSS] Table 2: the cumulative-threshold rule;
@@ -135,23 +146,28 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
  *          at least one and at least the forced blocks.
  *   DRIFT: score = ||contrib_ij||; start from the first keep_per_head[h]; then
  *          up to swap_rounds rounds, each making the single swap (restore a
- *          dropped block a, drop a kept non-forced block b) that minimises
- *          J^2 = ||sum_{dropped} contrib - contrib_a + contrib_b||^2 (ties: lower
- *          a, then lower b) if it lowers J, stopping otherwise.
+ *          dropped block a, drop a kept non-forced block b) that minimises the
+ *          drift J of the resulting set (ties: lower a, then lower b) if it
+ *          lowers J, stopping otherwise. J is chosen by drift_objective:
+ *          DROPPED_SUM  J = ||sum_{dropped} contrib||;
+ *          RENORMALISED J = ||sum_{kept} contrib / sum_{kept} zmass - sum_{all} contrib||,
+ *          the shift of the pooled query's attention output once the dropped
+ *          blocks are removed and the kept weights renormalised ([ReSS] Fig. 3(a)).
  *   q, k       device [B,H,N,D] (TOPK, CDF; may be NULL for DRIFT)
  *   contrib    device float [B,H,Nb,Nb,D] from bsgm_drift_scores (DRIFT only)
+ *   zmass      device float [B,H,Nb,Nb] from bsgm_drift_scores (RENORMALISED only)
  *   row_ptr    device int32 [B*H*Nb + 1], written
  *   col_idx    device int32 [col_capacity], first row_ptr[last] entries written
  *   col_capacity >= bsgm_col_capacity(layout, params)
  *   row_stat   device float [B*H*Nb] or NULL: kept pooled mass sum_{kept} P
- *              (TOPK, CDF) or the final drift J = ||sum_{dropped} contrib|| (DRIFT)
+ *              (TOPK, CDF) or the final drift J under the objective (DRIFT)
  *   scores_out device float [B,H,Nb,Nb] or NULL: the pooled logits (TOPK, CDF)
  *   swap_log   device int32 [B*H*Nb, swap_rounds, 2] or NULL: the (a, b) of each
  *              round, (-1, -1) once restoration has stopped (DRIFT)
  *   ws         device, >= bsgm_workspace_bytes(layout, mode) bytes
  */
 int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,
-                       const void* q, const void* k, const float* contrib,
+                       const void* q, const void* k, const float* contrib, const float* zmass,
                        int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                        float* row_stat, float* scores_out, int32_t* swap_log,
                        void* ws, size_t ws_bytes, void* stream);

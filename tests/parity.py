@@ -9,7 +9,8 @@ up to a score gap of 1e-4, measured on the oracle's float64 values:
   * drift: the initial set is a top-k set by drift score up to a relative gap
     of 1e-4, and every logged swap is optimal, and every stop justified, up to
     a relative 1e-4 in J (2e-4 in J^2) when replayed on the oracle's
-    contributions.
+    contributions, under the objective the selection used (for the renormalised
+    one with an absolute allowance for float32 rounding, see drift_valid).
 Outputs: fp32 max |O - O_ref| <= 1e-3; bf16 max_d |O - O_ref| <= 2e-2 * RMS_d(O_ref)
 for every real query row (see output_check).
 """
@@ -71,14 +72,20 @@ def cdf_valid(kept: Sequence[int], score_row: np.ndarray, p_row: np.ndarray, tau
 
 
 def drift_valid(kept_final: Sequence[int], swaps: np.ndarray, chat: np.ndarray, k: int,
-                forced: Sequence[int], gap: float = GAP) -> tuple:
+                forced: Sequence[int], gap: float = GAP, zhat=None, floor: float = 0.0) -> tuple:
     """Replays the GPU's swap log on the oracle's contributions.
 
+    zhat None: the dropped-sum objective J(S) = ||sum_{j not in S} chat_j||.
+    zhat given: the renormalised objective J(S) = ||sum_S chat_j / sum_S zhat_j -
+    sum_j chat_j||. Comparisons of J^2 allow a relative 2*gap plus `floor` (an
+    absolute allowance in J^2 for the float32 rounding of the kernel's update
+    rule, which works with differences of squared norms).
     Returns (ok, reason, replayed final J).
     """
     nb = chat.shape[0]
     fset = set(forced)
     d = np.sqrt((chat * chat).sum(axis=1))
+    obar = chat.sum(axis=0)
     # the initial set: final set with the logged swaps undone, newest first
     init = set(kept_final)
     for a, b in reversed([tuple(s) for s in swaps if s[0] >= 0]):
@@ -92,35 +99,56 @@ def drift_valid(kept_final: Sequence[int], swaps: np.ndarray, chat: np.ndarray, 
         return False, "initial set has the wrong size or misses a forced block", None
     if nf_kept and dropped and max(dropped) > min(nf_kept) * (1 + gap):
         return False, "initial set is not the top-k by drift score", None
+
+    def j2_of(cur):
+        """J^2 of the kept set cur."""
+        if zhat is None:
+            r = chat[sorted(set(range(nb)) - cur)].sum(axis=0)
+            return float(r @ r)
+        return oracle.drift_j_renorm(chat, zhat, sorted(cur)) ** 2
+
+    def j2_swaps(cur, drop, cand_b):
+        """J^2 after each swap, [len(drop), len(cand_b)]."""
+        if zhat is None:
+            r = chat[drop].sum(axis=0)
+            trial = r[None, None, :] - chat[drop][:, None, :] + chat[cand_b][None, :, :]
+            return (trial * trial).sum(axis=-1)
+        S = sorted(cur)
+        cs, zs = chat[S].sum(axis=0), float(zhat[S].sum())
+        c2 = cs[None, None, :] + chat[drop][:, None, :] - chat[cand_b][None, :, :]
+        z2 = zs + zhat[drop][:, None] - zhat[cand_b][None, :]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            u = c2 / z2[:, :, None] - obar[None, None, :]
+            return np.where(z2 > 0, (u * u).sum(axis=-1), np.inf)
+
     cur = set(init)
     for s in swaps:
         a, b = int(s[0]), int(s[1])
         drop = sorted(set(range(nb)) - cur)
         cand_b = sorted(cur - fset)
-        r = chat[drop].sum(axis=0)
-        rr = float(r @ r)
-        if drop and cand_b:
-            trial = r[None, None, :] - chat[drop][:, None, :] + chat[cand_b][None, :, :]
-            best = float((trial * trial).sum(axis=-1).min())
-        else:
-            best = np.inf
+        rr = j2_of(cur)
+        trial = j2_swaps(cur, drop, cand_b) if drop and cand_b else None
+        best = float(trial.min()) if trial is not None else np.inf
         if a < 0:
-            if best < rr * (1 - 2 * gap):
+            if best < rr * (1 - 2 * gap) - floor:
                 return False, "stopped although a swap lowers J", None
             break
+        if trial is None:
+            return False, "swap logged with nothing to swap", None
         if a in cur or b not in cur or b in fset:
             return False, "swap does not move a dropped block in and a kept block out", None
-        u = r - chat[a] + chat[b]
-        j2 = float(u @ u)
-        if j2 > best * (1 + 2 * gap) + 1e-30:
+        j2 = float(trial[drop.index(a), cand_b.index(b)])
+        if j2 > best * (1 + 2 * gap) + floor + 1e-30:
             return False, f"swap not optimal: {j2} vs best {best}", None
-        if j2 > rr * (1 + 2 * gap):
+        if j2 > rr * (1 + 2 * gap) + floor:
             return False, "swap raises J", None
         cur.remove(b)
         cur.add(a)
     if cur != set(kept_final):
         return False, "replay does not reach the final set", None
-    return True, "", oracle.drift_j(chat, sorted(cur))
+    if zhat is None:
+        return True, "", oracle.drift_j(chat, sorted(cur))
+    return True, "", oracle.drift_j_renorm(chat, zhat, sorted(cur))
 
 
 def output_error(o_gpu: np.ndarray, o_ref: np.ndarray, valid: np.ndarray):

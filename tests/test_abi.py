@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = bsgm.library()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert bsgm.version() == 10000
+    assert bsgm.version() == 10100
 
 
 class L:
@@ -70,16 +70,16 @@ def test_bad_layouts_rejected(kw, code):
 
 
 def _select(lay, mode=0, keep=(2, 2), force=False, rounds=0, tau=0.9, cap=None, wsb=None,
-            q=16, k=16, contrib=None, rp=16, ci=16):
+            q=16, k=16, contrib=None, rp=16, ci=16, objective=0, zmass=None):
     lib = bsgm.library()
     c = _lib.c_layout(lay)
-    P, arr = _lib.c_params(mode, keep, tau, force, rounds)
+    P, arr = _lib.c_params(mode, keep, tau, force, rounds, objective)
     need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
     cap = need if cap is None else cap
     wsb = ws(lay, mode) if wsb is None else wsb
     v = lambda x: None if x is None else ctypes.c_void_p(x)
-    rc = lib.bsgm_select_blocks(ctypes.byref(c), ctypes.byref(P), v(q), v(k), v(contrib), v(rp),
-                                v(ci), cap, None, None, None, ctypes.c_void_p(16), wsb, None)
+    rc = lib.bsgm_select_blocks(ctypes.byref(c), ctypes.byref(P), v(q), v(k), v(contrib),
+                                v(zmass), v(rp), v(ci), cap, None, None, None, ctypes.c_void_p(16), wsb, None)
     return rc, lib.bsgm_last_error().decode(), need
 
 
@@ -97,6 +97,8 @@ def test_select_argument_errors():
     assert _select(lay, mode=9)[0] == -1
     assert _select(lay, mode=2, contrib=None)[0] == -1
     assert _select(lay, mode=2, contrib=16, rounds=-1)[0] == -1
+    assert _select(lay, mode=2, contrib=16, objective=2, zmass=16)[0] == -1
+    assert _select(lay, mode=2, contrib=16, objective=1)[0] == -1       # renormalised needs zmass
     assert _select(lay, q=None)[0] == -1
     assert _select(lay, rp=None)[0] == -1
     big = L(frames=2, frame_len=128 * 300, frame_valid=128 * 300)
@@ -115,8 +117,9 @@ def test_pool_and_drift_null_arguments():
     c = _lib.c_layout(L())
     assert lib.bsgm_pool_blocks(ctypes.byref(c), None, ctypes.c_void_p(16), None) == -1
     one = ctypes.c_void_p(16)
-    assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, None, one, one, 1 << 20, None) == -1
-    assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, one, 10, None) == -4
+    assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, None, one, None, one, 1 << 20,
+                                 None) == -1
+    assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, None, one, 10, None) == -4
     assert lib.bsgm_pool_blocks(None, one, one, None) == -1
 
 

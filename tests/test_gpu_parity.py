@@ -471,8 +471,32 @@ def test_topk_layer8_full_size(dev):
 # --------------------------------------------------------------------------
 # drift
 # --------------------------------------------------------------------------
+def renorm_floor(chat, zhat, cg, zg, kept):
+    """Absolute allowance in J^2 for the renormalised objective on the GPU.
+
+    The kernel works on its own float32 contributions cg and masses zg with rows
+    x_j = z_j o - c_j (o = sum_j c_j) and scores a swap as (||u||^2 + delta) / Z^2,
+    u = sum_{dropped} x_j + (1 - sum_j z_j) o. Its J may therefore be off by the
+    input perturbation dJ_in = (sum_j ||dx_j||) / Z, with dx_j the change of x_j
+    from (chat, zhat) to (cg, zg), plus the float32 rounding of the update rule,
+    about 16 eps32 (||u|| + max_j ||x_j||)^2 / Z^2 in J^2. For Z it takes half the
+    final kept mass, a lower bound for the sets a few swaps away in these tests.
+    Returns (allowance in J^2, dJ_in)."""
+    o_ref, o_g = chat.sum(axis=0), cg.astype(np.float64).sum(axis=0)
+    x_ref = zhat[:, None] * o_ref[None, :] - chat
+    x_g = zg.astype(np.float64)[:, None] * o_g[None, :] - cg.astype(np.float64)
+    zmin = 0.5 * float(zhat[sorted(kept)].sum())
+    dj = float(np.sqrt(((x_g - x_ref) ** 2).sum(axis=1)).sum()) / zmin
+    xmax = float(np.sqrt((x_ref * x_ref).sum(axis=1)).max())
+    drop = sorted(set(range(chat.shape[0])) - set(kept))
+    unorm = float(np.sqrt((x_ref[drop].sum(axis=0) ** 2).sum()))
+    jmax = (unorm + 2 * xmax) / zmin
+    eps = float(np.finfo(np.float32).eps)
+    return 2 * jmax * dj + dj * dj + 16 * eps * (unorm + 2 * xmax) ** 2 / zmin ** 2, dj
+
+
 def check_drift(lay, vals, keep, rounds, force, contrib_g, score_g, rpn, cin, stat_g, log_g,
-                rows_to_check):
+                rows_to_check, objective=oracle.RAW, zmass_g=None):
     q, k, v = vals
     nb = lay.nblocks
     forced = oracle.forced_blocks(lay, force)
@@ -481,13 +505,30 @@ def check_drift(lay, vals, keep, rounds, force, contrib_g, score_g, rpn, cin, st
     for (h, i) in rows_to_check:
         qbar = oracle.pool(q[:, h:h + 1], lay)[0, 0]
         chat, z, Z = oracle.drift_row(qbar[i], k[0, h], v[0, h], lay)
+        zhat = z / Z
         cg = contrib_g[0, h, i]
         scale = np.sqrt((chat * chat).sum(axis=1)).max()
         assert np.abs(cg - chat).max() <= 1e-4 * scale, (h, i)
         dref = np.sqrt((chat * chat).sum(axis=1))
         assert np.abs(score_g[0, h, i] - dref).max() <= 1e-4 * dref.max()
+        if zmass_g is not None:
+            # normalised masses lie in [0, 1] and sum to one; a float32 logit
+            # error of ~1e-6 moves each by that relative amount
+            assert np.abs(zmass_g[0, h, i] - zhat).max() <= 1e-5, (h, i)
         r = h * nb + i
         swaps = log_g[r] if rounds > 0 else np.zeros((0, 2), np.int64)
+        if objective == oracle.RENORM:
+            floor, dj = renorm_floor(chat, zhat, cg, zmass_g[0, h, i], rows[r])
+            ok, why, jrep = parity.drift_valid(rows[r], swaps, chat, int(keep[h]), forced,
+                                               zhat=zhat, floor=floor)
+            assert ok, f"row {(h, i)}: {why}"
+            assert abs(stat_g[r] - jrep) <= 1e-4 * jrep + dj + 1e-30, (h, i, stat_g[r], jrep, dj)
+            kept_ref, j_ref, _ = oracle.restore_row_renorm(chat, zhat, int(keep[h]), rounds,
+                                                           forced)
+            if kept_ref != rows[r]:
+                differ += 1
+                assert jrep <= j_ref * (1 + 1e-3) + dj
+            continue
         ok, why, jrep = parity.drift_valid(rows[r], swaps, chat, int(keep[h]), forced)
         assert ok, f"row {(h, i)}: {why}"
         assert abs(stat_g[r] - jrep) <= 1e-4 * max(jrep, 1e-30), (h, i, stat_g[r], jrep)
@@ -573,6 +614,86 @@ def test_drift_512_blocks_uncached_search(dev):
     differ = check_drift(lay, vals, keep, rounds, False, contrib.cpu().numpy(),
                          score.cpu().numpy(), rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows)
     say(f"drift 512: sampled rows whose final set differs from the oracle's own run: {differ}")
+
+
+# renormalised objective: the output shift once dropped blocks are removed
+@pytest.mark.parametrize("dtype,block,force", [("bf16", 64, False), ("bf16", 128, True),
+                                               ("f32", 64, True), ("f32", 128, False)])
+def test_drift_renorm_small_layouts(dev, dtype, block, force):
+    frames, per = (10, 4) if block == 64 else (11, 3)
+    lay = custom_layout(frames, per * block, per * block - 37, block, heads=2, dtype=dtype)
+    host, vals = random_inputs(lay, 71 + block)
+    nb = lay.nblocks
+    nf = frames if force else 0
+    keep = np.array([max(10, nf + 3), max(7, nf + 1)], dtype=np.int32)
+    rounds = 4
+    say(f"drift renorm small {dtype} block {block} force {force}: nb {nb}")
+    q, k, v = (to_dev(x, dev) for x in host)
+    zmass = torch.full((1, lay.heads, nb, nb), -1.0, dtype=torch.float32, device=dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v, zmass=zmass)
+    log = torch.full((lay.heads * nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    force=force, swap_log=log, objective=bsgm.RENORMALISED,
+                                    zmass=zmass)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    logn = log.cpu().numpy()
+    assert np.all(logn >= -1)
+    rows = [(h, i) for h in range(lay.heads) for i in range(nb)]
+    differ = check_drift(lay, vals, keep, rounds, force, contrib.cpu().numpy(),
+                         score.cpu().numpy(), rpn, cin, st.cpu().numpy(), logn, rows,
+                         objective=oracle.RENORM, zmass_g=zmass.cpu().numpy())
+    nswaps = int((logn[..., 0] >= 0).sum())
+    say(f"drift renorm small: {nswaps} swaps; rows differing from the oracle's run: {differ}")
+
+
+@pytest.mark.parametrize("rounds,force,heads", [(3, False, 2), (6, True, 1)])
+def test_drift_renorm_layer16(dev, rounds, force, heads):
+    say(f"drift renorm 16 frames, {heads} heads, rounds {rounds}, force {force}")
+    w, data = preset(4, heads=heads)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    nb = lay.nblocks
+    zmass = torch.empty((1, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v, zmass=zmass)
+    log = torch.full((lay.heads * nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, data["keep"], contrib=contrib,
+                                    swap_rounds=rounds, force=force, swap_log=log,
+                                    objective=bsgm.RENORMALISED, zmass=zmass)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    logn = log.cpu().numpy()
+    assert np.all(logn >= -1)
+    sample = [(h, i) for h in range(heads) for i in range(0, nb, 7)]
+    differ = check_drift(lay, (data["q"], data["k"], data["v"]), data["keep"], rounds, force,
+                         contrib.cpu().numpy(), score.cpu().numpy(), rpn, cin, st.cpu().numpy(),
+                         logn, sample, objective=oracle.RENORM, zmass_g=zmass.cpu().numpy())
+    nswaps = int((logn[..., 0] >= 0).sum())
+    say(f"drift renorm 16: {nswaps} swaps over all rows; sampled rows differing: {differ}")
+
+
+def test_drift_renorm_512_blocks_uncached_search(dev):
+    lay = custom_layout(32, 1024, 1000, 64, heads=1, dtype="bf16")
+    host, vals = random_inputs(lay, 67)
+    nb = lay.nblocks
+    keep = np.array([256], dtype=np.int32)
+    rounds = 2
+    say("drift renorm 512 blocks, keep 256, 2 rounds")
+    q, k, v = (to_dev(x, dev) for x in host)
+    zmass = torch.empty((1, 1, nb, nb), dtype=torch.float32, device=dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v, zmass=zmass)
+    log = torch.full((nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    swap_log=log, objective=bsgm.RENORMALISED, zmass=zmass)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    rows = [(0, i) for i in (0, 3, 256, 511)]
+    check_drift(lay, vals, keep, rounds, False, contrib.cpu().numpy(), score.cpu().numpy(), rpn,
+                cin, st.cpu().numpy(), log.cpu().numpy(), rows, objective=oracle.RENORM,
+                zmass_g=zmass.cpu().numpy())
 
 
 def test_drift_layer16_full_size_sampled(dev):
