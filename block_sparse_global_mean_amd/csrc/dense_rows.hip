@@ -51,6 +51,9 @@ __global__ __launch_bounds__(256, 2) void k_dense_rows_partial(DenseRowsArgs a) 
   const __bf16* V = a.v + hoff;
   const int gr = g * 128 + 32 * w + n;
   const bool row_ok = gr < a.nrows;
+  // a wave whose 32 rows are all past the last special row only helps with the
+  // tile copies (the last group of a head is usually partly empty)
+  const bool wave_live = g * 128 + 32 * w < a.nrows;
   const int tok = (gr / a.ns) * d.L + gr % a.ns;
 
   bf16x8 qf[4];
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(256, 2) void k_dense_rows_partial(DenseRowsArgs a) 
     wait_dma();
     __syncthreads();
     if (j + 1 < j1) BSGM_DMA_D(buf ^ 1, j + 1);
+    if (!wave_live) continue;
     const unsigned char* kb = smem + buf * 2 * TB;
     const unsigned char* vb = kb + TB;
 
@@ -186,6 +190,7 @@ __global__ __launch_bounds__(256, 2) void k_dense_rows_partial(DenseRowsArgs a) 
 
   // partial of this chunk: lane holds gathered row 32w + n, head dims
   // 32mt + 8(x/4) + 4hh + x%4
+  if (!wave_live) return;
   const size_t prow = (size_t)wg * 128 + 32 * w + n;
   float* po = a.po + prow * 64;
 #pragma unroll
@@ -198,6 +203,8 @@ __global__ __launch_bounds__(256, 2) void k_dense_rows_partial(DenseRowsArgs a) 
 }
 
 // One wave per gathered row: merge the chunk partials, write O (bf16) and LSE.
+// Lane c takes the (m, l) of chunks c, c + 64, ...; each chunk's weight is then
+// broadcast while the lanes (head dims) read the partial O rows eight at a time.
 __global__ __launch_bounds__(256) void k_dense_rows_merge(DenseRowsArgs a) {
   const Dims& d = a.d;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -207,16 +214,29 @@ __global__ __launch_bounds__(256) void k_dense_rows_merge(DenseRowsArgs a) {
   const int g = rr >> 7, r = rr & 127;
   const float c2 = d.scale * 1.4426950408889634f;
   const size_t base = ((size_t)(bh * a.ngroups + g) * a.nchunks) * 128 + r;
+  const int nc = a.nchunks;
   float m = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) m = fmaxf(m, a.pml[(base + (size_t)c * 128) * 2]);
+  for (int c = lane; c < nc; c += 64) m = fmaxf(m, a.pml[(base + (size_t)c * 128) * 2]);
+  m = wave_max(m);
   float l = 0.f, acc = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const size_t pr = base + (size_t)c * 128;
-    const float2 ml = *reinterpret_cast<const float2*>(a.pml + pr * 2);
-    const float f = ml.y > 0.f ? __builtin_amdgcn_exp2f((ml.x - m) * c2) : 0.f;
-    l += ml.y * f;
-    acc += a.po[pr * 64 + lane] * f;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    float f = 0.f;
+    if (c0 + lane < nc) {
+      const float2 ml = *reinterpret_cast<const float2*>(a.pml + (base + (size_t)(c0 + lane) * 128) * 2);
+      f = ml.y > 0.f ? __builtin_amdgcn_exp2f((ml.x - m) * c2) : 0.f;
+      l += ml.y * f;
+    }
+    const int cn = min(64, nc - c0);
+    for (int j0 = 0; j0 < cn; j0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        pv[u] = j0 + u < cn ? a.po[(base + (size_t)(c0 + j0 + u) * 128) * 64 + lane] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(pv[u], __shfl(f, j0 + u, 64), acc);
+    }
   }
+  l = wave_sum(l);
   const int tok = (rr / a.ns) * d.L + rr % a.ns;
   const size_t orow = (size_t)bh * d.N + tok;
   a.o[orow * 64 + lane] = (__bf16)(l > 0.f ? acc / l : 0.f);

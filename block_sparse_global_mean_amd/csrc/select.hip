@@ -1,12 +1,16 @@
 // Pooled block selection (top-k by pooled score, or cumulative pooled mass
 // under a per-head cap) and CSR emission.
 //
-// One workgroup of 256 threads per (b, h, query block). Keys are made unique
-// and totally ordered as 64-bit integers: high word = order-preserving bits of
-// the pooled score (forced blocks get all ones), low word = ~j so that equal
-// scores rank the lower block index first. The k-th largest key, and the
-// smallest prefix reaching the mass threshold, are found exactly by an MSB-first
-// bitwise search with block-wide counts, so no sort is needed.
+// One wave per (b, h, query block); a workgroup of four waves takes four
+// consecutive query blocks of one (b, h), so each 64-key tile of pooled K is
+// read from memory once per four rows and served to the waves from LDS. Lane l
+// owns key blocks l, l + 64, ...; every reduction of a row is wave-local.
+// Keys are made unique and totally ordered as 64-bit integers: high word =
+// order-preserving bits of the pooled score (forced blocks get all ones), low
+// word = ~j so that equal scores rank the lower block index first. The k-th
+// largest key, and the smallest prefix reaching the mass threshold, are found
+// exactly by an MSB-first bitwise search, so no sort is needed: counts come from
+// ballots and masses from cross-lane sums that stay on the VALU.
 #include "device_util.h"
 
 namespace bsgm {
@@ -27,89 +31,97 @@ struct SelArgs {
   uint32_t* bitmask;   // CDF: kept flags, ceil(nb/32) words per row
 };
 
-// Writes the kept flags of one row to col_idx[base...] in ascending block order.
-template <int PER>
-__device__ __forceinline__ void emit_ascending(const bool (&kept)[PER], int nb, long long base,
-                                               int32_t* col_idx, int* wtot) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  long long running = base;
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const unsigned long long m = __ballot(kept[p]);
-    __syncthreads();
-    if (lane == 0) wtot[w] = __popcll(m);
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      before += (q < w) ? wtot[q] : 0;
-      total += wtot[q];
-    }
-    if (kept[p]) col_idx[running + before + lanes_below(m)] = t + 256 * p;
-    running += total;
-  }
-}
+constexpr int kSelRowsPerWg = 4;
+constexpr int kKtStride = 68;   // LDS row stride (floats) of the pooled-K tile
 
-template <int PER>
+template <int PW>   // key blocks per lane: nb <= 64 * PW
 __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
-  __shared__ float qs[64];
-  __shared__ float redf[4];
-  __shared__ int redi[4];
-  __shared__ int wtot[4];
+  __shared__ __attribute__((aligned(16))) float kt[2][64 * kKtStride];
   const Dims& d = a.d;
-  const int r = blockIdx.x;
-  const int bh = r / d.nb, i = r - bh * d.nb;
+  const int wgs_per_bh = (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
+  const int bh = blockIdx.x / wgs_per_bh;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int i = (blockIdx.x - bh * wgs_per_bh) * kSelRowsPerWg + w;
+  const bool live = i < d.nb;
   const int h = bh % d.H, b = bh / d.H;
-  const int t = threadIdx.x;
-  if (t < 64) qs[t] = a.qbar[((size_t)bh * d.nb + i) * 64 + t];
-  __syncthreads();
+  const int r = bh * d.nb + i;
 
-  const float* kb = a.kbar + (size_t)bh * d.nb * 64;
-  float S[PER], P[PER];
-  unsigned long long key[PER];
-  bool valid[PER];
-  float mx = -INFINITY;
+  // the pooled query row, in registers (one broadcast load per float4)
+  float4 q4[16];
+  {
+    const float4* qr = reinterpret_cast<const float4*>(a.qbar + ((size_t)bh * d.nb + (live ? i : 0)) * 64);
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int j = t + 256 * p;
-    valid[p] = j < d.nb;
+    for (int c = 0; c < 16; ++c) q4[c] = qr[c];
+  }
+
+  // pooled scores S_j = scale <qbar_i, kbar_j>, 64 keys per tile; tiles are
+  // double-buffered in LDS and the next one is fetched while this one is used
+  const float* kb = a.kbar + (size_t)bh * d.nb * 64;
+  auto fetch = [&](int p, float4 (&v)[4]) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int x = t + 256 * s4;          // float4 index in the tile
+      const int j = 64 * p + (x >> 4);
+      v[s4] = j < d.nb ? reinterpret_cast<const float4*>(kb + (size_t)j * 64)[x & 15]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 nxt[4];
+  fetch(0, nxt);
+  float S[PW];
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
     S[p] = -INFINITY;
-    if (valid[p]) {
-      const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * 64);
+    if (64 * p >= d.nb) continue;   // uniform across the workgroup
+    float* tile = kt[p & 1];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int x = t + 256 * s4;
+      *reinterpret_cast<float4*>(&tile[(x >> 4) * kKtStride + 4 * (x & 15)]) = nxt[s4];
+    }
+    if (64 * (p + 1) < d.nb) fetch(p + 1, nxt);
+    __syncthreads();   // tile p written; every wave is past tile p - 1 (the other buffer)
+    if (live && 64 * p + lane < d.nb) {
+      const float4* kr = reinterpret_cast<const float4*>(&tile[lane * kKtStride]);
       float acc = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float4 kv = kr[q];
-        acc = fmaf(qs[4 * q + 0], kv.x, acc);
-        acc = fmaf(qs[4 * q + 1], kv.y, acc);
-        acc = fmaf(qs[4 * q + 2], kv.z, acc);
-        acc = fmaf(qs[4 * q + 3], kv.w, acc);
+      for (int c = 0; c < 16; ++c) {
+        const float4 kv = kr[c];
+        acc = fmaf(q4[c].x, kv.x, acc);
+        acc = fmaf(q4[c].y, kv.y, acc);
+        acc = fmaf(q4[c].z, kv.z, acc);
+        acc = fmaf(q4[c].w, kv.w, acc);
       }
       S[p] = d.scale * acc;
-      mx = fmaxf(mx, S[p]);
     }
   }
-  mx = block_max<256>(mx, redf);
+  if (!live) return;   // no barrier follows
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < PW; ++p) mx = fmaxf(mx, S[p]);
+  mx = wave_allmax(mx);
+  float P[PW];
+  unsigned long long key[PW];
   float esum = 0.f;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    P[p] = valid[p] ? expf(S[p] - mx) : 0.f;
+  for (int p = 0; p < PW; ++p) {
+    const int j = 64 * p + lane;
+    const bool valid = j < d.nb;
+    P[p] = valid ? expf(S[p] - mx) : 0.f;
     esum += P[p];
-  }
-  const float inv = 1.f / block_sum<256>(esum, redf);
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    P[p] *= inv;
-    const int j = t + 256 * p;
-    if (valid[p]) {
+    if (valid) {
       const bool f = a.force && block_forced(d, j);
       const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(S[p]);
       key[p] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
-      if (a.scores_out) a.scores_out[((size_t)bh * d.nb + i) * d.nb + j] = S[p];
+      if (a.scores_out) a.scores_out[(size_t)r * d.nb + j] = S[p];
     } else {
-      key[p] = 0ull;
+      key[p] = 0ull;   // sorts below every real key, whose high word is nonzero
     }
   }
+  const float inv = 1.f / wave_allsum(esum);
+#pragma unroll
+  for (int p = 0; p < PW; ++p) P[p] *= inv;
 
   const int nforced = a.force ? d.F : 0;
   int k;
@@ -120,13 +132,12 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
       const unsigned long long cand = T | (1ull << bit);
       float m = 0.f;
 #pragma unroll
-      for (int p = 0; p < PER; ++p) m += (valid[p] && key[p] >= cand) ? P[p] : 0.f;
-      if (block_sum<256>(m, redf) >= a.tau) T = cand;
+      for (int p = 0; p < PW; ++p) m += key[p] >= cand ? P[p] : 0.f;
+      if (wave_allsum(m) >= a.tau) T = cand;
     }
-    int c = 0;
+    int n = 0;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) c += (valid[p] && key[p] >= T) ? 1 : 0;
-    const int n = block_sum_i<256>(c, redi);
+    for (int p = 0; p < PW; ++p) n += __popcll(__ballot(key[p] != 0ull && key[p] >= T));
     const int cap = a.hb.keep[h];
     k = n < cap ? n : cap;
     k = k > nforced ? k : nforced;
@@ -140,39 +151,44 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
     const unsigned long long cand = T | (1ull << bit);
     int c = 0;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) c += (valid[p] && key[p] >= cand) ? 1 : 0;
-    if (block_sum_i<256>(c, redi) >= k) T = cand;
+    for (int p = 0; p < PW; ++p) c += __popcll(__ballot(key[p] >= cand));
+    if (c >= k) T = cand;
   }
-  bool kept[PER];
+  bool kept[PW];
   float km = 0.f;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    kept[p] = valid[p] && key[p] >= T;
+  for (int p = 0; p < PW; ++p) {
+    kept[p] = key[p] != 0ull && key[p] >= T;
     km += kept[p] ? P[p] : 0.f;
   }
-  km = block_sum<256>(km, redf);
-  if (t == 0 && a.row_stat) a.row_stat[r] = km;
+  km = wave_allsum(km);
+  if (lane == 0 && a.row_stat) a.row_stat[r] = km;
 
   if (a.mode == 1) {
     const int words = (d.nb + 31) >> 5;
-    const int lane = t & 63, w = t >> 6;
-    if (t == 0) a.counts[r] = k;
+    if (lane == 0) a.counts[r] = k;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
+    for (int p = 0; p < PW; ++p) {
       const unsigned long long m = __ballot(kept[p]);
-      const int w0 = 8 * p + 2 * w;
       if (lane == 0) {
-        if (w0 < words) a.bitmask[(size_t)r * words + w0] = (uint32_t)m;
-        if (w0 + 1 < words) a.bitmask[(size_t)r * words + w0 + 1] = (uint32_t)(m >> 32);
+        if (2 * p < words) a.bitmask[(size_t)r * words + 2 * p] = (uint32_t)m;
+        if (2 * p + 1 < words) a.bitmask[(size_t)r * words + 2 * p + 1] = (uint32_t)(m >> 32);
       }
     }
   } else {
     const long long base = (long long)b * a.hb.per_batch + a.hb.head_off[h] + (long long)i * k;
-    if (t == 0) {
+    if (lane == 0) {
       a.row_ptr[r] = (int32_t)base;
       if (r == d.rows - 1) a.row_ptr[d.rows] = (int32_t)(base + k);
     }
-    emit_ascending<PER>(kept, d.nb, base, a.col_idx, wtot);
+    // kept blocks in ascending order: tile p, then lane
+    long long running = base;
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const unsigned long long m = __ballot(kept[p]);
+      if (kept[p]) a.col_idx[running + lanes_below(m)] = 64 * p + lane;
+      running += __popcll(m);
+    }
   }
 }
 
@@ -250,13 +266,18 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
                                 hipStream_t s) {
   SelArgs a{d, hb, mode, tau, force, qbar, kbar, row_ptr, col_idx, row_stat, scores_out,
             counts, bitmask};
-  const int per = (d.nb + 255) / 256;
-  dim3 grid(d.rows), block(256);
+  const int per = (d.nb + 63) / 64;
+  dim3 grid(d.B * d.H * ((d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg)), block(256);
   if (per <= 1) hipLaunchKernelGGL(k_select_pooled<1>, grid, block, 0, s, a);
   else if (per <= 2) hipLaunchKernelGGL(k_select_pooled<2>, grid, block, 0, s, a);
   else if (per <= 4) hipLaunchKernelGGL(k_select_pooled<4>, grid, block, 0, s, a);
   else if (per <= 8) hipLaunchKernelGGL(k_select_pooled<8>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_select_pooled<16>, grid, block, 0, s, a);
+  else if (per <= 12) hipLaunchKernelGGL(k_select_pooled<12>, grid, block, 0, s, a);
+  else if (per <= 16) hipLaunchKernelGGL(k_select_pooled<16>, grid, block, 0, s, a);
+  else if (per <= 24) hipLaunchKernelGGL(k_select_pooled<24>, grid, block, 0, s, a);
+  else if (per <= 32) hipLaunchKernelGGL(k_select_pooled<32>, grid, block, 0, s, a);
+  else if (per <= 48) hipLaunchKernelGGL(k_select_pooled<48>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_select_pooled<64>, grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode != 1) return e;
   hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, s, counts, row_ptr, d.rows);

@@ -179,6 +179,39 @@ def test_topk_selection_matches_oracle(dev, case):
     say(f"topk {case}: rows differing from the oracle by near-ties: {mism}")
 
 
+@pytest.mark.parametrize("nb,keep", [(4095, 700), (2100, 300), (1600, 1), (999, 64), (702, 9)])
+def test_topk_selection_wide_rows(dev, nb, keep):
+    """Rows of 702 to 4095 key blocks: 11 to 64 blocks per lane of the selection
+    wave (every register layout above 8), with 2 heads in one launch."""
+    per = nb // 3
+    lay = custom_layout(3, 64 * per, 64 * per - 30, 64, heads=2)
+    host, vals = random_inputs(lay, 5 + nb)
+    dev_in = tuple(to_dev(x, dev) for x in host)
+    keeps = np.array([keep, max(1, keep // 2)], dtype=np.int32)
+    say(f"topk wide rows: nb {lay.nblocks}, keep {keeps.tolist()}")
+    scores = torch.empty((1, lay.heads, lay.nblocks, lay.nblocks), dtype=torch.float32,
+                         device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.TOPK, keeps, q=dev_in[0], k=dev_in[1],
+                                    force=True if keep > 3 else False, scores_out=scores)
+    torch.cuda.synchronize()
+    mism = check_topk(lay, vals, keeps, keep > 3, rp.cpu().numpy(), ci.cpu().numpy(),
+                      scores.cpu().numpy(), st.cpu().numpy())
+    say(f"topk wide rows: near-tie rows {mism}")
+
+
+def test_cdf_selection_wide_rows(dev):
+    lay = custom_layout(3, 64 * 700, 64 * 700 - 30, 64, heads=1)
+    host, vals = planted_peaked(lay, 43)
+    keep = np.array([500], dtype=np.int32)
+    say(f"cdf wide rows: nb {lay.nblocks}")
+    q, k = to_dev(host[0], dev), to_dev(host[1], dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.CDF, keep, q=q, k=k, cdf_tau=0.9)
+    torch.cuda.synchronize()
+    bound, mism = check_cdf(lay, vals, keep, 0.9, False, rp.cpu().numpy(), ci.cpu().numpy(),
+                            st.cpu().numpy())
+    say(f"cdf wide rows: rows stopped by the threshold {bound}, near-tie rows {mism}")
+
+
 def test_topk_deterministic(dev):
     w, data = preset(1, heads=2)
     q, k, _ = inputs(w, data, dev)
