@@ -6,15 +6,18 @@
 // ascending key-block order; K and V tiles (BLK x 64 bf16) are staged in LDS,
 // double-buffered: right after the barrier that opens a tile, the waves issue
 // direct global->LDS copies of the next tile into the other buffer, which land
-// while the current tile's math runs. The row's column list, each entry packed
-// with the number of real keys of its block, is kept in an LDS ring so that
-// the loop reads no global memory besides the tiles.
+// while the current tile's math runs. The row's column list is kept in an LDS
+// ring, entry x packing the block of tile x + 1 (whose copy tile x issues) with
+// the number of real keys of tile x, so the loop reads one LDS word and no
+// global memory besides the tiles per tile.
 //
-// Softmax uses a lazy reference maximum: the running maximum m of a query row
-// moves (and O, l are rescaled) only when a tile's maximum exceeds it by more
-// than 8 in log2 units, so P = exp2((s - m) c) stays below 2^8 and most tiles
-// skip the rescale. The row sum is taken from the bf16-rounded P, the values
-// that enter the second MFMA.
+// Softmax keeps a reference maximum m per query row instead of a running one:
+// m is the maximum of the row's first tile, and it moves (O and l rescaled)
+// only when a later tile would make some P = exp2((s - m) c) exceed 2^64, which
+// is detected from the tile's row sum (no per-tile maximum). P that large is
+// still far inside the fp32 and bf16 ranges, and the softmax is the same for
+// any reference. The row sum is taken from the bf16-rounded P, the values that
+// enter the second MFMA.
 //
 // Math per key tile, per wave (online softmax, exp2 with the scale folded in):
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q in VGPRs
@@ -116,10 +119,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   const float c2 = d.scale * 1.4426950408889634f;
 
   const int nt = end - beg;
-  for (int x = tid; x < min(nt, CB); x += NT) {
+  // entry x: the next tile's block (for its copy) and this tile's real-key count
+  auto entry = [&](int x) {
     const int c = a.col_idx[beg + x];
-    colbuf[x] = (c << 7) | (block_vlen(d, c) - 1);
-  }
+    const int cn = x + 1 < nt ? a.col_idx[beg + x + 1] : 0;
+    return (cn << 7) | (block_vlen(d, c) - 1);
+  };
+  for (int x = tid; x < min(nt, CB); x += NT) colbuf[x] = entry(x);
   if (nt > 0) BSGM_DMA(0, a.col_idx[beg]);
 
   for (int it = beg; it < end; ++it) {
@@ -128,57 +134,82 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
     wait_dma();
     __syncthreads();
     if ((jt & (CB / 2 - 1)) == 0 && jt > 0 && jt + CB / 2 < nt)
-      for (int x = jt + CB / 2 + tid; x < min(nt, jt + CB); x += NT) {
-        const int c = a.col_idx[beg + x];
-        colbuf[x & (CB - 1)] = (c << 7) | (block_vlen(d, c) - 1);
-      }
+      for (int x = jt + CB / 2 + tid; x < min(nt, jt + CB); x += NT) colbuf[x & (CB - 1)] = entry(x);
     const int ecur = __builtin_amdgcn_readfirstlane(colbuf[jt & (CB - 1)]);
     const bool has_next = it + 1 < end;
-    if (has_next) {
-      const int en = __builtin_amdgcn_readfirstlane(colbuf[(jt + 1) & (CB - 1)]);
-      BSGM_DMA(buf ^ 1, en >> 7);
-    }
+    if (has_next) BSGM_DMA(buf ^ 1, ecur >> 7);
     const unsigned char* kb = smem + buf * 2 * TB;
     const unsigned char* vb = kb + TB;
 
-    f32x16 s[KT];
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) s[t][x] = 0.f;
-      const int row = 32 * t + pim;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(kb + row * 128 + (((2 * ks + hh) ^ swz(row)) << 4));
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[t], 0, 0, 0);
-      }
-    }
-
     const int vlen = (ecur & 127) + 1;
-    if (vlen < BLK) {
+    auto scores = [&](f32x16 (&s)[KT]) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) s[t][x] = 0.f;
+        const int row = 32 * t + pim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(kb + row * 128 + (((2 * ks + hh) ^ swz(row)) << 4));
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[t], 0, 0, 0);
+        }
+      }
+      if (vlen < BLK) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int key = 32 * t + 16 * (x >> 3) + 8 * hh + (x & 7);
+            if (key >= vlen) s[t][x] = -INFINITY;
+          }
+      }
+    };
+    f32x16 s[KT];
+    scores(s);
+
+    bf16x8 pb[KT][2];
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    auto soft = [&](const f32x16 (&s)[KT]) {
+      const float mb = m_run * c2;
+      float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int key = 32 * t + 16 * (x >> 3) + 8 * hh + (x & 7);
-          if (key >= vlen) s[t][x] = -INFINITY;
+        for (int e = 0; e < 2; ++e) {
+          float pf[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) pf[x] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * e + x], c2, -mb));
+          const bf16x8 pv = {(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3],
+                             (__bf16)pf[4], (__bf16)pf[5], (__bf16)pf[6], (__bf16)pf[7]};
+          pb[t][e] = pv;
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, psum, false);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, psum, false);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, psum, false);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, psum, false);
         }
-    }
-
-    float mx = -INFINITY;
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum),
+                                                       false, false);
+      return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    };
+    float psum = soft(s);
+    // The reference m stays while every P of the row is at most 2^64 (far from
+    // the fp32 and bf16 range limits). A row whose sum passes that, or is not
+    // finite (the first tile, where m is still -inf), moves m to the maximum of
+    // this tile's scores, recomputed from the K tile still in LDS.
+    if (__ballot(!(psum <= 1.8446744e19f))) {
+      const bool big = !(psum <= 1.8446744e19f);
+      scores(s);
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[t][x]);
-    {
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[t][x]);
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
       mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-    }
-    const bool grow = (mx - m_run) * c2 > 8.f;
-    if (__ballot(grow)) {
-      const float m_new = grow ? mx : m_run;
+      const float m_new = big ? fmaxf(m_run, mx) : m_run;
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll
@@ -186,31 +217,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) oacc[mt][x] *= alpha;
       m_run = m_new;
-    }
-    const float mb = m_run * c2;
-    bf16x8 pb[KT][2];
-    float psum = 0.f;
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float pf[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) pf[x] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * e + x], c2, -mb));
-        const bf16x8 pv = {(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3],
-                           (__bf16)pf[4], (__bf16)pf[5], (__bf16)pf[6], (__bf16)pf[7]};
-        pb[t][e] = pv;
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, psum, false);
-      }
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum),
-                                                       false, false);
-      psum = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      psum = soft(s);
     }
     l_run += psum;
 

@@ -351,6 +351,37 @@ def test_attention_constant_values_and_lse_merge(dev):
     assert float((torch.logaddexp(ls_, ld_)[0, 0, valid] - la_[0, 0, valid]).abs().max()) <= 2e-3
 
 
+@pytest.mark.parametrize("dtype,block", [("bf16", 128), ("bf16", 64)])
+def test_attention_growing_logits(dev, dtype, block):
+    """Key blocks whose logits grow along the list by up to ~60 (moderate) and
+    ~330 (past the rescale bound of a 2^64 softmax weight) in log2 units over
+    the first kept block: every row must still match the float64 softmax."""
+    lay = custom_layout(2, 4 * block, 4 * block - 20, block, heads=2, dtype=dtype)
+    nb, N, D = lay.nblocks, lay.tokens, lay.head_dim
+    rng = np.random.default_rng(91 + block)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = np.zeros((1, 2, N, D), np.float32)
+    k = np.zeros_like(q)
+    blk_of = np.arange(N) // block
+    for h, top in enumerate((40.0, 220.0)):      # logit of the last block: scale * 8 * top
+        q[0, h] = 8.0 * u[None, :] + 0.05 * rng.standard_normal((N, D))
+        growth = np.linspace(0.2, top, nb)[blk_of]
+        k[0, h] = growth[:, None] * u[None, :] + 0.05 * rng.standard_normal((N, D))
+    v = rng.standard_normal(q.shape).astype(np.float32)
+    pad = (np.arange(N) % lay.frame_len) >= lay.frame_valid
+    for a_ in (q, k, v):
+        a_[:, :, pad] = 0
+    if dtype == "bf16":
+        host = [workloads.bf16_bits_from_float(a_) for a_ in (q, k, v)]
+        vals = [workloads.float_from_bf16_bits(b) for b in host]
+    else:
+        host = vals = [q, k, v]
+    rows = [list(range(nb)) for _ in range(lay.heads * nb)]
+    o, lse = run_attention_case(dev, lay, host, vals, rows, f"growing logits {dtype} block {block}")
+    assert np.all(np.isfinite(o))
+
+
 # --------------------------------------------------------------------------
 # CDF selection
 # --------------------------------------------------------------------------
