@@ -14,8 +14,8 @@ Sources (pages, by title):
   * "ReSS: Residual-Restoring Sparse Attention for 3D Vision Transformers"
     (thelatestinai.com, 2609.35593) - abstract, Figs. 1-3, Tables 1, 2, S3, S5.
   * "VASC: Value-Aware Sparse Attention with Cross-Layer Memory for Efficient
-    3D Reconstruction" (paperlayer.ai summary, 2610.01013v1) - sections 3, 4.2,
-    A.1, A.2, A.5.
+    3D Reconstruction" (paperlayer.ai summary, 2610.01013v1) - sections 3,
+    4.1-4.3, A.1-A.5 (value-aware selection and pair memory: oracle/vasc.py).
 
 Parity status: every function below is pinned by tests/test_oracle_*.py
 (closed forms, brute force, exhaustive search, hand-derived golden fixtures).
@@ -23,3 +23,4 @@ Equivalence with the published ReSS / SparseVGGT / VASC code is parity
 unpinned: no code or step-level numbers of theirs exist on the pages.
 """
 from .reference import *  # noqa: F401,F403
+from .vasc import *  # noqa: F401,F403
