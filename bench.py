@@ -14,7 +14,9 @@ executed block pair) divided by the measured time of the whole step.
 `detail.other_layers` gives the per-layer times of the other presets (8 frames
 at 50 %, 100 frames with the cumulative-mass rule and per-head caps, 16 frames
 with drift selection and three restoration rounds), each phase timed over
-back-to-back launches; they are side measurements, not part of `value`.
+back-to-back launches; `detail.special_rows_dense` and `detail.vasc_selection`
+time the dense camera/register rows and the value-aware selection with pair
+memory on the bench layer. All are side measurements, not part of `value`.
 """
 from __future__ import annotations
 
@@ -214,6 +216,22 @@ def main():
         "rows_per_frame": ns, "ms": round(sp_ms, 4),
         "gflop": round(sp_flops / 1e9, 3),
         "tflops": round(sp_flops / (sp_ms * 1e-3) / 1e12, 2)}
+
+    # value-aware selection with pair memory on the same layer and budget; each
+    # call is one layer (the memory carries over), timed over back-to-back calls
+    vmem = torch.zeros((lay.batch, lay.heads, bsgm.vasc_pairs(lay)), dtype=torch.float32,
+                       device=dev)
+    vws = torch.empty(bsgm.workspace_bytes(lay, bsgm.VASC), dtype=torch.uint8, device=dev)
+
+    def vasc_select():
+        bsgm.vasc_select_blocks(lay, keep, q, k, v, vmem, force=True, row_ptr=row_ptr,
+                                col_idx=col_idx, workspace=vws, want_stat=False)
+    vasc_ms = gpu_ms(torch, vasc_select, 10)
+    vasc_attn_ms = gpu_ms(torch, attend, 5)
+    detail["vasc_selection"] = {
+        "select_ms": round(vasc_ms, 4), "attn_ms": round(vasc_attn_ms, 4),
+        "layers_carried": 11, "max_pair_deficit": round(float(vmem.max()), 4),
+        "executed_block_pairs": int(row_ptr[-1].item())}
 
     if not args.no_side:
         detail["other_layers"] = {

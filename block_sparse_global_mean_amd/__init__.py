@@ -1,13 +1,13 @@
 """Block-sparse global attention for multi-view geometry transformers on MI355X.
 
-Selection (pooled top-k, cumulative pooled mass, or drift score with swap
-restoration), the block-sparse attention forward and the dense attention of the
-camera/register query rows run in the HIP kernels of
-libbsgm.so; this package is the thin ctypes binding to its C ABI
-(include/bsgm.h).
+Selection (pooled top-k, cumulative pooled mass, drift score with swap
+restoration, or value-aware demand with cross-layer pair memory), the
+block-sparse attention forward and the dense attention of the camera/register
+query rows run in the HIP kernels of libbsgm.so; this package is the thin
+ctypes binding to its C ABI (include/bsgm.h).
 """
 from ._lib import (  # noqa: F401
-    BF16, CDF, DRIFT, DROPPED_SUM, F32, RENORMALISED, TOPK, BsgmError, EXPORTS, LIB_PATH, col_capacity, drift_scores,
-    library, pool_blocks, select_blocks, sparse_attn_fwd, special_rows_dense_fwd,
-    special_rows_workspace_bytes, version, workspace_bytes,
+    BF16, CDF, DRIFT, DROPPED_SUM, F32, RENORMALISED, TOPK, VASC, BsgmError, EXPORTS, LIB_PATH,
+    col_capacity, drift_scores, library, pool_blocks, select_blocks, sparse_attn_fwd, special_rows_dense_fwd,
+    special_rows_workspace_bytes, vasc_pairs, vasc_select_blocks, version, workspace_bytes,
 )

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbsgm.so")
 
 F32, BF16 = 0, 1
-TOPK, CDF, DRIFT = 0, 1, 2
+TOPK, CDF, DRIFT, VASC = 0, 1, 2, 3
 # Drift objectives: the norm of the dropped blocks' summed contribution, or the
 # output shift after the kept blocks are renormalised.
 DROPPED_SUM, RENORMALISED = 0, 1
@@ -27,7 +27,8 @@ STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_
 # Every symbol include/bsgm.h declares.
 EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_capacity",
            "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
-           "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd")
+           "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
+           "bsgm_vasc_select_blocks")
 
 
 class BsgmError(RuntimeError):
@@ -76,8 +77,11 @@ def library() -> ctypes.CDLL:
         lib.bsgm_special_rows_workspace_bytes.argtypes = [lp, ctypes.c_int32]
         lib.bsgm_special_rows_workspace_bytes.restype = sz
         lib.bsgm_special_rows_dense_fwd.argtypes = [lp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
+        lib.bsgm_vasc_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
+                                                vp, vp, sz, vp]
         for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
-                     "bsgm_sparse_attn_fwd"):
+                     "bsgm_sparse_attn_fwd", "bsgm_special_rows_dense_fwd",
+                     "bsgm_vasc_select_blocks"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -223,6 +227,43 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return row_ptr, col_idx, row_stat
+
+
+def vasc_pairs(layout) -> int:
+    """Pairs of adjacent key blocks per (b, h): ceil(Nb / 2)."""
+    return (_dims(layout)[1] + 1) // 2
+
+
+def vasc_select_blocks(layout, keep: Sequence[int], q, k, v, memory, force: bool = False,
+                       row_ptr=None, col_idx=None, row_stat=None, demand_out=None,
+                       workspace=None, want_stat: bool = True, stream=None):
+    """One layer of value-aware selection; updates `memory` (float32
+    [B, H, ceil(Nb/2)], zero for a new inference) in place. Returns (row_ptr,
+    col_idx, row_stat)."""
+    n, nb, rows = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, _tdtype(layout), shape)
+    _expect(memory, "memory", torch.float32, (layout.batch, layout.heads, vasc_pairs(layout)))
+    if demand_out is not None:
+        _expect(demand_out, "demand_out", torch.float32, (layout.batch, layout.heads, nb, nb))
+    dev = q.device
+    cap = col_capacity(layout, VASC, keep, force)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_stat is None and want_stat:
+        row_stat = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(layout, VASC), dtype=torch.uint8, device=dev)
+    L = c_layout(layout)
+    P, _keep = c_params(VASC, keep, force=force)
+    _check(library().bsgm_vasc_select_blocks(
+        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(v), _ptr(memory), _ptr(row_ptr),
+        _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(demand_out), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 

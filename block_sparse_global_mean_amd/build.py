@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsgm.so")
-SOURCES = ["api.hip", "pool.hip", "select.hip", "drift.hip", "drift_mfma.hip", "attn_bf16.hip", "attn_f32.hip", "dense_rows.hip"]
+SOURCES = ["api.hip", "pool.hip", "select.hip", "drift.hip", "drift_mfma.hip", "attn_bf16.hip", "attn_f32.hip", "dense_rows.hip", "vasc.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

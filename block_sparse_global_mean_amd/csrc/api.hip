@@ -79,8 +79,10 @@ int check_layout(const bsgm_layout* L, bsgm::Dims* d) {
 using bsgm::align256;
 
 struct WsLayout {
-  size_t qbar, kbar, counts, bitmask, stats, mz, total;
+  size_t qbar, kbar, counts, bitmask, stats, mz, vbar, fac, mhat, pdem, pexe, total;
 };
+
+int vasc_pairs(const bsgm::Dims& d) { return (d.nb + 1) / 2; }
 
 WsLayout ws_layout(const bsgm::Dims& d, int mode) {
   WsLayout w{};
@@ -88,9 +90,22 @@ WsLayout ws_layout(const bsgm::Dims& d, int mode) {
   size_t off = 0;
   w.qbar = off;
   off += align256(pooled);
-  if (mode == BSGM_SEL_TOPK || mode == BSGM_SEL_CDF) {
+  if (mode == BSGM_SEL_TOPK || mode == BSGM_SEL_CDF || mode == BSGM_SEL_VASC) {
     w.kbar = off;
     off += align256(pooled);
+  }
+  if (mode == BSGM_SEL_VASC) {
+    const size_t np = (size_t)vasc_pairs(d);
+    w.vbar = off;
+    off += align256(pooled);
+    w.fac = off;
+    off += align256((size_t)d.B * d.H * np * sizeof(float));
+    w.mhat = off;
+    off += align256((size_t)d.B * d.H * np * sizeof(float));
+    w.pdem = off;
+    off += align256((size_t)d.rows * np * sizeof(float));
+    w.pexe = off;
+    off += align256((size_t)d.rows * np * sizeof(float));
   }
   if (mode == BSGM_SEL_DRIFT) {
     w.stats = off;
@@ -139,7 +154,8 @@ const char* bsgm_last_error(void) { return g_err.c_str(); }
 size_t bsgm_workspace_bytes(const bsgm_layout* layout, int32_t mode) {
   bsgm::Dims d;
   if (check_layout(layout, &d) != BSGM_OK) return 0;
-  if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF && mode != BSGM_SEL_DRIFT) {
+  if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF && mode != BSGM_SEL_DRIFT &&
+      mode != BSGM_SEL_VASC) {
     fail(BSGM_E_ARG, "unknown selection mode %d", mode);
     return 0;
   }
@@ -237,6 +253,8 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
   st = check_budget(d, params, &hb);
   if (st != BSGM_OK) return st;
   const int mode = params->mode;
+  if (mode == BSGM_SEL_VASC)
+    return fail(BSGM_E_ARG, "VASC selection carries memory: use bsgm_vasc_select_blocks");
   if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF && mode != BSGM_SEL_DRIFT)
     return fail(BSGM_E_ARG, "unknown selection mode %d", mode);
   if (!row_ptr || !col_idx) return fail(BSGM_E_ARG, "row_ptr and col_idx must be non-NULL");
@@ -288,6 +306,59 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
                                  params->force_frame_first_block ? 1 : 0, qbar, kbar, row_ptr,
                                  col_idx, row_stat, scores_out, counts, bitmask, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+int bsgm_vasc_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,
+                            const void* q, const void* k, const void* v, float* memory,
+                            int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                            float* row_stat, float* demand_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  bsgm::HeadBudget hb;
+  st = check_budget(d, params, &hb);
+  if (st != BSGM_OK) return st;
+  if (params->mode != BSGM_SEL_VASC)
+    return fail(BSGM_E_ARG, "params->mode must be BSGM_SEL_VASC (got %d)", params->mode);
+  if (!q || !k || !v || !memory || !row_ptr || !col_idx || !ws)
+    return fail(BSGM_E_ARG, "q, k, v, memory, row_ptr, col_idx and ws must be non-NULL");
+  const long long need = (long long)d.B * hb.per_batch;
+  if (need > 0x7FFFFFFFLL)
+    return fail(BSGM_E_UNSUPPORTED, "worst-case nnz %lld does not fit int32 CSR", need);
+  if (col_capacity < need)
+    return fail(BSGM_E_CAPACITY, "col_capacity %lld below worst-case nnz %lld",
+                (long long)col_capacity, need);
+  if (d.nb > bsgm::kSelectMaxBlocks)
+    return fail(BSGM_E_UNSUPPORTED, "pooled selection supports at most %d blocks per row",
+                bsgm::kSelectMaxBlocks);
+  const WsLayout w = ws_layout(d, BSGM_SEL_VASC);
+  if (ws_bytes < w.total)
+    return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  char* base = static_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(base + w.qbar);
+  float* kbar = reinterpret_cast<float*>(base + w.kbar);
+  float* vbar = reinterpret_cast<float*>(base + w.vbar);
+  const int np = vasc_pairs(d);
+  float* fac = reinterpret_cast<float*>(base + w.fac);
+  float* mhat = reinterpret_cast<float*>(base + w.mhat);
+  float* pdem = reinterpret_cast<float*>(base + w.pdem);
+  float* pexe = reinterpret_cast<float*>(base + w.pexe);
+  const bsgm::VascSel vs{np, fac, mhat, pdem, pexe, demand_out};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
+  if (e == hipSuccess) e = bsgm::launch_pool(d, layout->dtype, k, kbar, s);
+  if (e == hipSuccess) e = bsgm::launch_pool(d, layout->dtype, v, vbar, s);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  e = bsgm::launch_vasc_prep(d, np, vbar, memory, fac, mhat, s);
+  if (e != hipSuccess) return hip_fail(e, "vasc prep launch");
+  e = bsgm::launch_select_pooled(d, hb, BSGM_SEL_VASC, 0.f, params->force_frame_first_block ? 1 : 0,
+                                 qbar, kbar, row_ptr, col_idx, row_stat, nullptr, nullptr, nullptr,
+                                 s, &vs);
+  if (e != hipSuccess) return hip_fail(e, "vasc select launch");
+  e = bsgm::launch_vasc_update(d, np, pdem, pexe, memory, s);
+  if (e != hipSuccess) return hip_fail(e, "vasc memory launch");
   return ok();
 }
 

@@ -31,12 +31,32 @@ struct HeadBudget {
 // Pooling: mean over real tokens of each block. dtype: 0 f32, 1 bf16.
 hipError_t launch_pool(const Dims& d, int dtype, const void* x, float* mean, hipStream_t s);
 
-// Pooled selection (TOPK = 0, CDF = 1) from pooled Q and K.
+// Value-aware selection state for one layer (mode 3): per (b, h) and pair of
+// key blocks the contrast factor and the memory's ranking copy (inputs), per
+// row and pair the summed clipped demand and executed children (outputs).
+struct VascSel {
+  int npairs;
+  const float* pair_fac;
+  const float* mhat;
+  float* pair_dem;
+  float* pair_exe;
+  float* demand_out;   // [rows, nb] or null
+};
+
+// Pooled selection (TOPK = 0, CDF = 1, VASC = 3 with vasc set) from pooled Q and K.
 hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, float tau,
                                 int force, const float* qbar, const float* kbar,
                                 int32_t* row_ptr, int32_t* col_idx, float* row_stat,
                                 float* scores_out, int32_t* counts, uint32_t* bitmask,
-                                hipStream_t s);
+                                hipStream_t s, const VascSel* vasc = nullptr);
+
+// VASC, before selection: pair contrast factors and the memory's ranking copy
+// from the pooled values and the raw memory [B*H, npairs].
+hipError_t launch_vasc_prep(const Dims& d, int npairs, const float* vbar, const float* memory,
+                            float* pair_fac, float* mhat, hipStream_t s);
+// VASC, after selection: memory += mean demand - mean execution per pair.
+hipError_t launch_vasc_update(const Dims& d, int npairs, const float* pair_dem,
+                              const float* pair_exe, float* memory, hipStream_t s);
 
 // Drift contributions and scores from pooled Q and K, V.
 hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, const void* k,

@@ -11,6 +11,8 @@
 // largest key, and the smallest prefix reaching the mass threshold, are found
 // exactly by an MSB-first bitwise search, so no sort is needed: counts come from
 // ballots and masses from cross-lane sums that stay on the VALU.
+#include <type_traits>
+
 #include "device_util.h"
 
 namespace bsgm {
@@ -18,7 +20,7 @@ namespace bsgm {
 struct SelArgs {
   Dims d;
   HeadBudget hb;
-  int mode;            // 0 TOPK, 1 CDF
+  int mode;            // 0 TOPK, 1 CDF, 3 VASC
   float tau;
   int force;
   const float* qbar;
@@ -29,12 +31,21 @@ struct SelArgs {
   float* scores_out;
   int32_t* counts;     // CDF: kept count per row
   uint32_t* bitmask;   // CDF: kept flags, ceil(nb/32) words per row
+  // VASC: per (b, h) and pair of key blocks, the contrast factor 1 + c / cbar
+  // and the ranking copy of the memory; per row and pair, the summed clipped
+  // demand and the number of executed children
+  int npairs;
+  const float* pair_fac;
+  const float* mhat;
+  float* pair_dem;
+  float* pair_exe;
+  float* demand_out;   // VASC: [rows, nb] clipped demand, or null
 };
 
 constexpr int kSelRowsPerWg = 4;
 constexpr int kKtStride = 68;   // LDS row stride (floats) of the pooled-K tile
 
-template <int PW>   // key blocks per lane: nb <= 64 * PW
+template <int PW, bool VASC>   // key blocks per lane: nb <= 64 * PW; VASC: mode 3
 __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
   __shared__ __attribute__((aligned(16))) float kt[2][64 * kKtStride];
   const Dims& d = a.d;
@@ -107,21 +118,48 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
 #pragma unroll
   for (int p = 0; p < PW; ++p) {
     const int j = 64 * p + lane;
-    const bool valid = j < d.nb;
-    P[p] = valid ? expf(S[p] - mx) : 0.f;
+    P[p] = j < d.nb ? expf(S[p] - mx) : 0.f;
     esum += P[p];
-    if (valid) {
-      const bool f = a.force && block_forced(d, j);
-      const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(S[p]);
-      key[p] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
-      if (a.scores_out) a.scores_out[(size_t)r * d.nb + j] = S[p];
-    } else {
-      key[p] = 0ull;   // sorts below every real key, whose high word is nonzero
-    }
+    if (j < d.nb && a.scores_out) a.scores_out[(size_t)r * d.nb + j] = S[p];
   }
   const float inv = 1.f / wave_allsum(esum);
 #pragma unroll
   for (int p = 0; p < PW; ++p) P[p] *= inv;
+
+  // ranking value: the pooled score, or for VASC the clipped value-aware
+  // demand d = min(1, k a / sum a), a = P (1 + c / cbar), plus the memory copy
+  float dem[VASC ? PW : 1];
+  if constexpr (VASC) {
+    const float* fac = a.pair_fac + (size_t)bh * a.npairs;
+    float asum = 0.f;
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int j = 64 * p + lane;
+      dem[p] = j < d.nb ? P[p] * fac[j >> 1] : 0.f;
+      asum += dem[p];
+    }
+    asum = wave_allsum(asum);
+    const float kf = (float)a.hb.keep[h];
+    const float* mh = a.mhat + (size_t)bh * a.npairs;
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int j = 64 * p + lane;
+      dem[p] = j < d.nb ? fminf(1.f, kf * dem[p] / asum) : 0.f;
+      S[p] = j < d.nb ? dem[p] + mh[j >> 1] : 0.f;
+      if (j < d.nb && a.demand_out) a.demand_out[(size_t)r * d.nb + j] = dem[p];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    const int j = 64 * p + lane;
+    if (j < d.nb) {
+      const bool f = a.force && block_forced(d, j);
+      const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(S[p]);
+      key[p] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
+    } else {
+      key[p] = 0ull;   // sorts below every real key, whose high word is nonzero
+    }
+  }
 
   const int nforced = a.force ? d.F : 0;
   int k;
@@ -163,6 +201,20 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
   }
   km = wave_allsum(km);
   if (lane == 0 && a.row_stat) a.row_stat[r] = km;
+
+  if constexpr (VASC) {
+    // pair p of tile t holds keys 64t + 2p' and 64t + 2p' + 1: lanes l and l ^ 1
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const float dv = dem[p], xv = kept[p] ? 1.f : 0.f;
+      const float ds = dv + dpp_mov<0xB1>(dv), xs = xv + dpp_mov<0xB1>(xv);
+      const int pair = 32 * p + (lane >> 1);
+      if ((lane & 1) == 0 && pair < a.npairs) {
+        a.pair_dem[(size_t)r * a.npairs + pair] = ds;
+        a.pair_exe[(size_t)r * a.npairs + pair] = xs;
+      }
+    }
+  }
 
   if (a.mode == 1) {
     const int words = (d.nb + 31) >> 5;
@@ -263,21 +315,34 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
                                 int force, const float* qbar, const float* kbar,
                                 int32_t* row_ptr, int32_t* col_idx, float* row_stat,
                                 float* scores_out, int32_t* counts, uint32_t* bitmask,
-                                hipStream_t s) {
+                                hipStream_t s, const VascSel* vasc) {
   SelArgs a{d, hb, mode, tau, force, qbar, kbar, row_ptr, col_idx, row_stat, scores_out,
-            counts, bitmask};
+            counts, bitmask, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (vasc) {
+    a.npairs = vasc->npairs;
+    a.pair_fac = vasc->pair_fac;
+    a.mhat = vasc->mhat;
+    a.pair_dem = vasc->pair_dem;
+    a.pair_exe = vasc->pair_exe;
+    a.demand_out = vasc->demand_out;
+  }
   const int per = (d.nb + 63) / 64;
   dim3 grid(d.B * d.H * ((d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg)), block(256);
-  if (per <= 1) hipLaunchKernelGGL(k_select_pooled<1>, grid, block, 0, s, a);
-  else if (per <= 2) hipLaunchKernelGGL(k_select_pooled<2>, grid, block, 0, s, a);
-  else if (per <= 4) hipLaunchKernelGGL(k_select_pooled<4>, grid, block, 0, s, a);
-  else if (per <= 8) hipLaunchKernelGGL(k_select_pooled<8>, grid, block, 0, s, a);
-  else if (per <= 12) hipLaunchKernelGGL(k_select_pooled<12>, grid, block, 0, s, a);
-  else if (per <= 16) hipLaunchKernelGGL(k_select_pooled<16>, grid, block, 0, s, a);
-  else if (per <= 24) hipLaunchKernelGGL(k_select_pooled<24>, grid, block, 0, s, a);
-  else if (per <= 32) hipLaunchKernelGGL(k_select_pooled<32>, grid, block, 0, s, a);
-  else if (per <= 48) hipLaunchKernelGGL(k_select_pooled<48>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_select_pooled<64>, grid, block, 0, s, a);
+  auto go = [&](auto pw) {
+    constexpr int PW = decltype(pw)::value;
+    if (mode == 3) hipLaunchKernelGGL((k_select_pooled<PW, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_select_pooled<PW, false>), grid, block, 0, s, a);
+  };
+  if (per <= 1) go(std::integral_constant<int, 1>{});
+  else if (per <= 2) go(std::integral_constant<int, 2>{});
+  else if (per <= 4) go(std::integral_constant<int, 4>{});
+  else if (per <= 8) go(std::integral_constant<int, 8>{});
+  else if (per <= 12) go(std::integral_constant<int, 12>{});
+  else if (per <= 16) go(std::integral_constant<int, 16>{});
+  else if (per <= 24) go(std::integral_constant<int, 24>{});
+  else if (per <= 32) go(std::integral_constant<int, 32>{});
+  else if (per <= 48) go(std::integral_constant<int, 48>{});
+  else go(std::integral_constant<int, 64>{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode != 1) return e;
   hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, s, counts, row_ptr, d.rows);

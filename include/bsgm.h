@@ -63,7 +63,8 @@ typedef enum { BSGM_F32 = 0, BSGM_BF16 = 1 } bsgm_dtype;
 typedef enum {
   BSGM_SEL_TOPK = 0,   /* fixed budget by pooled score                        */
   BSGM_SEL_CDF = 1,    /* cumulative pooled mass >= tau, capped per head      */
-  BSGM_SEL_DRIFT = 2   /* drift score + swap restoration at a fixed budget    */
+  BSGM_SEL_DRIFT = 2,  /* drift score + swap restoration at a fixed budget    */
+  BSGM_SEL_VASC = 3    /* value-aware demand + pair memory (bsgm_vasc_select_blocks) */
 } bsgm_sel_mode;
 
 typedef struct {
@@ -99,9 +100,10 @@ int32_t bsgm_version(void);
  * next call of this library on the same thread. */
 const char* bsgm_last_error(void);
 
-/* Device workspace that bsgm_select_blocks (TOPK, CDF) or bsgm_drift_scores
- * (mode = BSGM_SEL_DRIFT) needs for this layout; 0 if the layout is invalid
- * (see bsgm_last_error). bsgm_select_blocks in DRIFT mode needs none. */
+/* Device workspace that bsgm_select_blocks (TOPK, CDF), bsgm_drift_scores
+ * (mode = BSGM_SEL_DRIFT) or bsgm_vasc_select_blocks (mode = BSGM_SEL_VASC)
+ * needs for this layout; 0 if the layout is invalid (see bsgm_last_error).
+ * bsgm_select_blocks in DRIFT mode needs none. */
 size_t bsgm_workspace_bytes(const bsgm_layout* layout, int32_t mode);
 
 /* Worst-case number of CSR entries: batch * Nb * sum_h keep_per_head[h];
@@ -188,6 +190,37 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
 int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
                          const int32_t* row_ptr, const int32_t* col_idx,
                          void* o, float* lse, void* stream);
+
+/* Value-aware block selection with cross-layer pair memory ([VASC] 4.1-4.3,
+ * A.1-A.5), one layer: selection from the memory, then the memory update.
+ * Key blocks 2p and 2p+1 form pair p (an odd last block is a singleton).
+ * Per (b, h): contrast c_p = sqrt(mean_d (vbar_2p - vbar_2p+1)^2) of the pooled
+ * values (0 for the singleton), cbar = mean_p c_p. Per query block i, with P
+ * the row softmax of the pooled scores (as in bsgm_select_blocks) and
+ * k = keep_per_head[h]:
+ *   a_ij   = P_ij * (1 + c_p(j) / cbar)      (factor 1 when cbar = 0)
+ *   d_ij   = min(1, k * a_ij / sum_j a_ij)  (proportional clipping)
+ *   rho_ij = d_ij + max(0, R_p(j)) / max_p max(0, R_p)   (0 if no deficit)
+ * keeps the forced blocks (force_frame_first_block) and then the highest rho
+ * (ties: lower block), exactly k per row, emitted as CSR like TOPK. Then for
+ * every pair, with x the executed flags and the means over all query blocks
+ * and the pair's children:  R_p += mean(d) - mean(x).
+ *   params->mode must be BSGM_SEL_VASC; keep_per_head and
+ *   force_frame_first_block are used
+ *   q, k, v      device [B,H,N,D] of layout->dtype
+ *   memory       device float [B, H, (Nb+1)/2], in/out: the raw pair balance
+ *                R; zero it for a new inference or a new layout. The caller
+ *                owns it and carries it from layer to layer.
+ *   row_ptr, col_idx, col_capacity   as bsgm_select_blocks
+ *   row_stat     device float [B*H*Nb] or NULL: kept pooled mass sum_kept P
+ *   demand_out   device float [B,H,Nb,Nb] or NULL: d
+ *   ws           device, >= bsgm_workspace_bytes(layout, BSGM_SEL_VASC) bytes
+ */
+int bsgm_vasc_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,
+                            const void* q, const void* k, const void* v, float* memory,
+                            int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                            float* row_stat, float* demand_out, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Dense attention of the camera and register query rows ([VASC] 4.2 and A.5:
  * camera and register queries keep dense attention while patch queries use the

@@ -51,6 +51,9 @@ def test_workspace_sizes():
     al = lambda x: (x + 255) // 256 * 256
     assert ws(lay, bsgm.DRIFT) == rows * 64 * 4 + al(rows * nb * 8) + al(rows * 8)
     assert ws(lay, bsgm.CDF) == 2 * rows * 64 * 4 + 256 + 256
+    # pooled q, k, v; per (b, h) and pair: factor and memory copy; per row and
+    # pair: demand and execution (4 pairs of 8 blocks)
+    assert ws(lay, bsgm.VASC) == 3 * rows * 64 * 4 + 2 * al(2 * 4 * 4) + 2 * al(rows * 4 * 4)
     assert ws(lay, 7) == 0
 
 
@@ -121,6 +124,30 @@ def test_pool_and_drift_null_arguments():
                                  None) == -1
     assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, None, one, 10, None) == -4
     assert lib.bsgm_pool_blocks(None, one, one, None) == -1
+
+
+def test_vasc_argument_errors():
+    lib = bsgm.library()
+    lay = L()
+    c = _lib.c_layout(lay)
+    one = ctypes.c_void_p(16)
+    nbytes = ws(lay, bsgm.VASC)
+
+    def call(mode=bsgm.VASC, keep=(3, 3), force=False, q=one, v=one, mem=one, cap=48,
+             wsb=nbytes):
+        P, arr = _lib.c_params(mode, keep, force=force)
+        return lib.bsgm_vasc_select_blocks(ctypes.byref(c), ctypes.byref(P), q, one, v, mem, one,
+                                           one, cap, None, None, one, wsb, None)
+    assert call(mode=bsgm.TOPK) == -1
+    assert call(q=None) == -1 and call(v=None) == -1 and call(mem=None) == -1
+    assert call(keep=(0, 3)) == -1
+    assert call(keep=(3, 3), force=True) == -1             # 4 forced blocks > 3
+    assert call(cap=47) == -3
+    assert call(wsb=nbytes - 1) == -4
+    P, arr = _lib.c_params(bsgm.VASC, (3, 3))
+    assert lib.bsgm_select_blocks(ctypes.byref(c), ctypes.byref(P), one, one, None, None, one, one,
+                                  48, None, None, None, one, nbytes, None) == -1
+    assert lib.bsgm_last_error().decode() != ""
 
 
 def test_special_rows_workspace_and_errors():

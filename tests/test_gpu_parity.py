@@ -867,3 +867,95 @@ def test_special_rows_full_size_sampled(dev):
             assert abs(lg[0, h, t] - lrf[n]) <= 2e-3 * max(1.0, abs(lrf[n]))
         # rows that are not special are left alone
         assert float(np.abs(og[0, h, 5:lay.frame_len]).max()) == 0.0
+
+
+# --------------------------------------------------------------------------
+# value-aware selection with pair memory
+# --------------------------------------------------------------------------
+def check_vasc(lay, vals, keep, force, mem_before, rpn, cin, stat_g, dem_g, mem_after_g,
+               rows_to_check=None):
+    """Selection of one layer against the oracle's demand and ranking (rows a
+    valid top-k by rho up to the 1e-4 gap), and the memory update against the
+    oracle's demand and the GPU's own executed flags."""
+    q, k, v = vals
+    nb = lay.nblocks
+    parity.check_csr_wellformed(rpn, cin, nb)
+    rows = parity.csr_rows(rpn, cin)
+    forced = oracle.forced_blocks(lay, force)
+    mism = 0
+    for b in range(lay.batch):
+        for h in range(lay.heads):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            qbar = oracle.pool(q[sl], lay)[0, 0]
+            kbar = oracle.pool(k[sl], lay)[0, 0]
+            vbar = oracle.pool(v[sl], lay)[0, 0]
+            p = oracle.row_softmax(lay.scale * (qbar @ kbar.T))
+            c = oracle.pair_contrast(vbar)
+            mhat = oracle.memory_rank_copy(mem_before[b, h])
+            kh = int(keep[h])
+            d = np.zeros((nb, nb))
+            x = np.zeros((nb, nb))
+            for i in range(nb):
+                r = (b * lay.heads + h) * nb + i
+                _, d[i] = oracle.demand_row(p[i], c, kh)
+                x[i, rows[r]] = 1.0
+                if rows_to_check is not None and i not in rows_to_check:
+                    continue
+                rho = d[i] + mhat[np.arange(nb) // 2]
+                exact = oracle.select_topk_row(rho, kh, forced)
+                if rows[r] != exact:
+                    mism += 1
+                    assert parity.topk_valid(rows[r], rho, kh, forced), \
+                        f"row {(b, h, i)}: {rows[r]} vs oracle {exact}"
+                assert abs(stat_g[r] - p[i, rows[r]].sum()) < 1e-4
+                if dem_g is not None:
+                    assert np.abs(dem_g[b, h, i] - d[i]).max() <= 1e-5, (b, h, i)
+            want = oracle.memory_update(mem_before[b, h], d, x)
+            assert np.abs(mem_after_g[b, h] - want).max() <= 1e-5, (b, h)
+    return mism
+
+
+def run_vasc_layers(dev, lay, host, vals, keep, force, layers, rows_to_check=None, label=""):
+    q, k, v = (to_dev(x_, dev) for x_ in host)
+    nb = lay.nblocks
+    mem = torch.zeros((lay.batch, lay.heads, bsgm.vasc_pairs(lay)), dtype=torch.float32,
+                      device=dev)
+    dem = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    total = 0
+    for layer in range(layers):
+        before = mem.cpu().numpy().astype(np.float64)
+        rp, ci, st = bsgm.vasc_select_blocks(lay, keep, q, k, v, mem, force=force, demand_out=dem)
+        torch.cuda.synchronize()
+        mism = check_vasc(lay, vals, keep, force, before, rp.cpu().numpy(), ci.cpu().numpy(),
+                          st.cpu().numpy(), dem.cpu().numpy(), mem.cpu().numpy().astype(np.float64),
+                          rows_to_check)
+        total += mism
+        say(f"vasc {label} layer {layer}: near-tie rows {mism}, "
+            f"max deficit {float(mem.max()):.4f}")
+    return total
+
+
+@pytest.mark.parametrize("dtype,block,force", [("bf16", 64, False), ("bf16", 128, True),
+                                               ("f32", 64, True), ("f32", 128, False)])
+def test_vasc_small_layouts_three_layers(dev, dtype, block, force):
+    """Ragged layouts with 40 (block 64) or 33 (block 128: odd, a singleton
+    pair) key blocks, two heads and batch 2, three layers carrying the memory."""
+    frames, per = (10, 4) if block == 64 else (11, 3)
+    lay = custom_layout(frames, per * block, per * block - 37, block, heads=2, dtype=dtype, batch=2)
+    host, vals = random_inputs(lay, 81 + block)
+    nf = frames if force else 0
+    keep = np.array([max(8, nf + 2), max(5, nf + 1)], dtype=np.int32)
+    say(f"vasc small {dtype} block {block} force {force}: nb {lay.nblocks}")
+    run_vasc_layers(dev, lay, host, vals, keep, force, 3, label="small")
+
+
+def test_vasc_layer32_full_size_sampled(dev):
+    """The 32-frame layer (16 heads, 352 blocks, 88 kept with the 32 forced
+    special blocks): two layers, sampled rows, every pair's memory."""
+    w, data = preset(2)
+    lay = w.layout
+    host = [data[n + "_bits"] for n in ("q", "k", "v")]
+    vals = (data["q"], data["k"], data["v"])
+    say("vasc 32 frames full size")
+    run_vasc_layers(dev, lay, host, vals, data["keep"], True, 2,
+                    rows_to_check={0, 1, 10, 11, 175, 351}, label="32 frames")
