@@ -118,7 +118,7 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB once (counter calibration)")
     ap.add_argument("--no-side", "--no-drift", dest="no_side", action="store_true",
-                    help="skip the per-layer side measurements of the other presets")
+                    help="skip the side measurements (other presets, value-aware selection)")
     ap.add_argument("--layer", default=None,
                     help="time only this other preset (e.g. vggt_layer_16f_drift) and print "
                          "its per-layer JSON; for profiling its kernels")
@@ -217,23 +217,22 @@ def main():
         "gflop": round(sp_flops / 1e9, 3),
         "tflops": round(sp_flops / (sp_ms * 1e-3) / 1e12, 2)}
 
-    # value-aware selection with pair memory on the same layer and budget; each
-    # call is one layer (the memory carries over), timed over back-to-back calls
-    vmem = torch.zeros((lay.batch, lay.heads, bsgm.vasc_pairs(lay)), dtype=torch.float32,
-                       device=dev)
-    vws = torch.empty(bsgm.workspace_bytes(lay, bsgm.VASC), dtype=torch.uint8, device=dev)
-
-    def vasc_select():
-        bsgm.vasc_select_blocks(lay, keep, q, k, v, vmem, force=True, row_ptr=row_ptr,
-                                col_idx=col_idx, workspace=vws, want_stat=False)
-    vasc_ms = gpu_ms(torch, vasc_select, 10)
-    vasc_attn_ms = gpu_ms(torch, attend, 5)
-    detail["vasc_selection"] = {
-        "select_ms": round(vasc_ms, 4), "attn_ms": round(vasc_attn_ms, 4),
-        "layers_carried": 11, "max_pair_deficit": round(float(vmem.max()), 4),
-        "executed_block_pairs": int(row_ptr[-1].item())}
-
     if not args.no_side:
+        # value-aware selection with pair memory on the same layer and budget; each
+        # call is one layer (the memory carries over), timed over back-to-back calls
+        vmem = torch.zeros((lay.batch, lay.heads, bsgm.vasc_pairs(lay)), dtype=torch.float32,
+                           device=dev)
+        vws = torch.empty(bsgm.workspace_bytes(lay, bsgm.VASC), dtype=torch.uint8, device=dev)
+
+        def vasc_select():
+            bsgm.vasc_select_blocks(lay, keep, q, k, v, vmem, force=True, row_ptr=row_ptr,
+                                    col_idx=col_idx, workspace=vws, want_stat=False)
+        vasc_ms = gpu_ms(torch, vasc_select, 10)
+        vasc_attn_ms = gpu_ms(torch, attend, 5)
+        detail["vasc_selection"] = {
+            "select_ms": round(vasc_ms, 4), "attn_ms": round(vasc_attn_ms, 4),
+            "layers_carried": 11, "max_pair_deficit": round(float(vmem.max()), 4),
+            "executed_block_pairs": int(row_ptr[-1].item())}
         detail["other_layers"] = {
             name: side_config(bsgm, workloads, torch, dev, name)
             for name in ("vggt_layer_8f_s50", "vggt_layer_100f_cdf", "vggt_layer_16f_drift")}

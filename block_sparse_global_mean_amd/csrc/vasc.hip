@@ -54,21 +54,41 @@ __global__ __launch_bounds__(256) void k_vasc_prep(Dims d, int npairs, const flo
   }
 }
 
-// One thread per (b, h, pair); rows summed in query-block order.
-__global__ __launch_bounds__(256) void k_vasc_update(Dims d, int npairs, const float* __restrict__ pair_dem,
-                                                     const float* __restrict__ pair_exe,
-                                                     float* __restrict__ memory) {
-  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (x >= (long long)d.B * d.H * npairs) return;
-  const int bh = (int)(x / npairs), p = (int)(x - (long long)bh * npairs);
-  const size_t base = (size_t)bh * d.nb * npairs + p;
+// One workgroup of 16 waves per (b, h) and 64 pairs: wave w sums the rows
+// i = w, w + 16, ... of its lane's pair, then wave 0 adds the 16 partial sums
+// in wave order (a fixed order: the result does not depend on scheduling).
+constexpr int kUpdWaves = 16;
+__global__ __launch_bounds__(64 * kUpdWaves) void k_vasc_update(Dims d, int npairs,
+                                                              const float* __restrict__ pair_dem,
+                                                              const float* __restrict__ pair_exe,
+                                                              float* __restrict__ memory) {
+  __shared__ float sd[kUpdWaves][64], sx[kUpdWaves][64];
+  const int chunks = (npairs + 63) / 64;
+  const int bh = blockIdx.x / chunks, p0 = (blockIdx.x - bh * chunks) * 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int p = p0 + lane;
   float dem = 0.f, exe = 0.f;
-  for (int i = 0; i < d.nb; ++i) {
-    dem += pair_dem[base + (size_t)i * npairs];
-    exe += pair_exe[base + (size_t)i * npairs];
+  if (p < npairs) {
+    const size_t base = (size_t)bh * d.nb * npairs + p;
+#pragma unroll 4
+    for (int i = w; i < d.nb; i += kUpdWaves) {
+      dem += pair_dem[base + (size_t)i * npairs];
+      exe += pair_exe[base + (size_t)i * npairs];
+    }
   }
-  const float n = (float)d.nb * (2 * p + 1 < d.nb ? 2.f : 1.f);
-  memory[x] += dem / n - exe / n;
+  sd[w][lane] = dem;
+  sx[w][lane] = exe;
+  __syncthreads();
+  if (w == 0 && p < npairs) {
+    float td = 0.f, tx = 0.f;
+#pragma unroll
+    for (int q = 0; q < kUpdWaves; ++q) {
+      td += sd[q][lane];
+      tx += sx[q][lane];
+    }
+    const float n = (float)d.nb * (2 * p + 1 < d.nb ? 2.f : 1.f);
+    memory[(size_t)bh * npairs + p] += td / n - tx / n;
+  }
 }
 
 hipError_t launch_vasc_prep(const Dims& d, int npairs, const float* vbar, const float* memory,
@@ -80,8 +100,8 @@ hipError_t launch_vasc_prep(const Dims& d, int npairs, const float* vbar, const 
 
 hipError_t launch_vasc_update(const Dims& d, int npairs, const float* pair_dem,
                               const float* pair_exe, float* memory, hipStream_t s) {
-  const long long n = (long long)d.B * d.H * npairs;
-  hipLaunchKernelGGL(k_vasc_update, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d, npairs,
+  const int chunks = (npairs + 63) / 64;
+  hipLaunchKernelGGL(k_vasc_update, dim3(d.B * d.H * chunks), dim3(64 * kUpdWaves), 0, s, d, npairs,
                      pair_dem, pair_exe, memory);
   return hipGetLastError();
 }
