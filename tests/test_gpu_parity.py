@@ -959,3 +959,16 @@ def test_vasc_layer32_full_size_sampled(dev):
     say("vasc 32 frames full size")
     run_vasc_layers(dev, lay, host, vals, data["keep"], True, 2,
                     rows_to_check={0, 1, 10, 11, 175, 351}, label="32 frames")
+
+
+@pytest.mark.parametrize("nb", [1099, 301])
+def test_vasc_wide_rows(dev, nb):
+    """Rows of 1099 and 301 key blocks (odd: a singleton pair), so the
+    value-aware mode runs in the 24- and 8-block-per-lane register layouts."""
+    lay = custom_layout(7, 64 * (nb // 7), 64 * (nb // 7) - 30, 64, heads=1)
+    assert lay.nblocks == nb
+    host, vals = random_inputs(lay, 13 + nb)
+    keep = np.array([max(9, nb // 5)], dtype=np.int32)
+    say(f"vasc wide rows: nb {nb}, keep {int(keep[0])}")
+    run_vasc_layers(dev, lay, host, vals, keep, True, 2,
+                    rows_to_check={0, 1, nb // 2, nb - 2, nb - 1}, label=f"wide {nb}")
