@@ -179,12 +179,20 @@ __device__ __forceinline__ bf16x8 v_frag(const unsigned char* vb, int kbase, int
 // wait for the copy before every later LDS read; the tile ring orders it
 // instead (wait_dma() and a barrier before the first read of a slot, a barrier
 // between the last read of a slot and the copy that refills it).
+//
+// The compiler does not resolve hazards for instructions inside inline asm, and
+// on gfx9-family chips a vector-memory instruction needs 5 wait states after a
+// VALU instruction (v_readfirstlane, v_readlane of a spilled SGPR) writes an
+// SGPR it reads, and an LDS-DMA load 1 wait state after a scalar write of M0.
+// Without them it can read the old register: a stale base gives a wrong or
+// unmapped source address. The s_nop 4 inside the asm covers both, whatever
+// the compiler schedules in front of it.
 __device__ __forceinline__ void dma16(const void* sbase, unsigned voff, unsigned lds) {
   const uint64_t b = reinterpret_cast<uint64_t>(sbase);
   const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(bs)),
-               "{m0}"(lds)
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(reinterpret_cast<const void*>(bs)), "{m0}"(lds)
                : "memory");
 }
 
