@@ -28,7 +28,7 @@ STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_
 EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_capacity",
            "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
-           "bsgm_vasc_select_blocks")
+           "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes")
 
 
 class BsgmError(RuntimeError):
@@ -73,7 +73,9 @@ def library() -> ctypes.CDLL:
         lib.bsgm_drift_scores.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                            vp, sz, vp]
-        lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.bsgm_attn_workspace_bytes.argtypes = [lp]
+        lib.bsgm_attn_workspace_bytes.restype = sz
         lib.bsgm_special_rows_workspace_bytes.argtypes = [lp, ctypes.c_int32]
         lib.bsgm_special_rows_workspace_bytes.restype = sz
         lib.bsgm_special_rows_dense_fwd.argtypes = [lp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
@@ -267,9 +269,21 @@ def vasc_select_blocks(layout, keep: Sequence[int], q, k, v, memory, force: bool
     return row_ptr, col_idx, row_stat
 
 
+def attn_workspace_bytes(layout) -> int:
+    """Scratch of the attention forward's fp16 logits (the fp16 copy of K and two
+    int32 flags per (b, h, block)); 0 for fp32 layouts."""
+    L = c_layout(layout)
+    return int(library().bsgm_attn_workspace_bytes(ctypes.byref(L)))
+
+
 def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_lse=False,
-                    stream=None):
-    """Block-sparse attention forward; returns (o, lse or None)."""
+                    workspace="auto", stream=None):
+    """Block-sparse attention forward; returns (o, lse or None).
+
+    workspace: a uint8 tensor of attn_workspace_bytes(layout), "auto" (allocated
+    here), or None (bf16 products for the logits, no fp16 copy of K). With a
+    workspace, rows whose scaled queries or listed key blocks leave the fp16
+    range still take bf16 products."""
     n, nb, rows = _dims(layout)
     shape = (layout.batch, layout.heads, n, layout.head_dim)
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -280,9 +294,14 @@ def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_ls
         o = torch.empty(shape, dtype=_tdtype(layout), device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((layout.batch, layout.heads, n), dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str):
+        nbytes = attn_workspace_bytes(layout)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     L = c_layout(layout)
     _check(library().bsgm_sparse_attn_fwd(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
+                                          _ptr(workspace),
+                                          0 if workspace is None else workspace.numel(),
                                           _stream(stream)))
     return o, lse
 

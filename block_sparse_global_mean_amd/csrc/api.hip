@@ -147,7 +147,7 @@ int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBud
 
 extern "C" {
 
-int32_t bsgm_version(void) { return 10100; }
+int32_t bsgm_version(void) { return 10200; }
 
 const char* bsgm_last_error(void) { return g_err.c_str(); }
 
@@ -362,18 +362,33 @@ int bsgm_vasc_select_blocks(const bsgm_layout* layout, const bsgm_select_params*
   return ok();
 }
 
+size_t bsgm_attn_workspace_bytes(const bsgm_layout* layout) {
+  bsgm::Dims d;
+  if (check_layout(layout, &d) != BSGM_OK) return 0;
+  ok();
+  return layout->dtype == BSGM_BF16 ? bsgm::attn_workspace_bytes(d) : 0;
+}
+
 int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
                          const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
-                         void* stream) {
+                         void* ws, size_t ws_bytes, void* stream) {
   bsgm::Dims d;
   int st = check_layout(layout, &d);
   if (st != BSGM_OK) return st;
   if (!q || !k || !v || !row_ptr || !col_idx || !o)
     return fail(BSGM_E_ARG, "q, k, v, row_ptr, col_idx and o must be non-NULL");
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = layout->dtype == BSGM_BF16
-                     ? bsgm::launch_attn_bf16(d, q, k, v, row_ptr, col_idx, o, lse, s)
-                     : bsgm::launch_attn_f32(d, q, k, v, row_ptr, col_idx, o, lse, s);
+  hipError_t e;
+  if (layout->dtype == BSGM_BF16) {
+    if (ws && ws_bytes < bsgm::attn_workspace_bytes(d))
+      return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes,
+                  bsgm::attn_workspace_bytes(d));
+    if (reinterpret_cast<uintptr_t>(ws) % 256)
+      return fail(BSGM_E_ARG, "workspace must be 256-byte aligned");
+    e = bsgm::launch_attn_bf16(d, q, k, v, row_ptr, col_idx, o, lse, ws, s);
+  } else {
+    e = bsgm::launch_attn_f32(d, q, k, v, row_ptr, col_idx, o, lse, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }

@@ -1,27 +1,37 @@
 // Block-sparse flash-attention forward, bf16 inputs, fp32 accumulation, for
-// gfx950 (CDNA4) with 64-wide waves and bf16 MFMA.
+// gfx950 (CDNA4) with 64-wide waves and matrix cores.
 //
 // Work split: one workgroup per (b, h, query block) with BLK/32 waves; each
 // wave owns 32 query rows. The workgroup walks the CSR list of its row in
-// ascending key-block order; K and V tiles (BLK x 64 bf16) are staged in LDS,
-// double-buffered: right after the barrier that opens a tile, the waves issue
-// direct global->LDS copies of the next tile into the other buffer, which land
-// while the current tile's math runs. The row's column list is kept in an LDS
-// ring, entry x packing the block of tile x + 1 (whose copy tile x issues) with
-// the number of real keys of tile x, so the loop reads one LDS word and no
-// global memory besides the tiles per tile.
+// ascending key-block order; K and V tiles (BLK x 64, 2 bytes per element) are
+// staged in LDS, double-buffered: right after the barrier that opens a tile, the
+// waves issue direct global->LDS copies of the next tile into the other buffer,
+// which land while the current tile's math runs. The row's column list is kept
+// in an LDS ring, entry x packing the block of tile x + 1 (whose copy tile x
+// issues) with the number of real keys of tile x, so the loop reads one LDS word
+// and no global memory besides the tiles per tile.
 //
+// Logits, in one of two forms:
+//  - fp16 (with a workspace): k_k_to_f16 first copies K to fp16, which is exact
+//    for bf16 values inside the fp16 range, and each wave holds its queries as
+//    fp16(q * scale * log2 e) (11 significant bits). The first product then
+//    yields base-2 logits, and its accumulator starts at -m, so
+//    P = exp2(accumulator) takes no per-score arithmetic. A query block whose
+//    scaled Q, or one of whose listed key blocks, leaves the fp16 range is
+//    flagged and left to the bf16 form, which a second launch runs for the
+//    flagged rows only.
+//  - bf16: S = K Q^T on the bf16 inputs, P = exp2(S c - m c), c = scale log2 e.
 // Softmax keeps a reference maximum m per query row instead of a running one:
 // m is the maximum of the row's first tile, and it moves (O and l rescaled)
-// only when a later tile would make some P = exp2((s - m) c) exceed 2^64, which
-// is detected from the tile's row sum (no per-tile maximum). P that large is
-// still far inside the fp32 and bf16 ranges, and the softmax is the same for
-// any reference. The row sum is taken from the bf16-rounded P, the values that
-// enter the second MFMA.
+// only when a later tile would make some P exceed 2^64, which is detected from
+// the tile's row sum (no per-tile maximum). P that large is still far inside
+// the fp32 and bf16 ranges, and the softmax is the same for any reference. The
+// row sum is taken from the bf16-rounded P, the values that enter the second
+// MFMA.
 //
-// Math per key tile, per wave (online softmax, exp2 with the scale folded in):
-//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q in VGPRs
-//   P   = exp2(S*c - m*c)  rounded to bf16 in registers
+// Math per key tile, per wave:
+//   S^T = K Q^T      v_mfma_f32_32x32x16_{f16,bf16}, A = K rows from LDS, B = Q in VGPRs
+//   P   = exp2(...)  rounded to bf16 in registers
 //   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, A = V^T via ds_read_b64_tr_b16, B = P
 // Computing the transposes puts one query per lane pair (lanes l and l^32), so
 // row max/sum need only in-lane work plus one v_permlane32_swap, and P feeds the
@@ -32,9 +42,13 @@
 // LDS tiles are row-major (128 B per key row) with the 16-byte chunk index
 // XOR-swizzled by swz(row), which keeps both the 16-byte K reads and the 8-byte
 // transposing V reads free of bank conflicts within each access phase.
+#include <type_traits>
+
 #include "device_util.h"
 
 namespace bsgm {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 struct AttnArgs {
   Dims d;
@@ -45,9 +59,41 @@ struct AttnArgs {
   const int32_t* col_idx;
   __bf16* o;
   float* lse;
+  const _Float16* kh;   // fp16 form: K in fp16
+  const int32_t* kbad;  // fp16 form: per (b, h, key block), nonzero if its K leaves the fp16 range
+  int32_t* redo;        // per row: the fp16 form writes 1 (left to the bf16 form) or 0;
+                        // the bf16 form, when given it, runs only the rows marked 1
 };
 
+// Largest magnitude taken into fp16 (its largest finite value; larger, infinite
+// or NaN inputs flag their block).
+constexpr float kF16Max = 65504.f;
+
+// fp16 copy of K, one workgroup per (b, h, key block), and the block's range flag.
 template <int BLK>
+__global__ __launch_bounds__(256) void k_k_to_f16(const __bf16* __restrict__ k,
+                                                  _Float16* __restrict__ kh,
+                                                  int32_t* __restrict__ kbad) {
+  constexpr int V8 = BLK * 64 / 8;   // 8-element vectors per block
+  const size_t base = (size_t)blockIdx.x * V8;
+  int out = 0;
+#pragma unroll
+  for (int x = threadIdx.x; x < V8; x += 256) {
+    const bf16x8 v = reinterpret_cast<const bf16x8*>(k)[base + x];
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = (float)v[e];
+      out |= !(fabsf(f) < kF16Max);
+      h[e] = (_Float16)f;
+    }
+    reinterpret_cast<f16x8*>(kh)[base + x] = h;
+  }
+  out = __syncthreads_or(out);
+  if (threadIdx.x == 0) kbad[blockIdx.x] = out != 0;
+}
+
+template <int BLK, bool F16>
 __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   constexpr int NT = BLK * 2;          // threads (BLK/32 waves)
   constexpr int KT = BLK / 32;         // 32-key sub-tiles per key block
@@ -60,63 +106,69 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   const Dims& d = a.d;
   const int r = head_sync_row(blockIdx.x, d.nb);
   if (r < 0) return;
+  if constexpr (!F16) {
+    if (a.redo && a.redo[r] == 0) return;
+  }
   const int bh = r / d.nb, i = r - bh * d.nb;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const size_t hoff = (size_t)bh * d.N * 64;
   const __bf16* Q = a.q + hoff;
-  const __bf16* K = a.k + hoff;
-  const __bf16* V = a.v + hoff;
+  const unsigned char* Kb = F16 ? reinterpret_cast<const unsigned char*>(a.kh + hoff)
+                                : reinterpret_cast<const unsigned char*>(a.k + hoff);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(a.v + hoff);
   const int beg = a.row_ptr[r], end = a.row_ptr[r + 1];
   const int qrow = i * BLK + 32 * w + n;
+  const float c2 = d.scale * 1.4426950408889634f;
 
   // B operand of S^T = K Q^T: column n = query, k-slots 8*hh.. = head dims.
-  bf16x8 qf[4];
+  typedef std::conditional_t<F16, f16x8, bf16x8> qvec;
+  qvec qf[4];
+  int bad = 0;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * 64 + 16 * ks + 8 * hh);
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * 64 + 16 * ks + 8 * hh);
+    if constexpr (F16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)qb[e] * c2;
+        bad |= !(fabsf(f) < kF16Max);
+        qf[ks][e] = (_Float16)f;
+      }
+    } else {
+      qf[ks] = qb;
+    }
+  }
 
   // Key row that A-operand lane row m reads: pi(m) with m = 8a + 4h + j maps to
   // 16(a/2) + 8h + 4(a%2) + j, so accumulator register x of lane l holds key
   // 16(x/8) + 8(l/32) + x%8 of the 32-key sub-tile.
-  const int pim = ((n >> 4) << 4) | (((n >> 2) & 1) << 3) | (((n >> 3) & 1) << 2) | (n & 3);
+  const int pim = key_perm(n);
 
-  int goff[CPT];
-#pragma unroll
-  for (int s2 = 0; s2 < CPT; ++s2) {
-    const int q = NT * s2 + tid;
-    const int row = q >> 3, pc = q & 7;
-    goff[s2] = row * 64 + ((pc ^ swz(row)) << 3);
-  }
-  const int wv = tid >> 6;
   unsigned voff[CPT];
 #pragma unroll
-  for (int s3 = 0; s3 < CPT; ++s3) voff[s3] = (unsigned)goff[s3] * 2u;
-  const unsigned lds0 = (unsigned)(uintptr_t)smem + __builtin_amdgcn_readfirstlane(wv) * 1024;
-#define BSGM_DMA(BUF, J)                                                         \
-  do {                                                                             \
-    const __bf16* kt_ = K + (size_t)(J) * BLK * 64;                                \
-    const __bf16* vt_ = V + (size_t)(J) * BLK * 64;                                \
-    const unsigned kb_ = lds0 + (BUF) * 2 * TB;                                    \
-    _Pragma("unroll") for (int s3 = 0; s3 < CPT; ++s3) {                           \
-      dma16(kt_, voff[s3], kb_ + s3 * NT * 16);                                 \
-      dma16(vt_, voff[s3], kb_ + TB + s3 * NT * 16);                            \
-    }                                                                              \
-  } while (0)
+  for (int s3 = 0; s3 < CPT; ++s3) {
+    const int q = NT * s3 + tid;
+    const int row = q >> 3, pc = q & 7;
+    voff[s3] = (unsigned)(row * 128 + ((pc ^ swz(row)) << 4));
+  }
+  const unsigned lds0 = (unsigned)(uintptr_t)smem + __builtin_amdgcn_readfirstlane(w) * 1024;
+  auto dma = [&](int buf, int j) {
+    const unsigned char* kt = Kb + (size_t)j * TB;
+    const unsigned char* vt = Vb + (size_t)j * TB;
+    const unsigned kb = lds0 + buf * 2 * TB;
+#pragma unroll
+    for (int s3 = 0; s3 < CPT; ++s3) {
+      dma16(kt, voff[s3], kb + s3 * NT * 16);
+      dma16(vt, voff[s3], kb + TB + s3 * NT * 16);
+    }
+  };
 
   // Lane-constant parts of the transposing V read: within each 16-lane group g,
   // lane jj fetches 4 head dims of key row 8*(g/2) + jj/4 (+4 for the upper half).
   const int g16 = lane >> 4, jj = lane & 15;
   const int vrow0 = 8 * (g16 >> 1) + (jj >> 2);
   const int vbyte = 32 * (g16 & 1) + 8 * (jj & 3);
-
-  f32x16 oacc[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int x = 0; x < 16; ++x) oacc[mt][x] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = d.scale * 1.4426950408889634f;
 
   const int nt = end - beg;
   // entry x: the next tile's block (for its copy) and this tile's real-key count
@@ -126,7 +178,40 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
     return (cn << 7) | (block_vlen(d, c) - 1);
   };
   for (int x = tid; x < min(nt, CB); x += NT) colbuf[x] = entry(x);
-  if (nt > 0) BSGM_DMA(0, a.col_idx[beg]);
+
+  if constexpr (F16) {
+    // The fp16 form needs every scaled query of the block and every listed key
+    // block inside the fp16 range; otherwise the row is left to the bf16 form.
+    for (int x = tid; x < nt; x += NT) bad |= a.kbad[(size_t)bh * d.nb + a.col_idx[beg + x]];
+    __shared__ int vote[NT / 64];
+    const bool wave_bad = __ballot(bad) != 0ull;
+    if (lane == 0) vote[w] = wave_bad;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int q = 0; q < NT / 64; ++q) any |= vote[q];
+    any = __builtin_amdgcn_readfirstlane(any);
+    if (tid == 0) a.redo[r] = any != 0;
+    if (any) return;
+  }
+
+  f32x16 oacc[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) oacc[mt][x] = 0.f;
+  // m_run: the reference maximum in the product's units (raw <q,k> for bf16,
+  // base-2 logits for fp16); sc converts them to base-2 units.
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = F16 ? 1.f : c2;
+  f32x16 cinit;   // fp16 form: the start -m of every score accumulator
+#pragma unroll
+  for (int x = 0; x < 16; ++x) cinit[x] = -m_run;
+
+  if (nt > 0) dma(0, a.col_idx[beg]);
+
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
   for (int it = beg; it < end; ++it) {
     const int jt = it - beg;
@@ -136,23 +221,34 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
     if ((jt & (CB / 2 - 1)) == 0 && jt > 0 && jt + CB / 2 < nt)
       for (int x = jt + CB / 2 + tid; x < min(nt, jt + CB); x += NT) colbuf[x & (CB - 1)] = entry(x);
     const int ecur = __builtin_amdgcn_readfirstlane(colbuf[jt & (CB - 1)]);
-    const bool has_next = it + 1 < end;
-    if (has_next) BSGM_DMA(buf ^ 1, ecur >> 7);
+    if (it + 1 < end) dma(buf ^ 1, ecur >> 7);
     const unsigned char* kb = smem + buf * 2 * TB;
     const unsigned char* vb = kb + TB;
-
     const int vlen = (ecur & 127) + 1;
-    auto scores = [&](f32x16 (&s)[KT]) {
+
+    // Scores of the tile; SHIFTED (fp16 form only): accumulators start at -m.
+    auto scores = [&](f32x16 (&s)[KT], auto shifted_tag) {
+      constexpr bool SHIFTED = decltype(shifted_tag)::value;
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) s[t][x] = 0.f;
         const int row = 32 * t + pim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(kb + row * 128 + (((2 * ks + hh) ^ swz(row)) << 4));
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[t], 0, 0, 0);
+          const unsigned char* p = kb + row * 128 + (((2 * ks + hh) ^ swz(row)) << 4);
+          f32x16 c;
+          if (ks == 0) {
+#pragma unroll
+            for (int x = 0; x < 16; ++x) c[x] = 0.f;
+            if constexpr (SHIFTED) c = cinit;
+          } else {
+            c = s[t];
+          }
+          if constexpr (F16)
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(p),
+                                                          qf[ks], c, 0, 0, 0);
+          else
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(p),
+                                                           qf[ks], c, 0, 0, 0);
         }
       }
       if (vlen < BLK) {
@@ -166,13 +262,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
       }
     };
     f32x16 s[KT];
-    scores(s);
+    scores(s, std::integral_constant<bool, F16>{});
 
     bf16x8 pb[KT][2];
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-    auto soft = [&](const f32x16 (&s)[KT]) {
-      const float mb = m_run * c2;
+    // P and its row sum: from shifted scores P = exp2(s), else exp2(s sc - m sc).
+    auto soft = [&](const f32x16 (&s)[KT], auto shifted_tag) {
+      constexpr bool SHIFTED = decltype(shifted_tag)::value;
+      const float mb = m_run * sc;
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
@@ -180,7 +276,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
         for (int e = 0; e < 2; ++e) {
           float pf[8];
 #pragma unroll
-          for (int x = 0; x < 8; ++x) pf[x] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * e + x], c2, -mb));
+          for (int x = 0; x < 8; ++x) {
+            const float z = s[t][8 * e + x];
+            pf[x] = __builtin_amdgcn_exp2f(SHIFTED ? z : (F16 ? z - mb : fmaf(z, sc, -mb)));
+          }
           const bf16x8 pv = {(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3],
                              (__bf16)pf[4], (__bf16)pf[5], (__bf16)pf[6], (__bf16)pf[7]};
           pb[t][e] = pv;
@@ -193,14 +292,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
                                                        false, false);
       return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
     };
-    float psum = soft(s);
+    float psum = soft(s, std::integral_constant<bool, F16>{});
     // The reference m stays while every P of the row is at most 2^64 (far from
     // the fp32 and bf16 range limits). A row whose sum passes that, or is not
     // finite (the first tile, where m is still -inf), moves m to the maximum of
     // this tile's scores, recomputed from the K tile still in LDS.
     if (__ballot(!(psum <= 1.8446744e19f))) {
       const bool big = !(psum <= 1.8446744e19f);
-      scores(s);
+      scores(s, std::false_type{});
       float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
@@ -210,14 +309,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
                                                        false, false);
       mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       const float m_new = big ? fmaxf(m_run, mx) : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sc);
       l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int x = 0; x < 16; ++x) oacc[mt][x] *= alpha;
       m_run = m_new;
-      psum = soft(s);
+      if constexpr (F16) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) cinit[x] = -m_run;
+      }
+      psum = soft(s, std::false_type{});
     }
     l_run += psum;
 
@@ -237,7 +340,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
           oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t][e], oacc[mt], 0, 0, 0);
         }
       }
-
   }
   wait_dma();
 
@@ -255,20 +357,36 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
       for (int x = 0; x < 4; ++x) ov[x] = (__bf16)(oacc[mt][4 * a4 + x] * inv);
       *reinterpret_cast<bf16x4*>(orow + 32 * mt + 8 * a4 + 4 * hh) = ov;
     }
-  if (a.lse && hh == 0)
-    a.lse[(size_t)bh * d.N + qrow] = any ? m_run * d.scale + logf(l_run) : -INFINITY;
+  // natural-log units: m_run * scale (bf16 form) or m_run * ln 2 (base-2 logits)
+  const float mnat = F16 ? m_run * 0.6931471805599453f : m_run * d.scale;
+  if (a.lse && hh == 0) a.lse[(size_t)bh * d.N + qrow] = any ? mnat + logf(l_run) : -INFINITY;
+}
+
+template <int BLK>
+static hipError_t launch_blk(const Dims& d, AttnArgs a, void* ws, hipStream_t s) {
+  const dim3 grid(head_sync_grid(d)), block(BLK * 2);
+  if (ws) {
+    unsigned char* p = static_cast<unsigned char*>(ws);
+    a.kh = reinterpret_cast<const _Float16*>(p);
+    p += align256((size_t)d.B * d.H * d.N * 64 * 2);
+    a.kbad = reinterpret_cast<const int32_t*>(p);
+    p += align256((size_t)d.rows * 4);
+    a.redo = reinterpret_cast<int32_t*>(p);
+    hipLaunchKernelGGL(k_k_to_f16<BLK>, dim3(d.rows), dim3(256), 0, s, a.k,
+                       const_cast<_Float16*>(a.kh), const_cast<int32_t*>(a.kbad));
+    hipLaunchKernelGGL((k_attn_bf16<BLK, true>), grid, block, 0, s, a);
+  }
+  // all rows without a workspace; else only the rows the fp16 form left over
+  hipLaunchKernelGGL((k_attn_bf16<BLK, false>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* row_ptr, const int32_t* col_idx, void* o,
-                            float* lse, hipStream_t s) {
+                            float* lse, void* ws, hipStream_t s) {
   AttnArgs a{d, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-             (__bf16*)o, lse};
-  if (d.blk == 128)
-    hipLaunchKernelGGL(k_attn_bf16<128>, dim3(head_sync_grid(d)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attn_bf16<64>, dim3(head_sync_grid(d)), dim3(128), 0, s, a);
-  return hipGetLastError();
+             (__bf16*)o, lse, nullptr, nullptr, nullptr};
+  return d.blk == 128 ? launch_blk<128>(d, a, ws, s) : launch_blk<64>(d, a, ws, s);
 }
 
 }  // namespace bsgm

@@ -7,6 +7,8 @@
 
 namespace bsgm {
 
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 // Layout as the kernels see it (validated on the host).
 struct Dims {
   int B, H, D;         // batch, heads, head_dim (64)
@@ -75,10 +77,15 @@ hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, i
                                int32_t* row_ptr, int32_t* col_idx, float* row_stat,
                                int32_t* swap_log, hipStream_t s);
 
-// Block-sparse attention forward.
+// Block-sparse attention forward. ws: attn_workspace_bytes(d) bytes of device
+// scratch (enables the fp16 logits: an fp16 copy of K, a range flag per
+// (b, h, key block) and a fallback flag per row), or null (bf16 logits only).
 hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* row_ptr, const int32_t* col_idx, void* o,
-                            float* lse, hipStream_t s);
+                            float* lse, void* ws, hipStream_t s);
+inline size_t attn_workspace_bytes(const Dims& d) {
+  return align256((size_t)d.B * d.H * d.N * 64 * 2) + 2 * align256((size_t)d.rows * 4);
+}
 hipError_t launch_attn_f32(const Dims& d, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, void* o,
                            float* lse, hipStream_t s);
@@ -91,8 +98,6 @@ struct DenseRowsPlan {
 DenseRowsPlan dense_rows_plan(const Dims& d, int ns);
 hipError_t launch_dense_rows(const Dims& d, int ns, const void* q, const void* k, const void* v,
                              void* o, float* lse, void* ws, hipStream_t s);
-
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Largest key-block count the drift selection keeps in LDS.
 constexpr int kDriftMaxBlocks = 512;

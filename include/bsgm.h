@@ -186,10 +186,28 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
  *   row_ptr, col_idx  device CSR as above (strictly ascending indices < Nb)
  *   o         device [B,H,N,D] of layout->dtype (bf16: rounded to nearest even)
  *   lse       device float [B,H,N] or NULL
+ *   ws        device, >= bsgm_attn_workspace_bytes(layout) bytes, or NULL. bf16
+ *             layouts: with ws, K is first copied to fp16 (exact for bf16 values
+ *             inside the fp16 range) and the logits come from fp16 products of
+ *             K and q * scale * log2(e), which takes no per-score arithmetic; a
+ *             query block whose scaled Q, or one of whose listed key blocks,
+ *             leaves the fp16 range takes bf16 products instead, as every block
+ *             does with ws = NULL. The workspace holds only scratch; its contents
+ *             on entry do not matter. fp32 layouts ignore ws.
+ *   ws_bytes  size of ws (ignored when ws is NULL)
+ * Errors: BSGM_E_ARG for a NULL q, k, v, row_ptr, col_idx or o, or a ws not
+ * 256-byte aligned; BSGM_E_WORKSPACE when ws is given with fewer bytes than
+ * needed; BSGM_E_HIP on a launch error.
  */
 int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
-                         const int32_t* row_ptr, const int32_t* col_idx,
-                         void* o, float* lse, void* stream);
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Scratch bytes for bsgm_sparse_attn_fwd's fp16 logits: the fp16 copy of K
+ * (2 * B * H * N * D bytes) and two int32 flags per (b, h, block), each part
+ * rounded up to 256 bytes, for bf16 layouts; 0 for fp32 or an invalid layout
+ * (see bsgm_last_error). */
+size_t bsgm_attn_workspace_bytes(const bsgm_layout* layout);
 
 /* Value-aware block selection with cross-layer pair memory ([VASC] 4.1-4.3,
  * A.1-A.5), one layer: selection from the memory, then the memory update.

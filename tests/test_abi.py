@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = bsgm.library()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert bsgm.version() == 10100
+    assert bsgm.version() == 10200
 
 
 class L:
@@ -67,7 +67,8 @@ def test_bad_layouts_rejected(kw, code):
     lib = bsgm.library()
     c = _lib.c_layout(L(**kw))
     fake = ctypes.c_void_p(16)
-    rc = lib.bsgm_sparse_attn_fwd(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, None)
+    rc = lib.bsgm_sparse_attn_fwd(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, None,
+                                  0, None)
     assert rc == code, lib.bsgm_last_error()
     assert lib.bsgm_last_error().decode() != ""
 
@@ -124,6 +125,22 @@ def test_pool_and_drift_null_arguments():
                                  None) == -1
     assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, None, one, 10, None) == -4
     assert lib.bsgm_pool_blocks(None, one, one, None) == -1
+
+
+def test_attention_workspace():
+    lib = bsgm.library()
+    lay = L()                                  # 2 heads, 4 x 256 tokens
+    c = _lib.c_layout(lay)
+    need = lib.bsgm_attn_workspace_bytes(ctypes.byref(c))
+    # the fp16 copy of K, then a flag per (b, h, key block) and one per row (16 rows)
+    assert need == 2 * 1024 * 64 * 2 + 256 + 256
+    assert bsgm.attn_workspace_bytes(L(dtype="f32")) == 0
+    one = ctypes.c_void_p(16)
+    assert lib.bsgm_sparse_attn_fwd(ctypes.byref(c), one, one, one, one, one, one, None, one,
+                                    need - 1, None) == -4
+    assert lib.bsgm_sparse_attn_fwd(ctypes.byref(c), one, one, one, one, one, one, None, one,
+                                    need, None) == -1          # not 256-byte aligned
+    assert "aligned" in lib.bsgm_last_error().decode()
 
 
 def test_vasc_argument_errors():

@@ -225,11 +225,12 @@ def test_topk_deterministic(dev):
 # --------------------------------------------------------------------------
 # attention on the oracle's CSR
 # --------------------------------------------------------------------------
-def run_attention_case(dev, lay, host_in, vals, rows, label):
-    say(f"attention {label}")
+def run_attention_case(dev, lay, host_in, vals, rows, label, workspace="auto"):
+    """workspace "auto": the scaled-f16 logits (with a workspace), None: bf16."""
+    say(f"attention {label} ({'bf16' if workspace is None else 'f16'} logits)")
     q, k, v = (to_dev(x, dev) for x in host_in)
     rp, ci = upload_csr(rows, dev)
-    o, lse = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True)
+    o, lse = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True, workspace=workspace)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()
@@ -253,16 +254,20 @@ def test_attention_tiny_f32(dev):
     run_attention_case(dev, w.layout, vals, vals, oracle_csr_rows(sets), "tiny f32 top-4")
 
 
-def test_attention_layer8_2heads(dev):
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_attention_layer8_2heads(dev, workspace):
     w, data = preset(1, heads=2)
     vals = (data["q"], data["k"], data["v"])
     sets, _ = oracle.select(*vals, w.layout, oracle.TOPK, data["keep"])
     host = (data["q_bits"], data["k_bits"], data["v_bits"])
-    run_attention_case(dev, w.layout, host, vals, oracle_csr_rows(sets), "8 frames, 2 heads, 50%")
+    run_attention_case(dev, w.layout, host, vals, oracle_csr_rows(sets), "8 frames, 2 heads, 50%",
+                       workspace)
 
 
-@pytest.mark.parametrize("dtype,block", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
-def test_attention_ragged_random_lists(dev, dtype, block):
+@pytest.mark.parametrize("dtype,block,workspace", [("bf16", 64, "auto"), ("bf16", 128, "auto"),
+                                                   ("bf16", 128, None), ("f32", 64, "auto"),
+                                                   ("f32", 128, "auto")])
+def test_attention_ragged_random_lists(dev, dtype, block, workspace):
     """Random kept lists (including empty rows and the partial last block of
     each frame) on a ragged layout with two batch entries."""
     lay = custom_layout(3, 2 * block, 2 * block - 37, block, heads=2, dtype=dtype, batch=2)
@@ -273,7 +278,7 @@ def test_attention_ragged_random_lists(dev, dtype, block):
     for r in range(lay.batch * lay.heads * nb):
         n = int(rng.integers(0, nb + 1)) if r % 7 else 0
         rows.append(sorted(rng.choice(nb, size=n, replace=False).tolist()))
-    run_attention_case(dev, lay, host, vals, rows, f"ragged {dtype} block {block}")
+    run_attention_case(dev, lay, host, vals, rows, f"ragged {dtype} block {block}", workspace)
 
 
 @pytest.mark.parametrize("dtype,block", [("bf16", 64), ("bf16", 128), ("f32", 64)])
@@ -351,8 +356,9 @@ def test_attention_constant_values_and_lse_merge(dev):
     assert float((torch.logaddexp(ls_, ld_)[0, 0, valid] - la_[0, 0, valid]).abs().max()) <= 2e-3
 
 
-@pytest.mark.parametrize("dtype,block", [("bf16", 128), ("bf16", 64)])
-def test_attention_growing_logits(dev, dtype, block):
+@pytest.mark.parametrize("dtype,block,workspace", [("bf16", 128, "auto"), ("bf16", 64, "auto"),
+                                                   ("bf16", 128, None)])
+def test_attention_growing_logits(dev, dtype, block, workspace):
     """Key blocks whose logits grow along the list by up to ~60 (moderate) and
     ~330 (past the rescale bound of a 2^64 softmax weight) in log2 units over
     the first kept block: every row must still match the float64 softmax."""
@@ -378,8 +384,44 @@ def test_attention_growing_logits(dev, dtype, block):
     else:
         host = vals = [q, k, v]
     rows = [list(range(nb)) for _ in range(lay.heads * nb)]
-    o, lse = run_attention_case(dev, lay, host, vals, rows, f"growing logits {dtype} block {block}")
+    o, lse = run_attention_case(dev, lay, host, vals, rows, f"growing logits {dtype} block {block}",
+                                workspace)
     assert np.all(np.isfinite(o))
+
+
+@pytest.mark.parametrize("block", [128, 64])
+def test_attention_outside_fp16_range(dev, block):
+    """Key block 0 of head 1 holds a key beyond the fp16 range and query block 1
+    of head 0 a scaled query beyond it. Rows whose scaled Q or one of whose
+    listed key blocks leaves the range take bf16 products, the rest fp16 ones:
+    the flags in the workspace must route exactly those rows, and every row
+    must match the float64 softmax."""
+    lay = custom_layout(2, 3 * block, 3 * block - 20, block, heads=2, dtype="bf16")
+    rng = np.random.default_rng(7 + block)
+    shape = (1, 2, lay.tokens, 64)
+    q = (rng.standard_normal(shape) * 0.5).astype(np.float32)
+    k = (rng.standard_normal(shape) * 0.5).astype(np.float32)
+    v = rng.standard_normal(shape).astype(np.float32)
+    k[0, 1, 5, 3] = 9.0e4                 # |k| > 65504 in key block 0 of head 1
+    q[0, 0, block + 3, 7] = 4.0e5         # |q * scale * log2 e| > 65504 in query block 1
+    pad = (np.arange(lay.tokens) % lay.frame_len) >= lay.frame_valid
+    for a_ in (q, k, v):
+        a_[:, :, pad] = 0
+    host = [workloads.bf16_bits_from_float(a_) for a_ in (q, k, v)]
+    vals = [workloads.float_from_bf16_bits(b) for b in host]
+    nb = lay.nblocks
+    rows = [list(range(nb)) for _ in range(nb)]                       # head 0: everything
+    rows += [list(range(nb)) if i % 2 == 0 else list(range(1, nb)) for i in range(nb)]
+    want_redo = [int(i == 1) for i in range(nb)] + [int(i % 2 == 0) for i in range(nb)]
+    nbytes = bsgm.attn_workspace_bytes(lay)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev)   # stale contents
+    run_attention_case(dev, lay, host, vals, rows, f"outside the fp16 range block {block}", ws)
+    al = lambda x: (x + 255) // 256 * 256
+    off = al(lay.tokens * lay.heads * 64 * 2)
+    flags = ws.cpu().numpy()[off:].view(np.int32)
+    kbad, redo = flags[:2 * nb], flags[al(2 * nb * 4) // 4:][:2 * nb]
+    assert kbad.tolist() == [0] * nb + [1] + [0] * (nb - 1)
+    assert redo.tolist() == want_redo
 
 
 # --------------------------------------------------------------------------
@@ -492,15 +534,17 @@ def check_sampled_attention(lay, data, o_gpu, rpn, cin, samples, rule):
     assert checked >= len(samples) // 2, f"only {checked} sampled rows had oracle-equal lists"
 
 
-def test_topk_layer32_full_size_sampled(dev):
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_topk_layer32_full_size_sampled(dev, workspace):
     """32 frames, 16 heads, 75 % sparse with forced special blocks: the bench
-    launch (select + attention); sampled rows against the oracle."""
-    say("topk 32 frames full size")
+    launch (select + attention, fp16 logits with a workspace, else bf16);
+    sampled rows against the oracle."""
+    say(f"topk 32 frames full size, attention workspace {workspace}")
     w, data = preset(2)
     lay = w.layout
     q, k, v = inputs(w, data, dev)
     rp, ci, st = bsgm.select_blocks(lay, bsgm.TOPK, data["keep"], q=q, k=k, force=True)
-    o, _ = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci)
+    o, _ = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, workspace=workspace)
     torch.cuda.synchronize()
     rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
     parity.check_csr_wellformed(rpn, cin, lay.nblocks)
