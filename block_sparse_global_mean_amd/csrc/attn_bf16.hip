@@ -262,14 +262,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
       }
     };
     f32x16 s[KT];
-    scores(s, std::integral_constant<bool, F16>{});
 
     bf16x8 pb[KT][2];
     // P and its row sum: from shifted scores P = exp2(s), else exp2(s sc - m sc).
     auto soft = [&](const f32x16 (&s)[KT], auto shifted_tag) {
       constexpr bool SHIFTED = decltype(shifted_tag)::value;
       const float mb = m_run * sc;
-      float psum = 0.f;
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent sum chains
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
@@ -283,20 +282,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
           const bf16x8 pv = {(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3],
                              (__bf16)pf[4], (__bf16)pf[5], (__bf16)pf[6], (__bf16)pf[7]};
           pb[t][e] = pv;
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, psum, false);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, psum, false);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, psum, false);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, psum, false);
+          ps4[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, ps4[0], false);
+          ps4[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, ps4[1], false);
+          ps4[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, ps4[2], false);
+          ps4[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, ps4[3], false);
         }
+      const float psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum),
                                                        false, false);
       return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
     };
-    float psum = soft(s, std::integral_constant<bool, F16>{});
     // The reference m stays while every P of the row is at most 2^64 (far from
-    // the fp32 and bf16 range limits). A row whose sum passes that, or is not
-    // finite (the first tile, where m is still -inf), moves m to the maximum of
-    // this tile's scores, recomputed from the K tile still in LDS.
+    // the fp32 and bf16 range limits). A row whose sum passes that moves m to
+    // the maximum of this tile's scores, recomputed from the K tile still in
+    // LDS. The first tile, which has no reference yet (m = -inf), takes that
+    // path directly.
+    float psum = INFINITY;
+    if (jt > 0) {
+      scores(s, std::integral_constant<bool, F16>{});
+      psum = soft(s, std::integral_constant<bool, F16>{});
+    }
     if (__ballot(!(psum <= 1.8446744e19f))) {
       const bool big = !(psum <= 1.8446744e19f);
       scores(s, std::false_type{});
