@@ -114,6 +114,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _ws(t: Optional[torch.Tensor], name: str = "workspace"):
+    """(pointer, size in bytes) of a caller's workspace tensor, or (None, 0)."""
+    if t is None:
+        return None, 0
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -192,7 +201,7 @@ def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stre
     if zmass is not None:
         _expect(zmass, "zmass", torch.float32, (layout.batch, layout.heads, nb, nb))
     _check(library().bsgm_drift_scores(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), _ptr(contrib),
-                                       _ptr(score), _ptr(zmass), _ptr(workspace), workspace.numel(),
+                                       _ptr(score), _ptr(zmass), *_ws(workspace),
                                        _stream(stream)))
     return contrib, score
 
@@ -228,7 +237,7 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
     _check(library().bsgm_select_blocks(
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
-        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+        *_ws(workspace), _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 
@@ -264,8 +273,8 @@ def vasc_select_blocks(layout, keep: Sequence[int], q, k, v, memory, force: bool
     P, _keep = c_params(VASC, keep, force=force)
     _check(library().bsgm_vasc_select_blocks(
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(v), _ptr(memory), _ptr(row_ptr),
-        _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(demand_out), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+        _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(demand_out), *_ws(workspace),
+        _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 
@@ -284,6 +293,8 @@ def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_ls
     here), or None (bf16 products for the logits, no fp16 copy of K). With a
     workspace, rows whose scaled queries or listed key blocks leave the fp16
     range still take bf16 products."""
+    if isinstance(workspace, str) and workspace != "auto":
+        raise ValueError('workspace must be a tensor, "auto" or None')
     n, nb, rows = _dims(layout)
     shape = (layout.batch, layout.heads, n, layout.head_dim)
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -300,9 +311,7 @@ def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_ls
     L = c_layout(layout)
     _check(library().bsgm_sparse_attn_fwd(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
-                                          _ptr(workspace),
-                                          0 if workspace is None else workspace.numel(),
-                                          _stream(stream)))
+                                          *_ws(workspace), _stream(stream)))
     return o, lse
 
 
@@ -328,5 +337,5 @@ def special_rows_dense_fwd(layout, q, k, v, n_special: int, o, lse=None, workspa
     L = c_layout(layout)
     _check(library().bsgm_special_rows_dense_fwd(
         ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), int(n_special), _ptr(o), _ptr(lse),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+        *_ws(workspace), _stream(stream)))
     return o, lse

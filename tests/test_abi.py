@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_sparse_global_mean_amd as bsgm
 from block_sparse_global_mean_amd import _lib
@@ -185,3 +186,13 @@ def test_special_rows_workspace_and_errors():
     c32 = _lib.c_layout(L(dtype="f32"))
     assert f(ctypes.byref(c32), one, one, one, 5, one, None, one, nbytes, None) == -2
     assert lib.bsgm_last_error().decode() != ""
+
+
+def test_workspace_arguments_validated_in_the_binding():
+    """A workspace must be a contiguous device tensor; its size is taken in bytes."""
+    assert _lib._ws(None) == (None, 0)
+    with pytest.raises(ValueError, match="device tensor"):
+        _lib._ws(torch.empty(16, dtype=torch.uint8))            # host memory
+    q = torch.empty(1)
+    with pytest.raises(ValueError, match="auto"):
+        bsgm.sparse_attn_fwd(L(), q, q, q, q, q, workspace="yes")
