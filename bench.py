@@ -19,7 +19,9 @@ at 50 %, 100 frames with the cumulative-mass rule and per-head caps, 16 frames
 with drift selection and three restoration rounds), each phase timed over
 back-to-back launches; `detail.special_rows_dense` and `detail.vasc_selection`
 time the dense camera/register rows and the value-aware selection with pair
-memory on the bench layer. All are side measurements, not part of `value`.
+memory on the bench layer, and `detail.graph_replay` the same step captured
+once in a HIP graph and replayed. All are side measurements, not part of
+`value`.
 """
 from __future__ import annotations
 
@@ -195,6 +197,7 @@ def main():
     achieved = flops / (attn_avg * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms (select {np.mean(sel_ms):.3f}, attention {attn_avg:.3f})")
 
+    graph = None if args.no_side else graph_step(torch, select, attend, K)
     calibration_copy(torch, dev, args.calib_copy_mib)
 
     traffic = traffic_per_launch()
@@ -207,6 +210,7 @@ def main():
         "executed_gflop": round(flops / 1e9, 3),
         "attn_effective_tflops": round(achieved, 2),
         "device": torch.cuda.get_device_name(0),
+        "graph_replay": graph,
     }
 
     # dense camera/register rows (5 per frame) on the same layer, after the sparse pass
@@ -268,6 +272,35 @@ def main():
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, data, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def graph_step(torch, select, attend, reps: int):
+    """The same step captured once in a HIP graph and replayed `reps` times
+    (side measurement: launch overhead is all it can remove)."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            select()
+            attend()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            select()
+            attend()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return {"step_ms": round(e0.elapsed_time(e1) / reps, 4), "replays": reps}
+    except Exception as exc:   # a side measurement must not cost the bench line
+        return {"error": str(exc)[:200]}
 
 
 def calibration_copy(torch, dev, mib: int):

@@ -136,6 +136,20 @@ def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ..
                          f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
 
 
+def _opt(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape: Tuple[int, ...]):
+    """_expect for an optional tensor."""
+    if t is not None:
+        _expect(t, name, dtype, shape)
+
+
+def _expect_1d(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous 1-D {dtype} tensor, got {t.dtype} "
+                         f"{tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
 def _dims(layout):
     n = layout.frames * layout.frame_len
     nb = n // layout.block
@@ -171,6 +185,7 @@ def pool_blocks(layout, x: torch.Tensor, out: Optional[torch.Tensor] = None, str
     """Block means of x over real tokens -> float32 [B,H,Nb,64]."""
     n, nb, _ = _dims(layout)
     _expect(x, "x", _tdtype(layout), (layout.batch, layout.heads, n, layout.head_dim))
+    _opt(out, "out", torch.float32, (layout.batch, layout.heads, nb, layout.head_dim))
     if out is None:
         out = torch.empty((layout.batch, layout.heads, nb, layout.head_dim), dtype=torch.float32,
                           device=x.device)
@@ -190,6 +205,8 @@ def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stre
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _expect(t, name, _tdtype(layout), shape)
     dev = q.device
+    _opt(contrib, "contrib", torch.float32, (layout.batch, layout.heads, nb, nb, layout.head_dim))
+    _opt(score, "score", torch.float32, (layout.batch, layout.heads, nb, nb))
     if contrib is None:
         contrib = torch.empty((layout.batch, layout.heads, nb, nb, layout.head_dim),
                               dtype=torch.float32, device=dev)
@@ -223,6 +240,17 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
                 (layout.batch, layout.heads, nb, nb, layout.head_dim))
         if zmass is not None:
             _expect(zmass, "zmass", torch.float32, (layout.batch, layout.heads, nb, nb))
+    _opt(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    if col_idx is not None:
+        _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(row_stat, "row_stat", torch.float32, (rows,))
+    _opt(scores_out, "scores_out", torch.float32, (layout.batch, layout.heads, nb, nb))
+    if swap_log is not None:
+        if not isinstance(swap_log, torch.Tensor) or not swap_log.is_cuda or \
+                swap_log.dtype != torch.int32 or not swap_log.is_contiguous() or \
+                swap_log.numel() < rows * swap_rounds * 2:
+            raise ValueError(f"swap_log must be a contiguous int32 device tensor of at least "
+                             f"{rows} x {swap_rounds} x 2 elements")
     cap = col_capacity(layout, mode, keep, force)
     if row_ptr is None:
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
@@ -260,6 +288,10 @@ def vasc_select_blocks(layout, keep: Sequence[int], q, k, v, memory, force: bool
     if demand_out is not None:
         _expect(demand_out, "demand_out", torch.float32, (layout.batch, layout.heads, nb, nb))
     dev = q.device
+    _opt(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    if col_idx is not None:
+        _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(row_stat, "row_stat", torch.float32, (rows,))
     cap = col_capacity(layout, VASC, keep, force)
     if row_ptr is None:
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
@@ -299,8 +331,10 @@ def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_ls
     shape = (layout.batch, layout.heads, n, layout.head_dim)
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _expect(t, name, _tdtype(layout), shape)
-    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32 or row_ptr.numel() != rows + 1:
-        raise ValueError("row_ptr must be int32 [rows+1] and col_idx int32")
+    _expect(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(o, "o", _tdtype(layout), shape)
+    _opt(lse, "lse", torch.float32, (layout.batch, layout.heads, n))
     if o is None:
         o = torch.empty(shape, dtype=_tdtype(layout), device=q.device)
     if lse is None and want_lse:
@@ -331,6 +365,7 @@ def special_rows_dense_fwd(layout, q, k, v, n_special: int, o, lse=None, workspa
     shape = (layout.batch, layout.heads, n, layout.head_dim)
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _expect(t, name, _tdtype(layout), shape)
+    _opt(lse, "lse", torch.float32, (layout.batch, layout.heads, n))
     if workspace is None:
         workspace = torch.empty(special_rows_workspace_bytes(layout, n_special), dtype=torch.uint8,
                                 device=q.device)

@@ -247,6 +247,32 @@ def run_attention_case(dev, lay, host_in, vals, rows, label, workspace="auto"):
     return o, lse
 
 
+def test_binding_rejects_bad_buffers(dev):
+    """Host, mistyped or misshaped buffers are refused before anything is enqueued."""
+    w, data = preset(0)
+    lay = w.layout
+    q, k, v = (torch.from_numpy(data[n]).to(dev) for n in ("q", "k", "v"))
+    nb, rows = lay.nblocks, lay.heads * lay.nblocks
+    rp = torch.zeros(rows + 1, dtype=torch.int32, device=dev)
+    ci = torch.zeros(1, dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError, match="row_ptr"):
+        bsgm.sparse_attn_fwd(lay, q, k, v, rp.cpu(), ci)
+    with pytest.raises(ValueError, match="col_idx"):
+        bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci.to(torch.int64))
+    with pytest.raises(ValueError, match="lse"):
+        bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, lse=torch.empty(3, device=dev))
+    with pytest.raises(ValueError, match="workspace"):
+        bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, workspace=torch.empty(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="scores_out"):
+        bsgm.select_blocks(lay, bsgm.TOPK, data["keep"], q=q, k=k,
+                           scores_out=torch.empty((1, lay.heads, nb, nb), dtype=torch.float64,
+                                                  device=dev))
+    with pytest.raises(ValueError, match="swap_log"):
+        bsgm.select_blocks(lay, bsgm.TOPK, data["keep"], q=q, k=k, swap_rounds=2,
+                           swap_log=torch.empty((rows, 1, 2), dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+
+
 def test_attention_tiny_f32(dev):
     w, data = preset(0)
     vals = (data["q"], data["k"], data["v"])
@@ -561,6 +587,53 @@ def test_topk_layer32_full_size_sampled(dev, workspace):
     check_sampled_attention(lay, data, o, rpn, cin,
                             [(h, i) for h in (0, 5, 15) for i in (0, 1, 11, 200, 351)],
                             lambda h, i, s, p: oracle.select_topk_row(s, 88, forced))
+
+
+def test_hot_path_graph_replay(dev):
+    """Selection and attention captured once in a HIP graph (the library enqueues
+    no memset, allocation or synchronisation) and replayed several times, with
+    eager work that clobbers the outputs between replays: every replay must
+    reproduce the eager results bit for bit."""
+    w, data = preset(1, heads=2)
+    lay = w.layout
+    q, k, v = inputs(w, data, dev)
+    keep = data["keep"]
+    rows = lay.heads * lay.nblocks
+    cap = bsgm.col_capacity(lay, bsgm.TOPK, keep, force=True)
+    rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(cap, dtype=torch.int32, device=dev)
+    sws = torch.empty(bsgm.workspace_bytes(lay, bsgm.TOPK), dtype=torch.uint8, device=dev)
+    aws = torch.empty(bsgm.attn_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, lay.heads, lay.tokens), dtype=torch.float32, device=dev)
+
+    def step():
+        bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=True, row_ptr=rp, col_idx=ci,
+                           workspace=sws, want_stat=False)
+        bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, o=o, lse=lse, workspace=aws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (rp, ci, o, lse)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (rp, ci, o, lse):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((rp, ci, o, lse), ref, ("row_ptr", "col_idx", "o", "lse")):
+            assert torch.equal(got, want), (rep, name)
+    say("graph replay: 3 replays equal to the eager step")
 
 
 def test_topk_layer8_full_size(dev):
