@@ -19,8 +19,9 @@ at 50 %, 100 frames with the cumulative-mass rule and per-head caps, 16 frames
 with drift selection and three restoration rounds), each phase timed over
 back-to-back launches; `detail.special_rows_dense` and `detail.vasc_selection`
 time the dense camera/register rows and the value-aware selection with pair
-memory on the bench layer, and `detail.graph_replay` the same step captured
-once in a HIP graph and replayed. All are side measurements, not part of
+memory on the bench layer, `detail.graph_replay` the same step captured once
+in a HIP graph and replayed, and `detail.cold` one step after a 512 MiB write
+has evicted the caches (median of 3). All are side measurements, not part of
 `value`.
 """
 from __future__ import annotations
@@ -205,13 +206,17 @@ def main():
         "select_ms": round(float(np.mean(sel_ms)), 4),
         "attn_ms": round(attn_avg, 4),
         "attn_ms_min": round(float(np.min(att_ms)), 4),
+        "attn_ms_median": round(float(np.median(att_ms)), 4),
+        "select_ms_median": round(float(np.median(sel_ms)), 4),
         "executed_block_pairs": executed,
         "measured_block_sparsity": round(1.0 - executed / (rows * nb), 6),
         "executed_gflop": round(flops / 1e9, 3),
         "attn_effective_tflops": round(achieved, 2),
-        "device": torch.cuda.get_device_name(0),
+        "device": device_info(torch),
         "graph_replay": graph,
     }
+    if not args.no_side:
+        detail["cold"] = cold_step(torch, dev, select, attend)
 
     # dense camera/register rows (5 per frame) on the same layer, after the sparse pass
     ns = 5
@@ -272,6 +277,35 @@ def main():
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, data, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def device_info(torch):
+    """Name, compute units and architecture of cuda:0 as the runtime reports them."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "compute_units": p.multi_processor_count,
+            "arch": getattr(p, "gcnArchName", "")}
+
+
+def cold_step(torch, dev, select, attend, reps: int = 3):
+    """One step after writing a 512 MiB buffer, which evicts the L2 caches and the
+    256 MB Infinity Cache; the median of `reps` such steps (side measurement)."""
+    flush = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sel, att = [], []
+    for r in range(reps):
+        flush.fill_(float(r))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        select()
+        e[1].record(stream)
+        attend()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        sel.append(e[0].elapsed_time(e[1]))
+        att.append(e[1].elapsed_time(e[2]))
+    del flush
+    return {"select_ms": round(float(np.median(sel)), 4), "attn_ms": round(float(np.median(att)), 4),
+            "flush_mib": 512, "reps": reps}
 
 
 def graph_step(torch, select, attend, reps: int):
