@@ -299,8 +299,9 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
   int32_t* counts = mode == BSGM_SEL_CDF ? reinterpret_cast<int32_t*>(base + w.counts) : nullptr;
   uint32_t* bitmask =
       mode == BSGM_SEL_CDF ? reinterpret_cast<uint32_t*>(base + w.bitmask) : nullptr;
-  hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
-  if (e == hipSuccess) e = bsgm::launch_pool(d, layout->dtype, k, kbar, s);
+  const void* xs[2] = {q, k};
+  float* means[2] = {qbar, kbar};
+  hipError_t e = bsgm::launch_pool_n(d, layout->dtype, 2, xs, means, s);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   e = bsgm::launch_select_pooled(d, hb, mode, params->cdf_tau,
                                  params->force_frame_first_block ? 1 : 0, qbar, kbar, row_ptr,
@@ -347,9 +348,9 @@ int bsgm_vasc_select_blocks(const bsgm_layout* layout, const bsgm_select_params*
   float* pexe = reinterpret_cast<float*>(base + w.pexe);
   const bsgm::VascSel vs{np, fac, mhat, pdem, pexe, demand_out};
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
-  if (e == hipSuccess) e = bsgm::launch_pool(d, layout->dtype, k, kbar, s);
-  if (e == hipSuccess) e = bsgm::launch_pool(d, layout->dtype, v, vbar, s);
+  const void* xs[3] = {q, k, v};
+  float* means[3] = {qbar, kbar, vbar};
+  hipError_t e = bsgm::launch_pool_n(d, layout->dtype, 3, xs, means, s);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   e = bsgm::launch_vasc_prep(d, np, vbar, memory, fac, mhat, s);
   if (e != hipSuccess) return hip_fail(e, "vasc prep launch");

@@ -32,6 +32,9 @@ struct HeadBudget {
 
 // Pooling: mean over real tokens of each block. dtype: 0 f32, 1 bf16.
 hipError_t launch_pool(const Dims& d, int dtype, const void* x, float* mean, hipStream_t s);
+// The same for n <= 3 tensors in one launch.
+hipError_t launch_pool_n(const Dims& d, int dtype, int n, const void* const* xs,
+                        float* const* means, hipStream_t s);
 
 // Value-aware selection state for one layer (mode 3): per (b, h) and pair of
 // key blocks the contrast factor and the memory's ranking copy (inputs), per
