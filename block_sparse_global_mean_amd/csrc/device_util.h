@@ -75,6 +75,32 @@ __device__ __forceinline__ float wave_allmax(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+// All-lane bitwise AND and OR over a wave, the same way. All 64 lanes active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_alland(uint32_t x) {
+  x &= dpp_mov_u<0xB1>(x);
+  x &= dpp_mov_u<0x4E>(x);
+  x &= dpp_mov_u<0x141>(x);
+  x &= dpp_mov_u<0x140>(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = p[0] & p[1];
+  const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return q[0] & q[1];
+}
+__device__ __forceinline__ uint32_t wave_allor(uint32_t x) {
+  x |= dpp_mov_u<0xB1>(x);
+  x |= dpp_mov_u<0x4E>(x);
+  x |= dpp_mov_u<0x141>(x);
+  x |= dpp_mov_u<0x140>(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = p[0] | p[1];
+  const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return q[0] | q[1];
+}
+
 // Block-wide reductions for NT threads (NT / 64 waves). `red` is LDS scratch
 // of at least NT / 64 entries; every thread gets the result. Two barriers.
 template <int NT>

@@ -161,12 +161,33 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
     }
   }
 
+  // Both searches below end on a real key, so a bit on which every real key of
+  // the row agrees is that key's bit: it starts set in T if it is a one and is
+  // never tested. Only the bits that vary (a uniform set) are searched.
+  uint32_t and_hi = ~0u, and_lo = ~0u, or_hi = 0u, or_lo = 0u;
+#pragma unroll
+  for (int p = 0; p < PW; ++p)
+    if (64 * p + lane < d.nb) {
+      and_hi &= (uint32_t)(key[p] >> 32);
+      and_lo &= (uint32_t)key[p];
+      or_hi |= (uint32_t)(key[p] >> 32);
+      or_lo |= (uint32_t)key[p];
+    }
+  and_hi = __builtin_amdgcn_readfirstlane(wave_alland(and_hi));
+  and_lo = __builtin_amdgcn_readfirstlane(wave_alland(and_lo));
+  or_hi = __builtin_amdgcn_readfirstlane(wave_allor(or_hi));
+  or_lo = __builtin_amdgcn_readfirstlane(wave_allor(or_lo));
+  const unsigned long long common1 = ((unsigned long long)and_hi << 32) | and_lo;
+  const unsigned long long vary = common1 ^ (((unsigned long long)or_hi << 32) | or_lo);
+
   const int nforced = a.force ? d.F : 0;
   int k;
   if (a.mode == 1) {
     // largest key threshold T whose keys >= T hold mass >= tau
-    unsigned long long T = 0ull;
-    for (int bit = 63; bit >= 0; --bit) {
+    unsigned long long T = common1;
+    for (unsigned long long rest = vary; rest != 0ull;) {
+      const int bit = 63 - __clzll(rest);
+      rest &= ~(1ull << bit);
       const unsigned long long cand = T | (1ull << bit);
       float m = 0.f;
 #pragma unroll
@@ -184,8 +205,10 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
     k = a.hb.keep[h];
   }
   // k-th largest key (keys are unique)
-  unsigned long long T = 0ull;
-  for (int bit = 63; bit >= 0; --bit) {
+  unsigned long long T = common1;
+  for (unsigned long long rest = vary; rest != 0ull;) {
+    const int bit = 63 - __clzll(rest);
+    rest &= ~(1ull << bit);
     const unsigned long long cand = T | (1ull << bit);
     int c = 0;
 #pragma unroll
