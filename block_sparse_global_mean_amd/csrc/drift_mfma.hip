@@ -108,7 +108,7 @@ __device__ __forceinline__ int tile_key(int t, int x, int lane) {
 }
 
 template <int BLK>
-__global__ __launch_bounds__(256, 2) void k_drift_stats(DriftMfmaArgs a) {
+__global__ __launch_bounds__(256, 4) void k_drift_stats(DriftMfmaArgs a) {
   constexpr int KT = BLK / 32, TB = BLK * 128;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kDriftBlocksPerWg * TB];
   const Dims& d = a.d;
@@ -127,31 +127,36 @@ __global__ __launch_bounds__(256, 2) void k_drift_stats(DriftMfmaArgs a) {
     bf16x8 qh[4], qm[4], ql[4];
     load_qbar(qbar_bh, d.nb, 32 * rt, lane, qh, qm, ql);
     const int vlen = block_vlen(d, j);
-    f32x16 s[KT];
+    // one 32-key sub-tile at a time, merged online: (mx, z) over the real keys
+    const float c2 = d.scale * kLog2e;
+    float mx = -INFINITY, z = 0.f;
 #pragma unroll
-    for (int t = 0; t < KT; ++t) s[t] = qk_tile(smem + jj * TB, t, lane, qh, qm, ql);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (tile_key(t, x, lane) < vlen) mx = fmaxf(mx, s[t][x]);
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-    }
-    const float c2 = d.scale * kLog2e, mb = mx * c2;
-    float z = 0.f;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
+    for (int t = 0; t < KT; ++t) {
+      if (32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
+      const f32x16 s = qk_tile(smem + jj * TB, t, lane, qh, qm, ql);
+      float mt = -INFINITY;
 #pragma unroll
       for (int x = 0; x < 16; ++x)
-        if (tile_key(t, x, lane) < vlen) z += __builtin_amdgcn_exp2f(fmaf(s[t][x], c2, -mb));
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z),
-                                                       false, false);
-      z = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        if (tile_key(t, x, lane) < vlen) mt = fmaxf(mt, s[x]);
+      {
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                         false, false);
+        mt = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+      }
+      const float mb = mt * c2;
+      float zt = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        if (tile_key(t, x, lane) < vlen) zt += __builtin_amdgcn_exp2f(fmaf(s[x], c2, -mb));
+      {
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(zt), __float_as_uint(zt),
+                                                         false, false);
+        zt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      }
+      // every sub-tile before vlen holds a real key, so mt is finite
+      const float mn = fmaxf(mx, mt);
+      z = z * __builtin_amdgcn_exp2f((mx - mn) * c2) + zt * __builtin_amdgcn_exp2f((mt - mn) * c2);
+      mx = mn;
     }
     const int i = 32 * rt + (lane & 31);
     if (lane < 32 && i < d.nb)
