@@ -28,7 +28,8 @@ STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_
 EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_capacity",
            "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
-           "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes")
+           "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes", "bsgm_attn_prepare",
+           "bsgm_sparse_attn_fwd_prepared")
 
 
 class BsgmError(RuntimeError):
@@ -74,6 +75,8 @@ def library() -> ctypes.CDLL:
         lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                            vp, sz, vp]
         lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.bsgm_attn_prepare.argtypes = [lp, vp, vp, sz, vp]
+        lib.bsgm_sparse_attn_fwd_prepared.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.bsgm_attn_workspace_bytes.argtypes = [lp]
         lib.bsgm_attn_workspace_bytes.restype = sz
         lib.bsgm_special_rows_workspace_bytes.argtypes = [lp, ctypes.c_int32]
@@ -317,14 +320,25 @@ def attn_workspace_bytes(layout) -> int:
     return int(library().bsgm_attn_workspace_bytes(ctypes.byref(L)))
 
 
+def attn_prepare(layout, k, workspace, stream=None):
+    """The fp16 copy of K into `workspace` (a uint8 tensor of attn_workspace_bytes),
+    for a later sparse_attn_fwd(..., workspace=workspace, prepared=True)."""
+    n, _, _ = _dims(layout)
+    _expect(k, "k", _tdtype(layout), (layout.batch, layout.heads, n, layout.head_dim))
+    L = c_layout(layout)
+    _check(library().bsgm_attn_prepare(ctypes.byref(L), _ptr(k), *_ws(workspace),
+                                       _stream(stream)))
+
+
 def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_lse=False,
-                    workspace="auto", stream=None):
+                    workspace="auto", stream=None, prepared: bool = False):
     """Block-sparse attention forward; returns (o, lse or None).
 
     workspace: a uint8 tensor of attn_workspace_bytes(layout), "auto" (allocated
     here), or None (bf16 products for the logits, no fp16 copy of K). With a
     workspace, rows whose scaled queries or listed key blocks leave the fp16
-    range still take bf16 products."""
+    range still take bf16 products. prepared: the workspace already holds the
+    fp16 copy of this k (attn_prepare), so the call skips it."""
     if isinstance(workspace, str) and workspace != "auto":
         raise ValueError('workspace must be a tensor, "auto" or None')
     n, nb, rows = _dims(layout)
@@ -343,9 +357,9 @@ def sparse_attn_fwd(layout, q, k, v, row_ptr, col_idx, o=None, lse=None, want_ls
         nbytes = attn_workspace_bytes(layout)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     L = c_layout(layout)
-    _check(library().bsgm_sparse_attn_fwd(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v),
-                                          _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
-                                          *_ws(workspace), _stream(stream)))
+    fn = library().bsgm_sparse_attn_fwd_prepared if prepared else library().bsgm_sparse_attn_fwd
+    _check(fn(ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx), _ptr(o),
+              _ptr(lse), *_ws(workspace), _stream(stream)))
     return o, lse
 
 

@@ -147,7 +147,7 @@ int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBud
 
 extern "C" {
 
-int32_t bsgm_version(void) { return 10200; }
+int32_t bsgm_version(void) { return 10300; }
 
 const char* bsgm_last_error(void) { return g_err.c_str(); }
 
@@ -370,9 +370,25 @@ size_t bsgm_attn_workspace_bytes(const bsgm_layout* layout) {
   return layout->dtype == BSGM_BF16 ? bsgm::attn_workspace_bytes(d) : 0;
 }
 
-int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
-                         const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
-                         void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of an attention workspace (bf16 layouts): size and alignment, and
+// presence when `required`.
+int check_attn_ws(const bsgm::Dims& d, const void* ws, size_t ws_bytes, bool required) {
+  if (!ws) return required ? fail(BSGM_E_ARG, "ws must be non-NULL") : BSGM_OK;
+  if (ws_bytes < bsgm::attn_workspace_bytes(d))
+    return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes,
+                bsgm::attn_workspace_bytes(d));
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(BSGM_E_ARG, "workspace must be 256-byte aligned");
+  return BSGM_OK;
+}
+
+int attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
+             const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse, void* ws,
+             size_t ws_bytes, void* stream, bool k_ready) {
   bsgm::Dims d;
   int st = check_layout(layout, &d);
   if (st != BSGM_OK) return st;
@@ -381,17 +397,44 @@ int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (layout->dtype == BSGM_BF16) {
-    if (ws && ws_bytes < bsgm::attn_workspace_bytes(d))
-      return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes,
-                  bsgm::attn_workspace_bytes(d));
-    if (reinterpret_cast<uintptr_t>(ws) % 256)
-      return fail(BSGM_E_ARG, "workspace must be 256-byte aligned");
-    e = bsgm::launch_attn_bf16(d, q, k, v, row_ptr, col_idx, o, lse, ws, s);
+    st = check_attn_ws(d, ws, ws_bytes, k_ready);
+    if (st != BSGM_OK) return st;
+    e = bsgm::launch_attn_bf16(d, q, k, v, row_ptr, col_idx, o, lse, ws, s, k_ready);
   } else {
     e = bsgm::launch_attn_f32(d, q, k, v, row_ptr, col_idx, o, lse, s);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd(layout, q, k, v, row_ptr, col_idx, o, lse, ws, ws_bytes, stream, false);
+}
+
+int bsgm_attn_prepare(const bsgm_layout* layout, const void* k, void* ws, size_t ws_bytes,
+                      void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  if (!k) return fail(BSGM_E_ARG, "k must be non-NULL");
+  if (layout->dtype != BSGM_BF16) return ok();   // fp32 attention takes no workspace
+  st = check_attn_ws(d, ws, ws_bytes, true);
+  if (st != BSGM_OK) return st;
+  const hipError_t e = bsgm::launch_attn_prepare(d, k, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention prepare launch");
+  return ok();
+}
+
+int bsgm_sparse_attn_fwd_prepared(const bsgm_layout* layout, const void* q, const void* k,
+                                  const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                                  void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd(layout, q, k, v, row_ptr, col_idx, o, lse, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -367,18 +367,47 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   if (a.lse && hh == 0) a.lse[(size_t)bh * d.N + qrow] = any ? mnat + logf(l_run) : -INFINITY;
 }
 
+// Parts of the workspace: the fp16 copy of K, then a range flag per (b, h, key
+// block), then a fallback flag per row (each part 256-byte aligned).
+struct AttnWs {
+  _Float16* kh;
+  int32_t* kbad;
+  int32_t* redo;
+};
+static AttnWs attn_ws(const Dims& d, void* ws) {
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  AttnWs w;
+  w.kh = reinterpret_cast<_Float16*>(p);
+  p += align256((size_t)d.B * d.H * d.N * 64 * 2);
+  w.kbad = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)d.rows * 4);
+  w.redo = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+hipError_t launch_attn_prepare(const Dims& d, const void* k, void* ws, hipStream_t s) {
+  const AttnWs w = attn_ws(d, ws);
+  if (d.blk == 128)
+    hipLaunchKernelGGL(k_k_to_f16<128>, dim3(d.rows), dim3(256), 0, s, (const __bf16*)k, w.kh,
+                       w.kbad);
+  else
+    hipLaunchKernelGGL(k_k_to_f16<64>, dim3(d.rows), dim3(256), 0, s, (const __bf16*)k, w.kh,
+                       w.kbad);
+  return hipGetLastError();
+}
+
 template <int BLK>
-static hipError_t launch_blk(const Dims& d, AttnArgs a, void* ws, hipStream_t s) {
+static hipError_t launch_blk(const Dims& d, AttnArgs a, void* ws, bool k_ready, hipStream_t s) {
   const dim3 grid(head_sync_grid(d)), block(BLK * 2);
   if (ws) {
-    unsigned char* p = static_cast<unsigned char*>(ws);
-    a.kh = reinterpret_cast<const _Float16*>(p);
-    p += align256((size_t)d.B * d.H * d.N * 64 * 2);
-    a.kbad = reinterpret_cast<const int32_t*>(p);
-    p += align256((size_t)d.rows * 4);
-    a.redo = reinterpret_cast<int32_t*>(p);
-    hipLaunchKernelGGL(k_k_to_f16<BLK>, dim3(d.rows), dim3(256), 0, s, a.k,
-                       const_cast<_Float16*>(a.kh), const_cast<int32_t*>(a.kbad));
+    const AttnWs w = attn_ws(d, ws);
+    a.kh = w.kh;
+    a.kbad = w.kbad;
+    a.redo = w.redo;
+    if (!k_ready) {
+      const hipError_t e = launch_attn_prepare(d, a.k, ws, s);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((k_attn_bf16<BLK, true>), grid, block, 0, s, a);
   }
   // all rows without a workspace; else only the rows the fp16 form left over
@@ -388,10 +417,11 @@ static hipError_t launch_blk(const Dims& d, AttnArgs a, void* ws, hipStream_t s)
 
 hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* row_ptr, const int32_t* col_idx, void* o,
-                            float* lse, void* ws, hipStream_t s) {
+                            float* lse, void* ws, hipStream_t s, bool k_ready) {
   AttnArgs a{d, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
              (__bf16*)o, lse, nullptr, nullptr, nullptr};
-  return d.blk == 128 ? launch_blk<128>(d, a, ws, s) : launch_blk<64>(d, a, ws, s);
+  return d.blk == 128 ? launch_blk<128>(d, a, ws, k_ready, s)
+                      : launch_blk<64>(d, a, ws, k_ready, s);
 }
 
 }  // namespace bsgm

@@ -83,9 +83,12 @@ hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, i
 // Block-sparse attention forward. ws: attn_workspace_bytes(d) bytes of device
 // scratch (enables the fp16 logits: an fp16 copy of K, a range flag per
 // (b, h, key block) and a fallback flag per row), or null (bf16 logits only).
+// k_ready: ws already holds the fp16 copy of this k (launch_attn_prepare).
 hipError_t launch_attn_bf16(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* row_ptr, const int32_t* col_idx, void* o,
-                            float* lse, void* ws, hipStream_t s);
+                            float* lse, void* ws, hipStream_t s, bool k_ready = false);
+// The fp16 copy of K and its range flags into ws, on its own.
+hipError_t launch_attn_prepare(const Dims& d, const void* k, void* ws, hipStream_t s);
 inline size_t attn_workspace_bytes(const Dims& d) {
   return align256((size_t)d.B * d.H * d.N * 64 * 2) + 2 * align256((size_t)d.rows * 4);
 }

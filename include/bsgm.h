@@ -203,6 +203,29 @@ int bsgm_sparse_attn_fwd(const bsgm_layout* layout, const void* q, const void* k
                          const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* The fp16 copy of K and its range flags alone, into ws (the first step of
+ * bsgm_sparse_attn_fwd with a workspace). It depends on k only, so a caller can
+ * run it on another stream while the blocks are being selected, then call
+ * bsgm_sparse_attn_fwd_prepared, which skips the copy. fp32 layouts: nothing to
+ * do, returns BSGM_OK.
+ *   k         device [B,H,N,D] bf16
+ *   ws        device, >= bsgm_attn_workspace_bytes(layout) bytes, 256-byte
+ *             aligned (BSGM_E_ARG if NULL or misaligned, BSGM_E_WORKSPACE if
+ *             smaller)
+ */
+int bsgm_attn_prepare(const bsgm_layout* layout, const void* k, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* bsgm_sparse_attn_fwd for a workspace that already holds the fp16 copy of this
+ * k, made by bsgm_attn_prepare on the same layout (bf16 layouts; fp32 layouts
+ * behave as bsgm_sparse_attn_fwd). ws is required. The caller orders the two
+ * calls (an event, or the same stream) and keeps k and ws unchanged between
+ * them; nothing checks that.
+ */
+int bsgm_sparse_attn_fwd_prepared(const bsgm_layout* layout, const void* q, const void* k,
+                                  const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                                  void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Scratch bytes for bsgm_sparse_attn_fwd's fp16 logits: the fp16 copy of K
  * (2 * B * H * N * D bytes) and two int32 flags per (b, h, block), each part
  * rounded up to 256 bytes, for bf16 layouts; 0 for fp32 or an invalid layout

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = bsgm.library()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert bsgm.version() == 10200
+    assert bsgm.version() == 10300
 
 
 class L:
@@ -142,6 +142,14 @@ def test_attention_workspace():
     assert lib.bsgm_sparse_attn_fwd(ctypes.byref(c), one, one, one, one, one, one, None, one,
                                     need, None) == -1          # not 256-byte aligned
     assert "aligned" in lib.bsgm_last_error().decode()
+    # the prepared form needs its workspace; the prepare call too
+    assert lib.bsgm_sparse_attn_fwd_prepared(ctypes.byref(c), one, one, one, one, one, one, None,
+                                             None, 0, None) == -1
+    assert lib.bsgm_attn_prepare(ctypes.byref(c), one, None, 0, None) == -1
+    assert lib.bsgm_attn_prepare(ctypes.byref(c), one, one, need - 1, None) == -4
+    assert lib.bsgm_attn_prepare(ctypes.byref(c), None, one, need, None) == -1
+    f32 = _lib.c_layout(L(dtype="f32"))
+    assert lib.bsgm_attn_prepare(ctypes.byref(f32), one, None, 0, None) == 0   # nothing to do
 
 
 def test_vasc_argument_errors():

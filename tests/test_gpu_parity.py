@@ -636,6 +636,33 @@ def test_hot_path_graph_replay(dev):
     say("graph replay: 3 replays equal to the eager step")
 
 
+@pytest.mark.parametrize("block", [128, 64])
+def test_attention_prepared_on_a_side_stream(dev, block):
+    """The fp16 copy of K made by attn_prepare on another stream, overlapping the
+    selection, then the prepared attention call: bit-identical to the one-call
+    form."""
+    lay = custom_layout(3, 2 * block, 2 * block - 37, block, heads=2, dtype="bf16", batch=2)
+    host, vals = random_inputs(lay, 77 + block)
+    q, k, v = (to_dev(x, dev) for x in host)
+    keep = [max(1, lay.nblocks // 2)] * lay.heads
+    ws1 = torch.empty(bsgm.attn_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty_like(ws1)
+    rp, ci, _ = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=True)
+    o1, l1 = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True, workspace=ws1)
+    torch.cuda.synchronize()
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        bsgm.attn_prepare(lay, k, ws2)
+    rp2, ci2, _ = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=True)
+    main.wait_stream(side)
+    o2, l2 = bsgm.sparse_attn_fwd(lay, q, k, v, rp2, ci2, want_lse=True, workspace=ws2,
+                                  prepared=True)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp2) and torch.equal(ci, ci2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_topk_layer8_full_size(dev):
     say("topk 8 frames full size")
     w, data = preset(1)
