@@ -19,7 +19,9 @@
  *   - Q, K, V, O are device tensors [batch, heads, N, head_dim], row-major,
  *     head_dim contiguous, N = frames * frame_len. Token f*frame_len + p is a
  *     real token iff p < frame_valid; the others are padding and are ignored
- *     by every pool, softmax and drift sum (their contents do not matter).
+ *     by every pool, softmax and drift sum. Their contents must be finite
+ *     (any finite values give the same results; a padding NaN or infinity in
+ *     V reaches the outputs through a zero weight).
  *   - Blocks: block j covers tokens [j*block, (j+1)*block); Nb = N / block.
  *     Query and key blocks share the grid.
  *   - Block lists are CSR: row r = (b*heads + h)*Nb + i, row_ptr int32

@@ -663,6 +663,48 @@ def test_attention_prepared_on_a_side_stream(dev, block):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_padding_contents_are_ignored(dev):
+    """Finite garbage in the padding tokens of Q, K and V (including values past
+    the fp16 range, which route blocks to the bf16 form) changes neither the
+    selection nor any real output, in both attention forms."""
+    lay = custom_layout(3, 256, 200, 128, heads=2, dtype="bf16")
+    host, vals = random_inputs(lay, 91)
+    pad = (np.arange(lay.tokens) % lay.frame_len) >= lay.frame_valid
+    rng = np.random.default_rng(5)
+    dirty = []
+    for x in vals:
+        y = x.copy()
+        y[:, :, pad] = rng.uniform(-9e4, 9e4, size=y[:, :, pad].shape).astype(np.float32)
+        dirty.append(workloads.bf16_bits_from_float(y))
+    keep = [4] * lay.heads          # the 3 forced blocks and one more
+    outs = []
+    aws = torch.empty(bsgm.attn_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+    for h in (host, dirty):
+        q, k, v = (to_dev(x, dev) for x in h)
+        rp, ci, _ = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=True)
+        for ws in (aws, None):
+            o, l = bsgm.sparse_attn_fwd(lay, q, k, v, rp, ci, want_lse=True, workspace=ws)
+            outs.append((rp.clone(), ci.clone(), o.float(), l))
+    torch.cuda.synchronize()
+    # the dirty padding left some rows to the bf16 form (the fallback flags per row)
+    al = lambda x: (x + 255) // 256 * 256
+    rows = lay.heads * lay.nblocks
+    off = al(lay.tokens * lay.heads * 64 * 2) + al(rows * 4)
+    redo = aws.cpu().numpy()[off:off + 4 * rows].view(np.int32)
+    assert redo.sum() > 0
+    rp0, ci0 = outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy()
+    o_ref, lse_ref = oracle.sparse_attention(vals[0], vals[1], vals[2], lay, rp0, ci0)
+    valid = oracle.valid_mask(lay)
+    fin = np.isfinite(lse_ref)
+    for n, (rp, ci, o, l) in enumerate(outs):
+        assert np.array_equal(rp.cpu().numpy(), rp0) and np.array_equal(ci.cpu().numpy(), ci0)
+        o, l = o.cpu().numpy(), l.cpu().numpy()
+        assert np.all(np.isfinite(o)) and np.all(o[..., ~valid, :] == 0)
+        assert_outputs(lay, o, o_ref, valid, f"padding run {n}")
+        assert np.array_equal(np.isfinite(l), fin)
+        assert np.abs(l[fin] - lse_ref[fin]).max() <= 2e-3 * max(1.0, np.abs(lse_ref[fin]).max())
+
+
 def test_topk_layer8_full_size(dev):
     say("topk 8 frames full size")
     w, data = preset(1)
