@@ -236,6 +236,23 @@ def main():
     if not args.no_side:
         detail["cold"] = cold_step(torch, dev, select, attend)
 
+    # the same selection with pooling and selection in one launch, timed alone
+    # beside the two-launch form over back-to-back launches
+    fws = torch.zeros(bsgm.fused_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+    rp1, ci1 = torch.empty_like(row_ptr), torch.empty_like(col_idx)
+
+    def select_fused():
+        bsgm.select_blocks_fused(lay, keep, q, k, force=True, row_ptr=rp1, col_idx=ci1,
+                                 workspace=fws, want_stat=False)
+
+    two_ms = gpu_ms(torch, select, 20)
+    one_ms = gpu_ms(torch, select_fused, 20)
+    select()
+    torch.cuda.synchronize()
+    detail["select_one_launch"] = {
+        "ms": round(one_ms, 4), "two_launch_ms": round(two_ms, 4),
+        "same_csr": bool(torch.equal(rp1, row_ptr) and torch.equal(ci1, col_idx))}
+
     # dense camera/register rows (5 per frame) on the same layer, after the sparse pass
     ns = 5
     sws = torch.empty(bsgm.special_rows_workspace_bytes(lay, ns), dtype=torch.uint8, device=dev)

@@ -29,7 +29,7 @@ EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_
            "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
            "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes", "bsgm_attn_prepare",
-           "bsgm_sparse_attn_fwd_prepared")
+           "bsgm_sparse_attn_fwd_prepared", "bsgm_select_blocks_fused", "bsgm_fused_workspace_bytes")
 
 
 class BsgmError(RuntimeError):
@@ -77,6 +77,10 @@ def library() -> ctypes.CDLL:
         lib.bsgm_sparse_attn_fwd.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.bsgm_attn_prepare.argtypes = [lp, vp, vp, sz, vp]
         lib.bsgm_sparse_attn_fwd_prepared.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.bsgm_select_blocks_fused.argtypes = [lp, pp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
+                                                 sz, vp]
+        lib.bsgm_fused_workspace_bytes.argtypes = [lp]
+        lib.bsgm_fused_workspace_bytes.restype = sz
         lib.bsgm_attn_workspace_bytes.argtypes = [lp]
         lib.bsgm_attn_workspace_bytes.restype = sz
         lib.bsgm_special_rows_workspace_bytes.argtypes = [lp, ctypes.c_int32]
@@ -86,7 +90,8 @@ def library() -> ctypes.CDLL:
                                                 vp, vp, sz, vp]
         for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
                      "bsgm_sparse_attn_fwd", "bsgm_special_rows_dense_fwd",
-                     "bsgm_vasc_select_blocks"):
+                     "bsgm_vasc_select_blocks", "bsgm_select_blocks_fused", "bsgm_attn_prepare",
+                     "bsgm_sparse_attn_fwd_prepared"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -269,6 +274,48 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
         *_ws(workspace), _stream(stream)))
+    return row_ptr, col_idx, row_stat
+
+
+def fused_workspace_bytes(layout) -> int:
+    L = c_layout(layout)
+    n = library().bsgm_fused_workspace_bytes(ctypes.byref(L))
+    if n == 0:
+        raise BsgmError(-1, library().bsgm_last_error().decode())
+    return n
+
+
+def select_blocks_fused(layout, keep: Sequence[int], q, k, force: bool = False,
+                        row_ptr=None, col_idx=None, row_stat=None, scores_out=None,
+                        workspace=None, want_stat: bool = True, stream=None):
+    """TOPK selection with pooling and selection in one launch; same CSR as select_blocks.
+
+    A caller's `workspace` (uint8, >= fused_workspace_bytes) must be zero before its
+    first use; every call leaves it ready for the next. None allocates a zeroed one."""
+    n, nb, rows = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    _expect(q, "q", _tdtype(layout), shape)
+    _expect(k, "k", _tdtype(layout), shape)
+    _opt(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    if col_idx is not None:
+        _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(row_stat, "row_stat", torch.float32, (rows,))
+    _opt(scores_out, "scores_out", torch.float32, (layout.batch, layout.heads, nb, nb))
+    dev = q.device
+    cap = col_capacity(layout, TOPK, keep, force)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_stat is None and want_stat:
+        row_stat = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.zeros(fused_workspace_bytes(layout), dtype=torch.uint8, device=dev)
+    L = c_layout(layout)
+    P, _keep = c_params(TOPK, keep, force=force)
+    _check(library().bsgm_select_blocks_fused(
+        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(row_ptr), _ptr(col_idx),
+        col_idx.numel(), _ptr(row_stat), _ptr(scores_out), *_ws(workspace), _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 

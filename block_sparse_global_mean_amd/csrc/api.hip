@@ -10,6 +10,7 @@
 
 #include "../../include/bsgm.h"
 #include "internal.h"
+#include "pooled.h"
 
 namespace {
 
@@ -84,6 +85,22 @@ struct WsLayout {
 
 int vasc_pairs(const bsgm::Dims& d) { return (d.nb + 1) / 2; }
 
+// Workspace of the one-launch selection: its synchronisation words first (the
+// part that must be zero), then the pooled Q and K.
+struct FusedWs {
+  size_t sync, qbar, kbar, total;
+};
+
+FusedWs fused_ws_layout(const bsgm::Dims& d) {
+  FusedWs w{};
+  const size_t pooled = (size_t)d.rows * 64 * sizeof(float);
+  w.sync = 0;
+  w.qbar = align256(bsgm::fused_sync_words(d) * sizeof(int32_t));
+  w.kbar = w.qbar + align256(pooled);
+  w.total = w.kbar + align256(pooled);
+  return w;
+}
+
 WsLayout ws_layout(const bsgm::Dims& d, int mode) {
   WsLayout w{};
   const size_t pooled = (size_t)d.rows * 64 * sizeof(float);
@@ -147,7 +164,7 @@ int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBud
 
 extern "C" {
 
-int32_t bsgm_version(void) { return 10300; }
+int32_t bsgm_version(void) { return 10400; }
 
 const char* bsgm_last_error(void) { return g_err.c_str(); }
 
@@ -307,6 +324,53 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
                                  params->force_frame_first_block ? 1 : 0, qbar, kbar, row_ptr,
                                  col_idx, row_stat, scores_out, counts, bitmask, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+size_t bsgm_fused_workspace_bytes(const bsgm_layout* layout) {
+  bsgm::Dims d;
+  if (check_layout(layout, &d) != BSGM_OK) return 0;
+  ok();
+  return fused_ws_layout(d).total;
+}
+
+int bsgm_select_blocks_fused(const bsgm_layout* layout, const bsgm_select_params* params,
+                             const void* q, const void* k, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, float* row_stat, float* scores_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  bsgm::HeadBudget hb;
+  st = check_budget(d, params, &hb);
+  if (st != BSGM_OK) return st;
+  if (params->mode != BSGM_SEL_TOPK)
+    return fail(BSGM_E_UNSUPPORTED, "the one-launch selection takes TOPK only (got mode %d)",
+                params->mode);
+  if (!q || !k) return fail(BSGM_E_ARG, "q and k must be non-NULL");
+  if (!row_ptr || !col_idx) return fail(BSGM_E_ARG, "row_ptr and col_idx must be non-NULL");
+  const long long need = (long long)d.B * hb.per_batch;
+  if (need > 0x7FFFFFFFLL)
+    return fail(BSGM_E_UNSUPPORTED, "worst-case nnz %lld does not fit int32 CSR", need);
+  if (col_capacity < need)
+    return fail(BSGM_E_CAPACITY, "col_capacity %lld below worst-case nnz %lld",
+                (long long)col_capacity, need);
+  if (d.nb > bsgm::kSelectMaxBlocks)
+    return fail(BSGM_E_UNSUPPORTED, "pooled selection supports at most %d blocks per row",
+                bsgm::kSelectMaxBlocks);
+  if (!ws) return fail(BSGM_E_ARG, "ws must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(BSGM_E_ARG, "ws must be 256-byte aligned");
+  const FusedWs w = fused_ws_layout(d);
+  if (ws_bytes < w.total)
+    return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  char* base = static_cast<char*>(ws);
+  hipError_t e = bsgm::launch_select_fused(
+      d, hb, layout->dtype, params->force_frame_first_block ? 1 : 0, q, k,
+      reinterpret_cast<float*>(base + w.qbar), reinterpret_cast<float*>(base + w.kbar),
+      reinterpret_cast<int32_t*>(base + w.sync), row_ptr, col_idx, row_stat, scores_out,
+      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused select launch");
   return ok();
 }
 

@@ -13,7 +13,7 @@
 // ballots and masses from cross-lane sums that stay on the VALU.
 #include <type_traits>
 
-#include "device_util.h"
+#include "pooled.h"
 
 namespace bsgm {
 
@@ -45,14 +45,15 @@ struct SelArgs {
 constexpr int kSelRowsPerWg = 4;
 constexpr int kKtStride = 68;   // LDS row stride (floats) of the pooled-K tile
 
+// The rows of workgroup `wg` of (b, h) = bh: query blocks 4 wg .. 4 wg + 3, one
+// per wave. `kt` is 2 x 64 x kKtStride floats of LDS. No barrier follows the
+// point where a wave without a row returns.
 template <int PW, bool VASC>   // key blocks per lane: nb <= 64 * PW; VASC: mode 3
-__global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
-  __shared__ __attribute__((aligned(16))) float kt[2][64 * kKtStride];
+__device__ __forceinline__ void select_rows(const SelArgs& a, int bh, int wg,
+                                            float (*kt)[64 * kKtStride]) {
   const Dims& d = a.d;
-  const int wgs_per_bh = (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
-  const int bh = blockIdx.x / wgs_per_bh;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int i = (blockIdx.x - bh * wgs_per_bh) * kSelRowsPerWg + w;
+  const int i = wg * kSelRowsPerWg + w;
   const bool live = i < d.nb;
   const int h = bh % d.H, b = bh / d.H;
   const int r = bh * d.nb + i;
@@ -267,6 +268,14 @@ __global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
   }
 }
 
+template <int PW, bool VASC>
+__global__ __launch_bounds__(256) void k_select_pooled(SelArgs a) {
+  __shared__ __attribute__((aligned(16))) float kt[2][64 * kKtStride];
+  const int wgs_per_bh = (a.d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
+  const int bh = blockIdx.x / wgs_per_bh;
+  select_rows<PW, VASC>(a, bh, blockIdx.x - bh * wgs_per_bh, kt);
+}
+
 // Exclusive scan of per-row counts into row_ptr (one workgroup of 1024).
 __global__ __launch_bounds__(1024) void k_scan_counts(const int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ row_ptr, int rows) {
@@ -373,6 +382,139 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_emit_bitmask, dim3((d.rows + 3) / 4), dim3(256), 0, s, bitmask, row_ptr,
                      col_idx, d.rows, d.nb);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Pooled top-k selection in one launch: the pooling of Q and K and the
+// selection share one grid. Items: first the pooling items, head-major (item x
+// of (b, h) pools query and key blocks 2x and 2x + 1), then the selection
+// items, head-major (four query blocks each, as k_select_pooled). A workgroup
+// takes one item by an atomic ticket, so tickets follow the order in which
+// workgroups start rather than their index. A selection item waits until every
+// pooling item of its (b, h) has published; those items hold lower tickets,
+// so they were taken by workgroups already running, and a pooling item waits
+// on nothing: every wait ends. While one head selects, later heads still pool.
+//
+// Publication: each pooling thread makes its stores visible device-wide (a
+// device-scope release fence, which writes back the XCD's L2) before the item's
+// count goes up; the selecting workgroup acquires at device scope after its
+// wait. Each counter sits on a 128-byte line of its own.
+// The last workgroup to leave resets the ticket, the exit count and the item
+// counts, so every call finds them zero (the caller zeroes them once).
+// ---------------------------------------------------------------------------
+constexpr int kFusedPoolBlocks = 2;        // query and key blocks per pooling item
+constexpr int kFusedSpinLimit = 1 << 22;   // waits of about 64 clocks each
+
+template <typename T, int PW>
+__global__ __launch_bounds__(256) void k_select_fused(SelArgs a, const T* __restrict__ xq,
+                                                       const T* __restrict__ xk, float* qbar,
+                                                       float* kbar, int32_t* sync) {
+  constexpr size_t kSelLds = 2 * 64 * kKtStride * sizeof(float);
+  constexpr size_t kPoolLds = 2 * kFusedPoolBlocks * PoolGeom<T>::G * 65 * sizeof(float);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kSelLds > kPoolLds ? kSelLds : kPoolLds];
+  __shared__ int s_ticket, s_last;
+  const Dims& d = a.d;
+  const int t = threadIdx.x;
+  const int nbh = d.B * d.H;
+  const int pool_per_bh = (d.nb + kFusedPoolBlocks - 1) / kFusedPoolBlocks;
+  const int sel_per_bh = (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
+  const int npool = nbh * pool_per_bh, total = npool + nbh * sel_per_bh;
+  int32_t* ticket = sync;
+  int32_t* exits = sync + kFusedLine;
+  int32_t* error = sync + 2 * kFusedLine;
+  int32_t* done = sync + 3 * kFusedLine;   // item count of (b, h) = x at done[x * kFusedLine]
+
+  if (t == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int item = s_ticket;
+  if (item < npool) {
+    const int bh = item / pool_per_bh, j0 = (item - bh * pool_per_bh) * kFusedPoolBlocks;
+    PoolUnit<T> u[2 * kFusedPoolBlocks];
+#pragma unroll
+    for (int x = 0; x < kFusedPoolBlocks; ++x) {
+      const int j = j0 + x;
+      const bool real = j < d.nb;
+      const size_t tok = ((size_t)bh * d.N + (size_t)(real ? j : 0) * d.blk) * 64;
+      const size_t row = ((size_t)bh * d.nb + j) * 64;
+      const int vlen = real ? block_vlen(d, j) : 0;
+      u[2 * x] = PoolUnit<T>{xq + tok, real ? qbar + row : nullptr, vlen};
+      u[2 * x + 1] = PoolUnit<T>{xk + tok, real ? kbar + row : nullptr, vlen};
+    }
+    pool_units<T, 2 * kFusedPoolBlocks>(
+        u, reinterpret_cast<float(*)[PoolGeom<T>::G][65]>(lds));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (t == 0)
+      __hip_atomic_fetch_add(&done[bh * kFusedLine], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    const int sel = item - npool, bh = sel / sel_per_bh;
+    if (t == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(&done[bh * kFusedLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             pool_per_bh) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kFusedSpinLimit) {
+          __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    select_rows<PW, false>(a, bh, sel - bh * sel_per_bh,
+                           reinterpret_cast<float(*)[64 * kKtStride]>(lds));
+  }
+  __syncthreads();
+  if (t == 0)
+    s_last = __hip_atomic_fetch_add(exits, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+  __syncthreads();
+  if (s_last) {
+    // every other workgroup's release on the exit count precedes this acquire
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int x = t; x < nbh; x += 256)
+      __hip_atomic_store(&done[x * kFusedLine], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0) {
+      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(exits, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+hipError_t launch_select_fused(const Dims& d, const HeadBudget& hb, int dtype, int force,
+                               const void* q, const void* k, float* qbar, float* kbar,
+                               int32_t* sync, int32_t* row_ptr, int32_t* col_idx,
+                               float* row_stat, float* scores_out, hipStream_t s) {
+  SelArgs a{d, hb, 0, 0.f, force, qbar, kbar, row_ptr, col_idx, row_stat, scores_out,
+            nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const int nbh = d.B * d.H;
+  const long long items =
+      (long long)nbh * ((d.nb + kFusedPoolBlocks - 1) / kFusedPoolBlocks +
+                        (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg);
+  if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)items), block(256);
+  auto go = [&](auto pw) {
+    constexpr int PW = decltype(pw)::value;
+    if (dtype == 1)
+      hipLaunchKernelGGL((k_select_fused<__bf16, PW>), grid, block, 0, s, a,
+                         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), qbar, kbar,
+                         sync);
+    else
+      hipLaunchKernelGGL((k_select_fused<float, PW>), grid, block, 0, s, a,
+                         static_cast<const float*>(q), static_cast<const float*>(k), qbar, kbar,
+                         sync);
+  };
+  const int per = (d.nb + 63) / 64;
+  if (per <= 1) go(std::integral_constant<int, 1>{});
+  else if (per <= 2) go(std::integral_constant<int, 2>{});
+  else if (per <= 4) go(std::integral_constant<int, 4>{});
+  else if (per <= 8) go(std::integral_constant<int, 8>{});
+  else if (per <= 12) go(std::integral_constant<int, 12>{});
+  else if (per <= 16) go(std::integral_constant<int, 16>{});
+  else if (per <= 24) go(std::integral_constant<int, 24>{});
+  else if (per <= 32) go(std::integral_constant<int, 32>{});
+  else if (per <= 48) go(std::integral_constant<int, 48>{});
+  else go(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 

@@ -176,6 +176,40 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
                        float* row_stat, float* scores_out, int32_t* swap_log,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* TOPK selection with the pooling and the selection in one kernel launch
+ * ([ReSS] Table 1: selection overhead with and without a fused kernel). The
+ * result is bitwise that of bsgm_select_blocks in TOPK mode (same pooling and
+ * selection arithmetic); the pooled means stay in the workspace. Inside the
+ * launch the selection of a (batch, head) starts once that head's pooling is
+ * done, while later heads still pool.
+ *   params     mode must be BSGM_SEL_TOPK (BSGM_E_UNSUPPORTED otherwise);
+ *              keep_per_head and force_frame_first_block as bsgm_select_blocks
+ *   q, k, row_ptr, col_idx, col_capacity, row_stat, scores_out
+ *              as bsgm_select_blocks (TOPK)
+ *   ws         device, >= bsgm_fused_workspace_bytes(layout) bytes, 256-byte
+ *              aligned. Its first part holds synchronisation words that must
+ *              be zero before the first call on this workspace (allocate it
+ *              zeroed, or clear it once); every call leaves them zero again, so
+ *              later calls need no clearing. Calls that share a workspace must
+ *              not overlap in time (same stream, or ordered by events).
+ * Errors: BSGM_E_ARG for a NULL q, k, row_ptr, col_idx or ws, or a misaligned
+ * ws; BSGM_E_CAPACITY, BSGM_E_WORKSPACE and BSGM_E_UNSUPPORTED as above;
+ * BSGM_E_HIP on a launch error. The kernel's waits are bounded: a wait that
+ * has polled 2^22 times (on the order of a second) gives up and sets the
+ * word at int32 index 64 of ws to 1; it stays set and the
+ * results are then undefined. By construction every wait ends long before.
+ */
+int bsgm_select_blocks_fused(const bsgm_layout* layout, const bsgm_select_params* params,
+                             const void* q, const void* k, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, float* row_stat, float* scores_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Device workspace bytes of bsgm_select_blocks_fused: 128 * (3 + batch * heads)
+ * bytes of synchronisation words and the pooled Q and K (4 * B * H * Nb * D
+ * bytes each), each part rounded up to 256 bytes; 0 for an invalid layout (see
+ * bsgm_last_error). */
+size_t bsgm_fused_workspace_bytes(const bsgm_layout* layout);
+
 /* Block-sparse attention forward ([VASC] section 3: retained weights are
  * renormalised after dropping connections; [ReSS] Table S6: every selection
  * rule drives the same block grid and sparse kernel). For each real query

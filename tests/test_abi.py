@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = bsgm.library()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert bsgm.version() == 10300
+    assert bsgm.version() == 10400
 
 
 class L:
@@ -108,6 +108,42 @@ def test_select_argument_errors():
     assert _select(lay, rp=None)[0] == -1
     big = L(frames=2, frame_len=128 * 300, frame_valid=128 * 300)
     assert _select(big, mode=2, keep=(5, 5), contrib=16)[0] == -2      # 600 blocks > 512
+
+
+def _fused(lay, mode=0, keep=(2, 2), force=False, cap=None, wsb=None, wsp=256, q=16, k=16,
+           rp=16, ci=16):
+    lib = bsgm.library()
+    c = _lib.c_layout(lay)
+    P, arr = _lib.c_params(mode, keep, 0.9, force)
+    need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
+    cap = need if cap is None else cap
+    wsb = lib.bsgm_fused_workspace_bytes(ctypes.byref(c)) if wsb is None else wsb
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.bsgm_select_blocks_fused(ctypes.byref(c), ctypes.byref(P), v(q), v(k), v(rp), v(ci),
+                                        cap, None, None, v(wsp), wsb, None)
+
+
+def test_fused_select_workspace_and_errors():
+    lay = L(batch=3)                      # 3 x 2 (b, h), 8 blocks each, 48 rows
+    al = lambda x: (x + 255) // 256 * 256
+    assert bsgm.fused_workspace_bytes(lay) == al(128 * (3 + 6)) + 2 * al(48 * 64 * 4)
+    with pytest.raises(bsgm.BsgmError):
+        bsgm.fused_workspace_bytes(L(head_dim=32))
+    assert _fused(lay, mode=bsgm.CDF) == -2
+    assert _fused(lay, mode=bsgm.DRIFT) == -2
+    assert _fused(lay, keep=(0, 2)) == -1
+    assert _fused(lay, keep=(2, 2), force=True) == -1       # 4 forced blocks > 2
+    assert _fused(lay, q=None) == -1
+    assert _fused(lay, k=None) == -1
+    assert _fused(lay, rp=None) == -1
+    assert _fused(lay, ci=None) == -1
+    assert _fused(lay, wsp=None) == -1
+    assert _fused(lay, wsp=272) == -1                       # not 256-byte aligned
+    assert "aligned" in bsgm.library().bsgm_last_error().decode()
+    assert _fused(lay, wsb=1000) == -4
+    assert _fused(lay, cap=3 * 2 * 8 * 2 - 1) == -3
+    big = L(frames=2, frame_len=128 * 2100, frame_valid=128 * 2100)
+    assert _fused(big) == -2                                # 4200 blocks > 4096
 
 
 def test_col_capacity_and_errors():

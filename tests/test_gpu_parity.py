@@ -223,6 +223,133 @@ def test_topk_deterministic(dev):
 
 
 # --------------------------------------------------------------------------
+# pooled top-k selection in one launch
+# --------------------------------------------------------------------------
+def sync_words(lay, ws):
+    """The fused workspace's synchronisation area: ticket, exit count, error flag and
+    one count per (b, h), each on a 128-byte line (the rest of every line unused)."""
+    n = 32 * (3 + lay.batch * lay.heads)
+    return ws[:4 * n].view(torch.int32).cpu().numpy()
+
+
+def fused_vs_two_launch(lay, q, k, keep, force, ws=None, calls=2):
+    """Runs the one-launch selection `calls` times on one workspace and the
+    two-launch selection once; every output must agree bit for bit, and the
+    workspace's synchronisation words must be back at zero after each call."""
+    nb = lay.nblocks
+    ws = torch.zeros(bsgm.fused_workspace_bytes(lay), dtype=torch.uint8, device=q.device) \
+        if ws is None else ws
+    sc2 = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=q.device)
+    ref = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=force, scores_out=sc2)
+    outs = []
+    for c in range(calls):
+        sc1 = torch.full_like(sc2, float("nan"))
+        got = bsgm.select_blocks_fused(lay, keep, q, k, force=force, scores_out=sc1, workspace=ws)
+        torch.cuda.synchronize()
+        assert not sync_words(lay, ws).any(), f"call {c}: synchronisation words not reset"
+        for x, y, name in zip(got + (sc1,), ref + (sc2,), ("row_ptr", "col_idx", "row_stat", "scores")):
+            assert torch.equal(x, y), (c, name)
+        outs.append(got + (sc1,))
+    return outs[-1]
+
+
+@pytest.mark.parametrize("case", ["tiny_f32", "layer8_2heads", "layer32_forced_1head", "ragged_b64_2batch"])
+def test_fused_topk_matches_oracle(dev, case):
+    say(f"fused topk select {case}")
+    force = False
+    if case in ("tiny_f32", "layer8_2heads", "layer32_forced_1head"):
+        idx, heads = {"tiny_f32": (0, None), "layer8_2heads": (1, 2), "layer32_forced_1head": (2, 1)}[case]
+        w, data = preset(idx, heads=heads)
+        lay, dev_in, vals, keep = w.layout, inputs(w, data, dev), (data["q"], data["k"], data["v"]), data["keep"]
+        force = case == "layer32_forced_1head"
+    else:
+        lay = custom_layout(5, 192, 170, 64, heads=3, batch=2)
+        host_in, vals = random_inputs(lay, 3)
+        dev_in = tuple(to_dev(x, dev) for x in host_in)
+        keep = np.array([1, 7, 15], dtype=np.int32)
+    rp, ci, st, sc = fused_vs_two_launch(lay, dev_in[0], dev_in[1], keep, force)
+    mism = check_topk(lay, vals, keep, force, rp.cpu().numpy(), ci.cpu().numpy(),
+                      sc.cpu().numpy(), st.cpu().numpy())
+    say(f"fused topk {case}: rows differing from the oracle by near-ties: {mism}")
+
+
+@pytest.mark.parametrize("nb,keep", [(4095, 700), (999, 64), (702, 9)])
+def test_fused_topk_wide_rows(dev, nb, keep):
+    per = nb // 3
+    lay = custom_layout(3, 64 * per, 64 * per - 30, 64, heads=2)
+    host, vals = random_inputs(lay, 5 + nb)
+    q, k = to_dev(host[0], dev), to_dev(host[1], dev)
+    keeps = np.array([keep, max(1, keep // 2)], dtype=np.int32)
+    say(f"fused topk wide rows: nb {lay.nblocks}, keep {keeps.tolist()}")
+    rp, ci, st, sc = fused_vs_two_launch(lay, q, k, keeps, keep > 3)
+    if nb == 999:
+        check_topk(lay, vals, keeps, True, rp.cpu().numpy(), ci.cpu().numpy(), sc.cpu().numpy(),
+                   st.cpu().numpy())
+
+
+def test_fused_topk_layer32_full_size(dev):
+    """32 frames, 16 heads, forced special blocks, in the bench's launch
+    configuration: one workspace reused over three calls, equal to the
+    two-launch selection; sampled rows are valid top-k sets of the oracle's scores."""
+    say("fused topk 32 frames full size")
+    w, data = preset(2)
+    lay = w.layout
+    q, k, _ = inputs(w, data, dev)
+    rp, ci, st, sc = fused_vs_two_launch(lay, q, k, data["keep"], True, calls=3)
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, lay.nblocks)
+    rows = parity.csr_rows(rpn, cin)
+    forced = oracle.forced_blocks(lay, True)
+    nb = lay.nblocks
+    for h in (0, 9, 15):
+        qbar = oracle.pool(data["q"][:, h:h + 1], lay)[0, 0]
+        kbar = oracle.pool(data["k"][:, h:h + 1], lay)[0, 0]
+        for i in (0, 10, 177, 351):
+            s = lay.scale * (kbar @ qbar[i])
+            assert parity.topk_valid(rows[h * nb + i], s, 88, forced), (h, i)
+
+
+def test_fused_topk_graph_replay(dev):
+    """The one-launch selection captured in a HIP graph and replayed: its
+    synchronisation words reset inside every replay, so each replay reproduces
+    the eager result and leaves them zero."""
+    w, data = preset(1, heads=2)
+    lay = w.layout
+    q, k, _ = inputs(w, data, dev)
+    keep = data["keep"]
+    rows = lay.heads * lay.nblocks
+    cap = bsgm.col_capacity(lay, bsgm.TOPK, keep, force=True)
+    rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(cap, dtype=torch.int32, device=dev)
+    ws = torch.zeros(bsgm.fused_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+
+    def step():
+        bsgm.select_blocks_fused(lay, keep, q, k, force=True, row_ptr=rp, col_idx=ci,
+                                 workspace=ws, want_stat=False)
+
+    ref = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        rp.zero_()
+        ci.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(rp, ref[0]) and torch.equal(ci, ref[1]), rep
+        assert not sync_words(lay, ws).any(), rep
+    say("fused graph replay: 3 replays equal to the two-launch selection")
+
+
+# --------------------------------------------------------------------------
 # attention on the oracle's CSR
 # --------------------------------------------------------------------------
 def run_attention_case(dev, lay, host_in, vals, rows, label, workspace="auto"):
