@@ -11,9 +11,11 @@ bf16, blocks of 128, 75 % block sparsity.
 Prints one JSON line (see the keys below). `value` is the layer-effective
 throughput: algorithmic FLOP of the executed blocks (4 * 128^2 * 64 per
 executed block pair) divided by the measured time of the whole step. The
-attention runs the fp16-logit form: the fp16 copy of K (`attn_prepare`) runs
-on a second stream while the blocks are selected, then the prepared attention
-call runs the attention kernel and the bf16 launch for rows left over (none
+step pools Q and K (`pool_blocks`), then selects from the pooled means
+(`select_blocks_pooled`) while a second stream makes the fp16 copy of K
+(`attn_prepare`), so the copy's HBM stream overlaps the selection kernel
+rather than the pooling. The prepared attention call then runs the
+fp16-logit attention kernel and the bf16 launch for rows left over (none
 here); `roofline.achieved` divides the FLOP by the duration of that call.
 `detail.other_layers` gives the per-layer times of the other presets (8 frames
 at 50 %, 100 frames with the cumulative-mass rule and per-head caps, 16 frames
@@ -167,16 +169,28 @@ def main():
     def attend():
         bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o, workspace=aws)
 
-    # The timed step: the fp16 copy of K depends on K only, so it runs on a
-    # second stream while the blocks are selected; the attention call then
-    # skips it. The side stream first waits for the previous step's attention,
-    # which reads the same workspace.
+    # The timed step: Q and K are pooled, then the fp16 copy of K (which
+    # depends on K only) runs on a second stream while the selection kernel
+    # works from the pooled means; the attention call then skips the copy.
+    # The side stream waits for the pooling (and so for the previous step's
+    # attention, which reads the same workspace): the copy's HBM stream then
+    # overlaps the latency-bound selection instead of the HBM-bound pooling.
     side = torch.cuda.Stream()
+    qbar = torch.empty((lay.batch, lay.heads, nb, lay.head_dim), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
+
+    def pool():
+        bsgm.pool_blocks(lay, q, out=qbar)
+        bsgm.pool_blocks(lay, k, out=kbar)
 
     def prepare_side():
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             bsgm.attn_prepare(lay, k, aws)
+
+    def select_pooled():
+        bsgm.select_blocks_pooled(lay, bsgm.TOPK, keep, qbar, kbar, force=True, row_ptr=row_ptr,
+                                  col_idx=col_idx, want_stat=False)
 
     def attend_prepared():
         stream.wait_stream(side)
@@ -184,8 +198,9 @@ def main():
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
+        pool()
         prepare_side()
-        select()
+        select_pooled()
         attend_prepared()
     torch.cuda.synchronize()
     executed = int(row_ptr[-1].item())
@@ -200,8 +215,9 @@ def main():
     ev_all[0].record(stream)
     for s in range(K):
         ev[s][0].record(stream)
+        pool()
         prepare_side()
-        select()
+        select_pooled()
         ev[s][1].record(stream)
         attend_prepared()
         ev[s][2].record(stream)

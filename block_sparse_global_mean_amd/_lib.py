@@ -29,7 +29,8 @@ EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_
            "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
            "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes", "bsgm_attn_prepare",
-           "bsgm_sparse_attn_fwd_prepared", "bsgm_select_blocks_fused", "bsgm_fused_workspace_bytes")
+           "bsgm_sparse_attn_fwd_prepared", "bsgm_select_blocks_fused", "bsgm_fused_workspace_bytes",
+           "bsgm_select_blocks_pooled")
 
 
 class BsgmError(RuntimeError):
@@ -79,6 +80,8 @@ def library() -> ctypes.CDLL:
         lib.bsgm_sparse_attn_fwd_prepared.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.bsgm_select_blocks_fused.argtypes = [lp, pp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                                  sz, vp]
+        lib.bsgm_select_blocks_pooled.argtypes = [lp, pp, vp, vp, vp, vp, ctypes.c_int64, vp, vp,
+                                                  vp, sz, vp]
         lib.bsgm_fused_workspace_bytes.argtypes = [lp]
         lib.bsgm_fused_workspace_bytes.restype = sz
         lib.bsgm_attn_workspace_bytes.argtypes = [lp]
@@ -90,7 +93,8 @@ def library() -> ctypes.CDLL:
                                                 vp, vp, sz, vp]
         for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
                      "bsgm_sparse_attn_fwd", "bsgm_special_rows_dense_fwd",
-                     "bsgm_vasc_select_blocks", "bsgm_select_blocks_fused", "bsgm_attn_prepare",
+                     "bsgm_vasc_select_blocks", "bsgm_select_blocks_fused", "bsgm_select_blocks_pooled",
+                     "bsgm_attn_prepare",
                      "bsgm_sparse_attn_fwd_prepared"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -274,6 +278,37 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
         *_ws(workspace), _stream(stream)))
+    return row_ptr, col_idx, row_stat
+
+
+def select_blocks_pooled(layout, mode: int, keep: Sequence[int], qbar, kbar, cdf_tau: float = 0.9,
+                         force: bool = False, row_ptr=None, col_idx=None, row_stat=None,
+                         scores_out=None, workspace=None, want_stat: bool = True, stream=None):
+    """TOPK or CDF selection from block means already computed (pool_blocks of Q and K)."""
+    n, nb, rows = _dims(layout)
+    pshape = (layout.batch, layout.heads, nb, layout.head_dim)
+    _expect(qbar, "qbar", torch.float32, pshape)
+    _expect(kbar, "kbar", torch.float32, pshape)
+    _opt(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    if col_idx is not None:
+        _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(row_stat, "row_stat", torch.float32, (rows,))
+    _opt(scores_out, "scores_out", torch.float32, (layout.batch, layout.heads, nb, nb))
+    dev = qbar.device
+    cap = col_capacity(layout, mode, keep, force)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_stat is None and want_stat:
+        row_stat = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None and mode == CDF:
+        workspace = torch.empty(workspace_bytes(layout, CDF), dtype=torch.uint8, device=dev)
+    L = c_layout(layout)
+    P, _keep = c_params(mode, keep, cdf_tau, force)
+    _check(library().bsgm_select_blocks_pooled(
+        ctypes.byref(L), ctypes.byref(P), _ptr(qbar), _ptr(kbar), _ptr(row_ptr), _ptr(col_idx),
+        col_idx.numel(), _ptr(row_stat), _ptr(scores_out), *_ws(workspace), _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 

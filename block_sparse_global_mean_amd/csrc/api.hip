@@ -327,6 +327,51 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
   return ok();
 }
 
+int bsgm_select_blocks_pooled(const bsgm_layout* layout, const bsgm_select_params* params,
+                              const float* qbar, const float* kbar, int32_t* row_ptr,
+                              int32_t* col_idx, int64_t col_capacity, float* row_stat,
+                              float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  bsgm::HeadBudget hb;
+  st = check_budget(d, params, &hb);
+  if (st != BSGM_OK) return st;
+  const int mode = params->mode;
+  if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF)
+    return fail(BSGM_E_UNSUPPORTED, "selection from pooled means takes TOPK or CDF (got mode %d)",
+                mode);
+  if (!qbar || !kbar) return fail(BSGM_E_ARG, "qbar and kbar must be non-NULL");
+  if (!row_ptr || !col_idx) return fail(BSGM_E_ARG, "row_ptr and col_idx must be non-NULL");
+  const long long need = (long long)d.B * hb.per_batch;
+  if (need > 0x7FFFFFFFLL)
+    return fail(BSGM_E_UNSUPPORTED, "worst-case nnz %lld does not fit int32 CSR", need);
+  if (col_capacity < need)
+    return fail(BSGM_E_CAPACITY, "col_capacity %lld below worst-case nnz %lld",
+                (long long)col_capacity, need);
+  if (mode == BSGM_SEL_CDF && !(params->cdf_tau > 0.f && params->cdf_tau <= 1.f))
+    return fail(BSGM_E_ARG, "cdf_tau must be in (0, 1]");
+  if (d.nb > bsgm::kSelectMaxBlocks)
+    return fail(BSGM_E_UNSUPPORTED, "pooled selection supports at most %d blocks per row",
+                bsgm::kSelectMaxBlocks);
+  int32_t* counts = nullptr;
+  uint32_t* bitmask = nullptr;
+  if (mode == BSGM_SEL_CDF) {
+    if (!ws) return fail(BSGM_E_ARG, "CDF needs ws");
+    const WsLayout w = ws_layout(d, mode);
+    if (ws_bytes < w.total)
+      return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+    counts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.counts);
+    bitmask = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + w.bitmask);
+  }
+  hipError_t e = bsgm::launch_select_pooled(d, hb, mode, params->cdf_tau,
+                                            params->force_frame_first_block ? 1 : 0, qbar, kbar,
+                                            row_ptr, col_idx, row_stat, scores_out, counts, bitmask,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
 size_t bsgm_fused_workspace_bytes(const bsgm_layout* layout) {
   bsgm::Dims d;
   if (check_layout(layout, &d) != BSGM_OK) return 0;

@@ -176,6 +176,29 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
                        float* row_stat, float* scores_out, int32_t* swap_log,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* TOPK or CDF selection from pooled means the caller already holds (from
+ * bsgm_pool_blocks of Q and of K): the second half of bsgm_select_blocks, with
+ * the same results bit for bit when given the same means. A caller can thus
+ * order other work between the pooling and the selection, for instance the
+ * fp16 copy of K for the attention (bsgm_attn_prepare), which then overlaps
+ * the selection instead of the pooling.
+ *   params     mode BSGM_SEL_TOPK or BSGM_SEL_CDF (BSGM_E_UNSUPPORTED
+ *              otherwise); the other fields as bsgm_select_blocks
+ *   qbar, kbar device float [B,H,Nb,D], the block means of Q and K
+ *   row_ptr, col_idx, col_capacity, row_stat, scores_out
+ *              as bsgm_select_blocks
+ *   ws         CDF: device, >= bsgm_workspace_bytes(layout, BSGM_SEL_CDF)
+ *              bytes (its pooled-mean part is not used); TOPK: not used, may
+ *              be NULL
+ * Errors: BSGM_E_ARG for a NULL qbar, kbar, row_ptr or col_idx (or ws in CDF
+ * mode) or a bad budget or cdf_tau; BSGM_E_CAPACITY, BSGM_E_WORKSPACE,
+ * BSGM_E_UNSUPPORTED as bsgm_select_blocks; BSGM_E_HIP on a launch error.
+ */
+int bsgm_select_blocks_pooled(const bsgm_layout* layout, const bsgm_select_params* params,
+                              const float* qbar, const float* kbar, int32_t* row_ptr,
+                              int32_t* col_idx, int64_t col_capacity, float* row_stat,
+                              float* scores_out, void* ws, size_t ws_bytes, void* stream);
+
 /* TOPK selection with the pooling and the selection in one kernel launch
  * ([ReSS] Table 1: selection overhead with and without a fused kernel). The
  * result is bitwise that of bsgm_select_blocks in TOPK mode (same pooling and

@@ -146,6 +146,34 @@ def test_fused_select_workspace_and_errors():
     assert _fused(big) == -2                                # 4200 blocks > 4096
 
 
+def test_select_from_pooled_means_errors():
+    lay = L(batch=3)
+    lib = bsgm.library()
+    c = _lib.c_layout(lay)
+
+    def call(mode=0, keep=(2, 2), tau=0.9, qb=16, kb=16, rp=16, ci=16, cap=None, ws=256, wsb=None):
+        P, arr = _lib.c_params(mode, keep, tau, False)
+        need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
+        cap = need if cap is None else cap
+        wsb = ws_(lay, mode) if wsb is None else wsb
+        v = lambda x: None if x is None else ctypes.c_void_p(x)
+        return lib.bsgm_select_blocks_pooled(ctypes.byref(c), ctypes.byref(P), v(qb), v(kb), v(rp),
+                                             v(ci), cap, None, None, v(ws), wsb, None)
+
+    ws_ = lambda lay, mode: ws(lay, mode if mode in (0, 1) else 0)
+    assert call(mode=bsgm.DRIFT) == -2
+    assert call(mode=bsgm.VASC) == -2
+    assert call(qb=None) == -1
+    assert call(kb=None) == -1
+    assert call(rp=None) == -1
+    assert call(ci=None) == -1
+    assert call(keep=(0, 2)) == -1
+    assert call(cap=3 * 8 * 4 - 1) == -3
+    assert call(mode=bsgm.CDF, tau=0.0) == -1
+    assert call(mode=bsgm.CDF, ws=None) == -1
+    assert call(mode=bsgm.CDF, wsb=10) == -4
+
+
 def test_col_capacity_and_errors():
     lay = L(batch=3)
     assert bsgm.col_capacity(lay, bsgm.TOPK, [2, 5]) == 3 * 8 * 7

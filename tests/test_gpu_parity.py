@@ -222,6 +222,39 @@ def test_topk_deterministic(dev):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("mode", [bsgm.TOPK, bsgm.CDF])
+@pytest.mark.parametrize("case", ["layer8_2heads", "ragged_b64_2batch", "layer32_forced"])
+def test_select_from_pooled_means(dev, mode, case):
+    """Selection from means pooled by separate pool_blocks calls equals the
+    pool-and-select call bit for bit (CSR, statistic and scores)."""
+    say(f"select from pooled means {case} mode {mode}")
+    force = False
+    if case == "layer8_2heads":
+        w, data = preset(1, heads=2)
+        lay, (q, k, _), keep = w.layout, inputs(w, data, dev), data["keep"]
+    elif case == "layer32_forced":
+        w, data = preset(2)
+        lay, (q, k, _), keep = w.layout, inputs(w, data, dev), data["keep"]
+        force = True
+    else:
+        lay = custom_layout(5, 192, 170, 64, heads=3, batch=2)
+        host_in, _ = random_inputs(lay, 3)
+        q, k = to_dev(host_in[0], dev), to_dev(host_in[1], dev)
+        keep = np.array([1, 7, 15], dtype=np.int32)
+    nb = lay.nblocks
+    sc1 = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    sc2 = torch.full_like(sc1, float("nan"))
+    ref = bsgm.select_blocks(lay, mode, keep, q=q, k=k, force=force, cdf_tau=0.9, scores_out=sc1)
+    qbar, kbar = bsgm.pool_blocks(lay, q), bsgm.pool_blocks(lay, k)
+    got = bsgm.select_blocks_pooled(lay, mode, keep, qbar, kbar, cdf_tau=0.9, force=force,
+                                    scores_out=sc2)
+    torch.cuda.synchronize()
+    nnz = int(ref[0][-1].item())
+    assert torch.equal(got[0], ref[0])
+    assert torch.equal(got[1][:nnz], ref[1][:nnz])
+    assert torch.equal(got[2], ref[2]) and torch.equal(sc2, sc1)
+
+
 # --------------------------------------------------------------------------
 # pooled top-k selection in one launch
 # --------------------------------------------------------------------------
