@@ -22,8 +22,8 @@ at 50 %, 100 frames with the cumulative-mass rule and per-head caps, 16 frames
 with drift selection and three restoration rounds), each phase timed over
 back-to-back launches; `detail.special_rows_dense` and `detail.vasc_selection`
 time the dense camera/register rows and the value-aware selection with pair
-memory on the bench layer, `detail.graph_replay` the same step captured once
-in a HIP graph and replayed, and `detail.cold` one step after a 512 MiB write
+memory on the bench layer, `detail.graph_replay` the same step (both
+streams) captured once in a HIP graph and replayed, and `detail.cold` one step after a 512 MiB write
 has evicted the caches (median of 3). All are side measurements, not part of
 `value`.
 """
@@ -184,7 +184,7 @@ def main():
         bsgm.pool_blocks(lay, k, out=kbar)
 
     def prepare_side():
-        side.wait_stream(stream)
+        side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             bsgm.attn_prepare(lay, k, aws)
 
@@ -193,7 +193,7 @@ def main():
                                   col_idx=col_idx, want_stat=False)
 
     def attend_prepared():
-        stream.wait_stream(side)
+        torch.cuda.current_stream().wait_stream(side)
         bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o, workspace=aws, prepared=True)
 
     log(f"warmup {args.warmup}")
@@ -232,7 +232,13 @@ def main():
     achieved = flops / (attn_avg * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms (select {np.mean(sel_ms):.3f}, attention {attn_avg:.3f})")
 
-    graph = None if args.no_side else graph_step(torch, select, attend, K)
+    def step():
+        pool()
+        prepare_side()
+        select_pooled()
+        attend_prepared()
+
+    graph = None if args.no_side else graph_step(torch, step, K)
     calibration_copy(torch, dev, args.calib_copy_mib)
 
     traffic = traffic_per_launch()
@@ -359,21 +365,20 @@ def cold_step(torch, dev, select, attend, reps: int = 3):
             "flush_mib": 512, "reps": reps}
 
 
-def graph_step(torch, select, attend, reps: int):
-    """The same step captured once in a HIP graph and replayed `reps` times
-    (side measurement: launch overhead is all it can remove)."""
+def graph_step(torch, step, reps: int):
+    """The same step, both streams included, captured once in a HIP graph and
+    replayed `reps` times (side measurement: launch overhead is all it can
+    remove)."""
     try:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            select()
-            attend()
-        torch.cuda.current_stream().wait_stream(side)
+        warm = torch.cuda.Stream()
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):
+            step()
+        torch.cuda.current_stream().wait_stream(warm)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            select()
-            attend()
+            step()
         g.replay()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
