@@ -252,13 +252,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
         }
       }
       if (vlen < BLK) {
+        // the real keys are a prefix: sub-tiles past it are masked whole, and
+        // only the one that straddles its end compares key by key
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+        for (int t = 0; t < KT; ++t) {
+          if (32 * t >= vlen) {
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int key = 32 * t + 16 * (x >> 3) + 8 * hh + (x & 7);
-            if (key >= vlen) s[t][x] = -INFINITY;
+            for (int x = 0; x < 16; ++x) s[t][x] = -INFINITY;
+          } else if (32 * t + 32 > vlen) {
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+              const int key = 32 * t + 16 * (x >> 3) + 8 * hh + (x & 7);
+              if (key >= vlen) s[t][x] = -INFINITY;
+            }
           }
+        }
       }
     };
     f32x16 s[KT];
