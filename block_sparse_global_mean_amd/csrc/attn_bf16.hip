@@ -12,14 +12,21 @@
 // and no global memory besides the tiles per tile.
 //
 // Logits, in one of two forms:
-//  - fp16 (with a workspace): k_k_to_f16 first copies K to fp16, which is exact
-//    for bf16 values inside the fp16 range, and each wave holds its queries as
-//    fp16(q * scale * log2 e) (11 significant bits). The first product then
+//  - fp16 (with a workspace): k_k_to_f16 first copies K to fp16, and each wave
+//    holds its queries as fp16(q * scale * log2 e). The first product then
 //    yields base-2 logits, and its accumulator starts at -m, so
-//    P = exp2(accumulator) takes no per-score arithmetic. A query block whose
-//    scaled Q, or one of whose listed key blocks, leaves the fp16 range is
-//    flagged and left to the bf16 form, which a second launch runs for the
-//    flagged rows only.
+//    P = exp2(accumulator) takes no per-score arithmetic. The fp16 copy of a
+//    bf16 value x is exact for |x| >= 2^-17 (fp16 keeps 11 significant bits
+//    down to 2^-14 and steps of 2^-24 below); smaller values move by at most
+//    2^-25. The scaled query keeps 11 significant bits (relative error 2^-12)
+//    above 2^-14 and an absolute error of at most 2^-25 below. The form is
+//    used only where every |k| of the listed key blocks and every
+//    |q * scale * log2 e| of the query block is below 2^7, so that the two
+//    absolute terms add at most 64 * 2^7 * 2^-25 = 2^-12 each to a base-2
+//    logit: its error is at most 2^-12 * sum_d |q_d c k_d| + 2^-11, plus the
+//    fp32 accumulation. A query block outside that range, or one of whose
+//    listed key blocks is, is flagged and left to the bf16 form, which a
+//    second launch runs for the flagged rows only.
 //  - bf16: S = K Q^T on the bf16 inputs, P = exp2(S c - m c), c = scale log2 e.
 // Softmax keeps a reference maximum m per query row instead of a running one:
 // m is the maximum of the row's first tile, and it moves (O and l rescaled)
@@ -60,14 +67,15 @@ struct AttnArgs {
   __bf16* o;
   float* lse;
   const _Float16* kh;   // fp16 form: K in fp16
-  const int32_t* kbad;  // fp16 form: per (b, h, key block), nonzero if its K leaves the fp16 range
+  const int32_t* kbad;  // fp16 form: per (b, h, key block), nonzero if some |k| >= kF16FormMax
   int32_t* redo;        // per row: the fp16 form writes 1 (left to the bf16 form) or 0;
                         // the bf16 form, when given it, runs only the rows marked 1
 };
 
-// Largest magnitude taken into fp16 (its largest finite value; larger, infinite
-// or NaN inputs flag their block).
-constexpr float kF16Max = 65504.f;
+// Magnitude bound of K and of q * scale * log2 e in the fp16 form (larger,
+// infinite or NaN values flag their block). It caps what the fp16 rounding
+// below 2^-14 (absolute, at most 2^-25 per element) can add to a logit.
+constexpr float kF16FormMax = 128.f;
 
 // fp16 copy of K, one workgroup per (b, h, key block), and the block's range flag.
 template <int BLK>
@@ -84,7 +92,7 @@ __global__ __launch_bounds__(256) void k_k_to_f16(const __bf16* __restrict__ k,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float f = (float)v[e];
-      out |= !(fabsf(f) < kF16Max);
+      out |= !(fabsf(f) < kF16FormMax);
       h[e] = (_Float16)f;
     }
     reinterpret_cast<f16x8*>(kh)[base + x] = h;
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float f = (float)qb[e] * c2;
-        bad |= !(fabsf(f) < kF16Max);
+        bad |= !(fabsf(f) < kF16FormMax);
         qf[ks][e] = (_Float16)f;
       }
     } else {
@@ -180,8 +188,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_attn_bf16(AttnArgs a) {
   for (int x = tid; x < min(nt, CB); x += NT) colbuf[x] = entry(x);
 
   if constexpr (F16) {
-    // The fp16 form needs every scaled query of the block and every listed key
-    // block inside the fp16 range; otherwise the row is left to the bf16 form.
+    // The fp16 form needs every scaled query of the block and every value of
+    // every listed key block below kF16FormMax in magnitude; otherwise the row
+    // is left to the bf16 form.
     for (int x = tid; x < nt; x += NT) bad |= a.kbad[(size_t)bh * d.nb + a.col_idx[beg + x]];
     __shared__ int vote[NT / 64];
     const bool wave_bad = __ballot(bad) != 0ull;

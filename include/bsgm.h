@@ -246,13 +246,18 @@ size_t bsgm_fused_workspace_bytes(const bsgm_layout* layout);
  *   o         device [B,H,N,D] of layout->dtype (bf16: rounded to nearest even)
  *   lse       device float [B,H,N] or NULL
  *   ws        device, >= bsgm_attn_workspace_bytes(layout) bytes, or NULL. bf16
- *             layouts: with ws, K is first copied to fp16 (exact for bf16 values
- *             inside the fp16 range) and the logits come from fp16 products of
- *             K and q * scale * log2(e), which takes no per-score arithmetic; a
- *             query block whose scaled Q, or one of whose listed key blocks,
- *             leaves the fp16 range takes bf16 products instead, as every block
- *             does with ws = NULL. The workspace holds only scratch; its contents
- *             on entry do not matter. fp32 layouts ignore ws.
+ *             layouts: with ws, K is first copied to fp16 and the logits come
+ *             from fp16 products of K and q * scale * log2(e) (c below), which
+ *             takes no per-score arithmetic. That copy of K is exact for
+ *             |k| >= 2^-17 and within 2^-25 below; the scaled query keeps 11
+ *             significant bits above 2^-14 and is within 2^-25 below. The fp16
+ *             products are used for a query block only when every |q c| of the
+ *             block and every |k| of its listed key blocks is below 128; its
+ *             base-2 logits are then within 2^-12 * sum_d |q_d c k_d| + 2^-11 of
+ *             exact, plus fp32 accumulation. Every other query block takes bf16
+ *             products (exact products, fp32 accumulation), as every block does
+ *             with ws = NULL. The workspace holds only scratch; its contents on
+ *             entry do not matter. fp32 layouts ignore ws.
  *   ws_bytes  size of ws (ignored when ws is NULL)
  * Errors: BSGM_E_ARG for a NULL q, k, v, row_ptr, col_idx or o, or a ws not
  * 256-byte aligned; BSGM_E_WORKSPACE when ws is given with fewer bytes than
