@@ -26,6 +26,20 @@ memory on the bench layer, `detail.graph_replay` the same step (both
 streams) captured once in a HIP graph and replayed, and `detail.cold` one step after a 512 MiB write
 has evicted the caches (median of 3). All are side measurements, not part of
 `value`.
+
+Per preset (`detail.other_layers`, the bench layer included, and the tiny
+fp32 layer), `selection_phases` times pooling, selection from the means and
+the whole selection call (or drift scores and drift selection) both back to
+back ("cache_warm_gbs": the inputs may still sit in the L2 and Infinity
+caches) and after a 512 MiB write ("cold_hbm_gbs", the figure that speaks for
+HBM), each against its algorithmic bytes (real-token inputs read once, outputs
+written once); `workspace_mib` gives the device scratch of each call.
+`detail.attn_prepare_ms` is the fp16 copy of K alone (it runs beside the
+selection in the step), `attn_with_prepare_frac` the attention's roofline
+fraction with that time charged too, and `attn_rows_bf16_form` the rows the
+fp16-logit form handed to the bf16 form. `cpu_baseline` times the oracle on
+the host in float64 (`value`) and float32, BLAS threads pinned to the cores in
+this process's affinity mask.
 """
 from __future__ import annotations
 
@@ -78,16 +92,26 @@ def to_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def cpu_baseline(w, data, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the same layer: head by
-    head, pooled scores and top-k selection, then block-sparse attention per
-    query block, until about `budget_s` seconds have passed."""
-    import oracle
+def cpu_info():
+    """(model name, number of cores this process may run on) of the host."""
+    model = ""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    return model, cores
+
+
+def oracle_sample(w, data, budget_s: float, dtype):
+    """The oracle, as it stands, on a bounded sample of the bench layer in the
+    given float type: head by head, pooled scores and top-k selection, then
+    block-sparse attention per query block, until about `budget_s` seconds."""
+    import oracle
     lay = w.layout
     keep = data["keep"]
     forced = oracle.forced_blocks(lay, w.force_frame_first_block)
@@ -95,12 +119,12 @@ def cpu_baseline(w, data, budget_s: float):
     pairs = rows = heads = 0
     for h in range(lay.heads):
         q, k, v = data["q"][:, h:h + 1], data["k"][:, h:h + 1], data["v"][:, h:h + 1]
-        qbar, kbar = oracle.pool(q, lay), oracle.pool(k, lay)
+        qbar, kbar = oracle.pool(q, lay, dtype), oracle.pool(k, lay, dtype)
         s = oracle.pooled_scores(qbar, kbar, lay.scale)[0, 0]
         heads += 1
         for i in range(lay.nblocks):
             kept = oracle.select_topk_row(s[i], int(keep[h]), forced)
-            oracle.sparse_attention_row(q[0, 0], k[0, 0], v[0, 0], lay, i, kept)
+            oracle.sparse_attention_row(q[0, 0], k[0, 0], v[0, 0], lay, i, kept, dtype)
             pairs += len(kept)
             rows += 1
             if time.perf_counter() - t0 > budget_s:
@@ -109,12 +133,33 @@ def cpu_baseline(w, data, budget_s: float):
             break
     dt = time.perf_counter() - t0
     flops = pairs * 4.0 * lay.block ** 2 * lay.head_dim
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
+    return {"value": flops / dt / 1e12, "seconds": round(dt, 3),
             "sample": f"the 32-frame layer, head by head until the time budget: pooling and "
-                      f"pooled scores of {heads} head(s), then top-k selection + float64 "
-                      f"block-sparse attention for {rows} query blocks ({pairs} executed "
-                      f"block pairs, {flops / 1e9:.1f} GFLOP)"}
+                      f"pooled scores of {heads} head(s), then top-k selection + "
+                      f"{np.dtype(dtype).name} block-sparse attention for {rows} of "
+                      f"{lay.heads * lay.nblocks} query blocks ({pairs} executed block "
+                      f"pairs, {flops / 1e9:.1f} GFLOP)"}
+
+
+def cpu_baseline(w, data, budget_s: float):
+    """The oracle on the host cores: float64 (the parity oracle, `value`) and
+    float32 (the GPU's accumulation precision), each on a bounded sample, with
+    BLAS threads pinned to the cores this process may run on."""
+    model, cores = cpu_info()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:
+        limiter = None
+    try:
+        r64 = oracle_sample(w, data, budget_s, np.float64)
+        r32 = oracle_sample(w, data, budget_s * 0.5, np.float32)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    return {"value": r64["value"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "seconds": r64["seconds"], "sample": r64["sample"],
+            "fp32": {"value": r32["value"], "seconds": r32["seconds"], "sample": r32["sample"]}}
 
 
 def main():
@@ -255,8 +300,20 @@ def main():
         "device": device_info(torch),
         "graph_replay": graph,
     }
+    # the fp16 copy of K (on the side stream in the step, beside the selection)
+    # timed alone, and the attention fraction with its time charged as well
+    prep_ms = gpu_ms(torch, lambda: bsgm.attn_prepare(lay, k, aws), 20)
+    detail["attn_prepare_ms"] = round(prep_ms, 4)
+    detail["attn_with_prepare_frac"] = round(
+        flops / ((attn_avg + prep_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    # rows the fp16-logit form handed to the bf16 form (its range flags)
+    al = lambda x: (x + 255) // 256 * 256
+    redo = aws[al(lay.batch * lay.heads * lay.tokens * 64 * 2) + al(rows * 4):].view(torch.int32)
+    detail["attn_rows_bf16_form"] = int(redo[:rows].sum().item())
+    flush = None
     if not args.no_side:
-        detail["cold"] = cold_step(torch, dev, select, attend)
+        flush = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        detail["cold"] = cold_step(torch, dev, select, attend, flush)
 
     # the same selection with pooling and selection in one launch, timed alone
     # beside the two-launch form over back-to-back launches
@@ -304,8 +361,9 @@ def main():
             "layers_carried": 11, "max_pair_deficit": round(float(vmem.max()), 4),
             "executed_block_pairs": int(row_ptr[-1].item())}
         detail["other_layers"] = {
-            name: side_config(bsgm, workloads, torch, dev, name)
-            for name in ("vggt_layer_8f_s50", "vggt_layer_100f_cdf", "vggt_layer_16f_drift")}
+            name: side_config(bsgm, workloads, torch, dev, name, flush=flush)
+            for name in ("tiny_f32_1024tok", "vggt_layer_8f_s50", "vggt_layer_32f_s75",
+                         "vggt_layer_100f_cdf", "vggt_layer_16f_drift")}
 
     out = {
         "metric": "block-sparse global attn effective TFLOP/s + ms/layer, 32 frames, 75% sparse",
@@ -324,7 +382,12 @@ def main():
                                "16 heads, head_dim 64, block 128, top-88 of 352 key blocks "
                                "per query block with 32 forced special-token blocks",
                    "batch": lay.batch, "heads": lay.heads, "tokens": lay.tokens,
-                   "block": lay.block, "keep_per_query_block": int(keep[0])},
+                   "block": lay.block, "keep_per_query_block": int(keep[0]),
+                   "attention_arithmetic": "QK^T on fp16 MFMA (K copied to fp16, "
+                                           "q*scale*log2e rounded to fp16) for query blocks "
+                                           "whose |q*scale*log2e| and listed |k| stay below "
+                                           "128, else bf16 MFMA; PV on bf16 MFMA; fp32 "
+                                           "accumulation and softmax; bf16 output"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
@@ -343,10 +406,10 @@ def device_info(torch):
             "arch": getattr(p, "gcnArchName", "")}
 
 
-def cold_step(torch, dev, select, attend, reps: int = 3):
-    """One step after writing a 512 MiB buffer, which evicts the L2 caches and the
-    256 MB Infinity Cache; the median of `reps` such steps (side measurement)."""
-    flush = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+def cold_step(torch, dev, select, attend, flush, reps: int = 3):
+    """One step after writing the 512 MiB `flush` buffer, which evicts the L2
+    caches and the 256 MB Infinity Cache; the median of `reps` such steps
+    (side measurement)."""
     stream = torch.cuda.current_stream()
     sel, att = [], []
     for r in range(reps):
@@ -360,7 +423,6 @@ def cold_step(torch, dev, select, attend, reps: int = 3):
         torch.cuda.synchronize()
         sel.append(e[0].elapsed_time(e[1]))
         att.append(e[1].elapsed_time(e[2]))
-    del flush
     return {"select_ms": round(float(np.median(sel)), 4), "attn_ms": round(float(np.median(att)), 4),
             "flush_mib": 512, "reps": reps}
 
@@ -421,25 +483,75 @@ def gpu_ms(torch, fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5):
-    """Per-layer times of another preset: selection (drift scores + restoration
-    for the drift preset) and attention, each timed over back-to-back launches."""
+def cold_ms(torch, fn, flush, reps: int = 3) -> float:
+    """Median GPU time of fn, each call right after a write of the 512 MiB `flush`
+    buffer, which evicts the L2 caches and the 256 MB Infinity Cache: the
+    inputs then come from HBM."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for r in range(reps):
+        flush.fill_(float(r))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def rate(nbytes: float, ms: float) -> float:
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def mib(nbytes: float) -> float:
+    return round(nbytes / (1 << 20), 2)
+
+
+def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5, flush=None):
+    """Per-layer times of a preset: selection (drift scores + restoration for the
+    drift preset) and attention, each timed over back-to-back launches. The
+    selection's phases are also timed alone, warm (back to back, inputs still in
+    the caches) and cold (after `flush` has evicted them), with their
+    algorithmic bytes (real-token inputs read once, outputs written once) over
+    the time; only the cold rate speaks for HBM. Also the device memory each
+    phase needs besides inputs and outputs (workspace)."""
     w = workloads.config(name)
     lay = w.layout
     log(f"generating {w.name}")
     data = workloads.generate(w)
-    q, k, v = (to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
+    if lay.dtype == "bf16":
+        q, k, v = (to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
+    else:
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(data[n])).to(dev) for n in ("q", "k", "v"))
+    esize = 2 if lay.dtype == "bf16" else 4
     keep = data["keep"]
     nb, rows = lay.nblocks, lay.batch * lay.heads * lay.nblocks
+    real = lay.batch * lay.heads * lay.frames * lay.frame_valid
+    tensor_real = real * lay.head_dim * esize          # real-token bytes of Q, K or V
+    pooled = rows * lay.head_dim * 4
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
-    col_idx = torch.empty(max(bsgm.col_capacity(lay, w.mode, keep, w.force_frame_first_block), 1),
-                          dtype=torch.int32, device=dev)
-    ws = torch.empty(bsgm.workspace_bytes(lay, w.mode), dtype=torch.uint8, device=dev)
+    cap = max(bsgm.col_capacity(lay, w.mode, keep, w.force_frame_first_block), 1)
+    col_idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    ws_bytes = bsgm.workspace_bytes(lay, w.mode)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     out = {}
+    phases = {}
+
+    def phase(label, fn, nbytes):
+        warm = gpu_ms(torch, fn, reps)
+        ent = {"ms": round(warm, 4), "bytes": int(nbytes), "cache_warm_gbs": rate(nbytes, warm)}
+        if flush is not None:
+            cold = cold_ms(torch, fn, flush)
+            ent.update({"cold_ms": round(cold, 4), "cold_hbm_gbs": rate(nbytes, cold)})
+        phases[label] = ent
+        return warm
+
     if w.mode == bsgm.DRIFT:
         contrib = torch.empty((lay.batch, lay.heads, nb, nb, 64), dtype=torch.float32, device=dev)
         score = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+        zmass = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
 
         def scores():
             bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws)
@@ -448,8 +560,6 @@ def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5):
             bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=w.swap_rounds,
                                force=w.force_frame_first_block, row_ptr=row_ptr,
                                col_idx=col_idx, want_stat=False)
-        # the renormalised objective on the same layer (scores with block masses)
-        zmass = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
 
         def scores_z():
             bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws,
@@ -460,23 +570,51 @@ def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5):
                                force=w.force_frame_first_block, row_ptr=row_ptr,
                                col_idx=col_idx, want_stat=False,
                                objective=bsgm.RENORMALISED, zmass=zmass)
+        chat_bytes = rows * nb * 64 * 4
+        csr_bytes = 4 * (rows + 1) + 4 * lay.batch * nb * int(np.sum(keep))
+        # the renormalised objective on the same layer (scores with block masses)
         out["renorm_drift_scores_ms"] = round(gpu_ms(torch, scores_z, reps), 4)
         out["renorm_drift_select_ms"] = round(gpu_ms(torch, select_z, reps), 4)
-        out["drift_scores_ms"] = round(gpu_ms(torch, scores, reps), 4)
-        out["drift_select_ms"] = round(gpu_ms(torch, select, reps), 4)
+        out["drift_scores_ms"] = round(phase(
+            "drift_scores", scores, 3 * tensor_real + chat_bytes + rows * nb * 4), 4)
+        out["drift_select_ms"] = round(phase("drift_select", select, chat_bytes + csr_bytes), 4)
         sel = out["drift_scores_ms"] + out["drift_select_ms"]
+        out["workspace_mib"] = {"drift_scores": mib(ws_bytes),
+                                "contributions_and_scores": mib(chat_bytes + 2 * rows * nb * 4)}
     else:
         def select():
             bsgm.select_blocks(lay, w.mode, keep, q=q, k=k, cdf_tau=w.cdf_tau,
                                force=w.force_frame_first_block, row_ptr=row_ptr,
                                col_idx=col_idx, workspace=ws, want_stat=False)
-        out["select_ms"] = round(gpu_ms(torch, select, reps), 4)
-        sel = out["select_ms"]
+        qbar = torch.empty((lay.batch, lay.heads, nb, lay.head_dim), dtype=torch.float32,
+                           device=dev)
+        kbar = torch.empty_like(qbar)
 
-    aws = torch.empty(bsgm.attn_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+        def pool():
+            bsgm.pool_blocks(lay, q, out=qbar)
+            bsgm.pool_blocks(lay, k, out=kbar)
+
+        def select_pooled():
+            bsgm.select_blocks_pooled(lay, w.mode, keep, qbar, kbar, cdf_tau=w.cdf_tau,
+                                      force=w.force_frame_first_block, row_ptr=row_ptr,
+                                      col_idx=col_idx, workspace=ws, want_stat=False)
+        pool()
+        select()
+        torch.cuda.synchronize()
+        csr_bytes = 4 * (rows + 1) + 4 * int(row_ptr[-1].item())
+        phase("pool_q_k", pool, 2 * tensor_real + 2 * pooled)
+        phase("select_from_means", select_pooled, 2 * pooled + csr_bytes)
+        out["select_ms"] = round(phase("select", select, 2 * tensor_real + csr_bytes), 4)
+        sel = out["select_ms"]
+        out["workspace_mib"] = {"select": mib(ws_bytes)}
+
+    aws_bytes = bsgm.attn_workspace_bytes(lay)
+    aws = torch.empty(aws_bytes, dtype=torch.uint8, device=dev) if aws_bytes else None
+    out["workspace_mib"]["attention"] = mib(aws_bytes)
 
     def attend():
         bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o, workspace=aws)
+    select()
     attn = gpu_ms(torch, attend, reps)
     executed = int(row_ptr[-1].item())
     flops = executed * 4.0 * lay.block ** 2 * lay.head_dim
@@ -487,6 +625,7 @@ def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5):
         "measured_block_sparsity": round(1.0 - executed / (rows * nb), 6),
         "attn_effective_tflops": round(flops / (attn * 1e-3) / 1e12, 2),
         "layer_effective_tflops": round(flops / ((sel + attn) * 1e-3) / 1e12, 2),
+        "selection_phases": phases,
     })
     del q, k, v, o, data
     torch.cuda.empty_cache()

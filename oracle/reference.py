@@ -52,14 +52,16 @@ def forced_blocks(layout, force: bool) -> List[int]:
 # threshold on pooled query/key inner products; VASC A.1: pooled query blocks
 # index physical key/value child blocks).
 # --------------------------------------------------------------------------
-def pool(x: np.ndarray, layout) -> np.ndarray:
-    """Mean of x over the real tokens of every block: [B,H,N,D] -> [B,H,Nb,D]."""
+def pool(x: np.ndarray, layout, dtype=np.float64) -> np.ndarray:
+    """Mean of x over the real tokens of every block: [B,H,N,D] -> [B,H,Nb,D].
+    Computed in ``dtype`` (float64 for every parity check; float32 only for
+    timing the oracle at the GPU's accumulation precision)."""
     B, H, N, D = x.shape
     nb = num_blocks(layout)
-    out = np.zeros((B, H, nb, D), dtype=np.float64)
+    out = np.zeros((B, H, nb, D), dtype=dtype)
     for j in range(nb):
         t = block_tokens(layout, j)
-        out[:, :, j, :] = x[:, :, t, :].astype(np.float64).mean(axis=2)
+        out[:, :, j, :] = x[:, :, t, :].astype(dtype).mean(axis=2)
     return out
 
 
@@ -318,32 +320,33 @@ def csr(sets) -> Tuple[np.ndarray, np.ndarray]:
 # after dropping connections; ReSS Table S6: every selection rule feeds the
 # same block grid and the same sparse kernel).
 # --------------------------------------------------------------------------
-def attention_rows(q_rows: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float
-                   ) -> Tuple[np.ndarray, np.ndarray]:
-    """Exact softmax attention of the given query rows over the given keys."""
-    s = scale * (q_rows.astype(np.float64) @ keys.astype(np.float64).T)
+def attention_rows(q_rows: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float,
+                   dtype=np.float64) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact softmax attention of the given query rows over the given keys, in
+    ``dtype`` (float64 for parity; float32 only for timing)."""
+    s = dtype(scale) * (q_rows.astype(dtype) @ keys.astype(dtype).T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)
-    o = (e @ vals.astype(np.float64)) / l
+    o = (e @ vals.astype(dtype)) / l
     return o, (m + np.log(l))[:, 0]
 
 
-def sparse_attention_row(q_bh, k_bh, v_bh, layout, i: int, kept: Sequence[int]
-                         ) -> Tuple[np.ndarray, np.ndarray]:
+def sparse_attention_row(q_bh, k_bh, v_bh, layout, i: int, kept: Sequence[int],
+                         dtype=np.float64) -> Tuple[np.ndarray, np.ndarray]:
     """Output rows of query block i attending to the real keys of the kept blocks.
 
     Returns (o [Bk, D], lse [Bk]); padding query rows give o = 0, lse = -inf.
     """
     Bk, D = layout.block, q_bh.shape[-1]
-    o = np.zeros((Bk, D))
-    lse = np.full(Bk, -np.inf)
+    o = np.zeros((Bk, D), dtype=dtype)
+    lse = np.full(Bk, -np.inf, dtype=dtype)
     rows = block_tokens(layout, i)
     if not len(kept):
         return o, lse          # no listed block: nothing to attend to
     keys = np.concatenate([block_tokens(layout, j) for j in sorted(kept)])
     if len(rows) and len(keys):
-        orow, lrow = attention_rows(q_bh[rows], k_bh[keys], v_bh[keys], layout.scale)
+        orow, lrow = attention_rows(q_bh[rows], k_bh[keys], v_bh[keys], layout.scale, dtype)
         o[rows - i * Bk] = orow
         lse[rows - i * Bk] = lrow
     return o, lse
