@@ -189,6 +189,55 @@ def restore_row(chat: np.ndarray, k: int, rounds: int, forced: Sequence[int] = (
     return sorted(kept), float(math.sqrt(float(r @ r))), swaps
 
 
+def rerank_row(chat: np.ndarray, k: int, rounds: int, forced: Sequence[int] = (),
+               track_best: bool = True) -> Tuple[List[int], float, List[List[int]], List[float]]:
+    """Drift selection of one query block at budget k by re-rank rounds.
+
+    ReSS scores each block by the shift that dropping it leaves (Fig. 3(b):
+    the blocks of highest drift score form the initial selected set) and then
+    refines the drop set as a whole (abstract; Fig. 3(c)). Reading of a round
+    here: every block is scored again against the residual of the current drop
+    set D, r = sum_{j in D} chat_j. With r_j = r minus chat_j when j is in D
+    (else r), block j's score is the growth of J^2 that dropping it causes,
+        g_j = ||r_j + chat_j||^2 - ||r_j||^2,
+    and the new kept set is the forced blocks plus the highest g (ties: lower
+    index), k in all, all blocks moving at once. With D empty, g_j = ||chat_j||^2:
+    the initial set is the round-0 case of the same rule. Since many blocks move
+    together a round can raise J (ReSS Table S3 compares keeping the best set
+    seen, "track-best", with keeping the last); with track_best the returned set
+    is the one of least J among the initial set and every round's set (ties: the
+    earlier), else the last one.
+    Returns (kept ascending, J of that set, the kept set of every round with the
+    initial set first, J of each of those sets).
+    """
+    nb = chat.shape[0]
+    d2 = (chat * chat).sum(axis=1)
+    fset = set(forced)
+    kept = set(priority_order(d2, forced)[:k])
+
+    def jdrift(kset):
+        drop = [j for j in range(nb) if j not in kset]
+        r = chat[drop].sum(axis=0) if drop else np.zeros(chat.shape[1])
+        return r, float(math.sqrt(float(r @ r)))
+
+    r, j0 = jdrift(kept)
+    sets, js = [sorted(kept)], [j0]
+    for _ in range(rounds):
+        g = np.empty(nb)
+        for j in range(nb):
+            rj = r - chat[j] if j not in kept else r
+            g[j] = float((rj + chat[j]) @ (rj + chat[j])) - float(rj @ rj)
+        kept = set(priority_order(g, forced)[:k])
+        r, jn = jdrift(kept)
+        sets.append(sorted(kept))
+        js.append(jn)
+    if track_best:
+        best = min(range(len(js)), key=lambda x: (js[x], x))
+    else:
+        best = len(js) - 1
+    return sets[best], js[best], sets, js
+
+
 def drift_j(chat: np.ndarray, kept: Sequence[int]) -> float:
     """Realised drift of a kept set: the norm of the summed dropped contributions."""
     drop = sorted(set(range(chat.shape[0])) - set(kept))

@@ -200,3 +200,93 @@ def test_renormalised_restoration_takes_the_best_swap(seed, force, swapped):
     assert sorted(cur) == kept
     assert j_final == pytest.approx(j_cur, rel=1e-10)
     assert (len(swaps) >= 1) == swapped
+
+
+# --------------------------------------------------------------------------
+# re-rank rounds with and without track-best (ReSS abstract and Fig. 3(c):
+# the drop set is refined as a whole; Table S3: keeping the best set seen)
+# --------------------------------------------------------------------------
+PLANTED_RERANK = np.array([[-2.0, 0.0], [-2.0, -2.0], [2.0, -3.0], [-3.0, 3.0]])
+
+
+def test_rerank_planted_row_rises_and_track_best_keeps_the_best_set():
+    """Four 2-d contributions, keep 2. Squared norms 4, 8, 13, 18, so the
+    initial set is {2, 3}, D = {0, 1}, r = (-4, -2), J^2 = 20.
+    Round 1, g_j = ||r_j + c_j||^2 - ||r_j||^2: g0 = 20 - |(-2,-2)|^2 = 12,
+    g1 = 20 - |(-2,0)|^2 = 16, g2 = |(-2,-5)|^2 - 20 = 9, g3 = |(-7,1)|^2 - 20 =
+    30 -> keep {1, 3}, r = (0, -3), J^2 = 9.
+    Round 2: g0 = 9 - |(2,-3)|^2 = -4, g2 = 9 - |(-2,0)|^2 = 5,
+    g1 = |(-2,-5)|^2 - 9 = 20, g3 = |(-3,0)|^2 - 9 = 0 -> keep {1, 2},
+    r = (-5, 3), J^2 = 34: J rises.
+    Round 3: g0 = 34 - |(-3,3)|^2 = 16, g3 = 34 - |(-2,0)|^2 = 30,
+    g1 = |(-7,1)|^2 - 34 = 16, g2 = |(-3,0)|^2 - 34 = -25 -> 3, then the tie
+    g0 = g1 = 16 goes to block 0: keep {0, 3}, r = (0, -5), J^2 = 25."""
+    kept, j, sets, js = oracle.rerank_row(PLANTED_RERANK, 2, 3, track_best=False)
+    assert sets == [[2, 3], [1, 3], [1, 2], [0, 3]]
+    np.testing.assert_allclose(np.square(js), [20.0, 9.0, 34.0, 25.0], rtol=0, atol=1e-12)
+    assert kept == [0, 3] and j == pytest.approx(5.0, abs=1e-12)
+    kept_b, j_b, sets_b, _ = oracle.rerank_row(PLANTED_RERANK, 2, 3, track_best=True)
+    assert sets_b == sets and kept_b == [1, 3] and j_b == pytest.approx(3.0, abs=1e-12)
+    # the exhaustive optimum (keep {0, 1}: r = (-1, 0)) is below both
+    best = min(oracle.drift_j(PLANTED_RERANK, list(c)) for c in itertools.combinations(range(4), 2))
+    assert best == pytest.approx(1.0, abs=1e-12)
+    # and the single best-swap restoration of the same row reaches it in two rounds:
+    # (1, 2) to J^2 = 9, then (0, 3) to J^2 = 1
+    kept_s, j_s, swaps = oracle.restore_row(PLANTED_RERANK, 2, 3)
+    assert swaps == [(1, 2), (0, 3)] and kept_s == [0, 1] and j_s == pytest.approx(1.0, abs=1e-12)
+
+
+def rerank_scores_by_set_sums(chat, kept):
+    """Each block's score as two drift values computed from whole sets: J^2 of the
+    drop set with the block added, minus J^2 of the drop set without it."""
+    nb = chat.shape[0]
+    g = []
+    for j in range(nb):
+        drop_without = [x for x in range(nb) if x not in kept and x != j]
+        with_j = drop_without + [j]
+        jw = oracle.drift_j(chat, [x for x in range(nb) if x not in with_j]) ** 2
+        jo = oracle.drift_j(chat, [x for x in range(nb) if x not in drop_without]) ** 2
+        g.append(jw - jo)
+    return np.array(g)
+
+
+@pytest.mark.parametrize("seed,nb,k,forced", [(0, 7, 3, ()), (1, 9, 4, (2,)), (2, 10, 5, (0, 5)),
+                                                (3, 8, 2, ())])
+def test_rerank_rounds_exhaustive(seed, nb, k, forced):
+    """Small rows: every round's set is the forced blocks plus the top scores
+    computed from whole-set drift values; the track-best J is the least J of the
+    trace, never above the initial J and never below the exhaustive optimum
+    over all k-sets that hold the forced blocks."""
+    rng = np.random.default_rng(300 + seed)
+    chat = rng.standard_normal((nb, 3)) * rng.uniform(0.2, 2.0, (nb, 1))
+    rounds = 6
+    kept, j, sets, js = oracle.rerank_row(chat, k, rounds, forced, track_best=True)
+    for x in range(1, len(sets)):
+        g = rerank_scores_by_set_sums(chat, set(sets[x - 1]))
+        rest = sorted((j2 for j2 in range(nb) if j2 not in forced), key=lambda j2: (-g[j2], j2))
+        assert sets[x] == sorted(list(forced) + rest[:k - len(forced)]), x
+    for x, sx in enumerate(sets):
+        assert len(sx) == k and set(forced) <= set(sx)
+        assert js[x] == pytest.approx(oracle.drift_j(chat, sx), abs=1e-12)
+    assert j == pytest.approx(min(js), abs=1e-15) and j <= js[0] + 1e-15
+    opt = min(oracle.drift_j(chat, list(c)) for c in itertools.combinations(range(nb), k)
+              if set(forced) <= set(c))
+    assert j >= opt - 1e-12
+    kept_n, j_n, _, js_n = oracle.rerank_row(chat, k, rounds, forced, track_best=False)
+    assert js_n == js and kept_n == sets[-1]
+
+
+def test_rerank_zero_rounds_is_the_initial_drift_set():
+    rng = np.random.default_rng(7)
+    chat = rng.standard_normal((12, 4))
+    for forced in ((), (3, 8)):
+        kept, j, sets, js = oracle.rerank_row(chat, 5, 0, forced)
+        k0, j0, _ = oracle.restore_row(chat, 5, 0, forced)
+        assert kept == k0 and sets == [k0] and j == pytest.approx(j0, abs=1e-15)
+
+
+def test_rerank_fixed_point_stays():
+    """A set that a round leaves unchanged stays for every later round."""
+    chat = np.array([[5.0, 0.0], [0.0, 4.0], [0.1, 0.0], [0.0, -0.1]])
+    kept, j, sets, js = oracle.rerank_row(chat, 2, 4)
+    assert all(sx == [0, 1] for sx in sets) and len(set(js)) == 1
