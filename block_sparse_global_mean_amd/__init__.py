@@ -9,6 +9,7 @@ ctypes binding to its C ABI (include/bsgm.h).
 from ._lib import (  # noqa: F401
     BF16, CDF, DRIFT, DROPPED_SUM, F32, RENORMALISED, TOPK, VASC, BsgmError, EXPORTS, LIB_PATH,
     attn_prepare, attn_workspace_bytes, col_capacity, drift_scores, fused_workspace_bytes, library,
-    pool_blocks, select_blocks, select_blocks_fused, select_blocks_pooled, sparse_attn_fwd, special_rows_dense_fwd, special_rows_workspace_bytes,
+    NOALLOC_SCRATCH_BYTES, pool_blocks, select_blocks, select_blocks_fused, select_blocks_noalloc,
+    select_blocks_pooled, sparse_attn_fwd, special_rows_dense_fwd, special_rows_workspace_bytes,
     vasc_pairs, vasc_select_blocks, version, workspace_bytes,
 )

@@ -30,7 +30,7 @@ EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
            "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes", "bsgm_attn_prepare",
            "bsgm_sparse_attn_fwd_prepared", "bsgm_select_blocks_fused", "bsgm_fused_workspace_bytes",
-           "bsgm_select_blocks_pooled")
+           "bsgm_select_blocks_pooled", "bsgm_select_blocks_noalloc")
 
 
 class BsgmError(RuntimeError):
@@ -82,6 +82,8 @@ def library() -> ctypes.CDLL:
                                                  sz, vp]
         lib.bsgm_select_blocks_pooled.argtypes = [lp, pp, vp, vp, vp, vp, ctypes.c_int64, vp, vp,
                                                   vp, sz, vp]
+        lib.bsgm_select_blocks_noalloc.argtypes = [lp, pp, vp, vp, vp, vp, ctypes.c_int64, vp, vp,
+                                                   vp]
         lib.bsgm_fused_workspace_bytes.argtypes = [lp]
         lib.bsgm_fused_workspace_bytes.restype = sz
         lib.bsgm_attn_workspace_bytes.argtypes = [lp]
@@ -94,6 +96,7 @@ def library() -> ctypes.CDLL:
         for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
                      "bsgm_sparse_attn_fwd", "bsgm_special_rows_dense_fwd",
                      "bsgm_vasc_select_blocks", "bsgm_select_blocks_fused", "bsgm_select_blocks_pooled",
+                     "bsgm_select_blocks_noalloc",
                      "bsgm_attn_prepare",
                      "bsgm_sparse_attn_fwd_prepared"):
             getattr(lib, name).restype = ctypes.c_int
@@ -258,11 +261,12 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
     _opt(row_stat, "row_stat", torch.float32, (rows,))
     _opt(scores_out, "scores_out", torch.float32, (layout.batch, layout.heads, nb, nb))
     if swap_log is not None:
+        per_row = swap_rounds * 2
         if not isinstance(swap_log, torch.Tensor) or not swap_log.is_cuda or \
                 swap_log.dtype != torch.int32 or not swap_log.is_contiguous() or \
-                swap_log.numel() < rows * swap_rounds * 2:
+                swap_log.numel() < rows * per_row:
             raise ValueError(f"swap_log must be a contiguous int32 device tensor of at least "
-                             f"{rows} x {swap_rounds} x 2 elements")
+                             f"{rows} x {per_row} elements")
     cap = col_capacity(layout, mode, keep, force)
     if row_ptr is None:
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
@@ -309,6 +313,40 @@ def select_blocks_pooled(layout, mode: int, keep: Sequence[int], qbar, kbar, cdf
     _check(library().bsgm_select_blocks_pooled(
         ctypes.byref(L), ctypes.byref(P), _ptr(qbar), _ptr(kbar), _ptr(row_ptr), _ptr(col_idx),
         col_idx.numel(), _ptr(row_stat), _ptr(scores_out), *_ws(workspace), _stream(stream)))
+    return row_ptr, col_idx, row_stat
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # BSGM_NOALLOC_SCRATCH_BYTES of the header
+
+
+def select_blocks_noalloc(layout, mode: int, keep: Sequence[int], q, k, cdf_tau: float = 0.9,
+                          force: bool = False, row_ptr=None, col_idx=None, row_stat=None,
+                          scores_out=None, want_stat: bool = True, stream=None):
+    """TOPK or CDF selection like select_blocks, with the library's own scratch
+    array instead of a workspace (the C call allocates nothing; tensors not
+    given here are still allocated by this wrapper)."""
+    n, nb, rows = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    _expect(q, "q", _tdtype(layout), shape)
+    _expect(k, "k", _tdtype(layout), shape)
+    _opt(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    if col_idx is not None:
+        _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(row_stat, "row_stat", torch.float32, (rows,))
+    _opt(scores_out, "scores_out", torch.float32, (layout.batch, layout.heads, nb, nb))
+    dev = q.device
+    cap = col_capacity(layout, mode, keep, force)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_stat is None and want_stat:
+        row_stat = torch.empty(rows, dtype=torch.float32, device=dev)
+    L = c_layout(layout)
+    P, _keep = c_params(mode, keep, cdf_tau, force)
+    _check(library().bsgm_select_blocks_noalloc(
+        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(row_ptr), _ptr(col_idx),
+        col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/bsgm.h"
@@ -160,11 +161,46 @@ int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBud
   return BSGM_OK;
 }
 
+// Checks of the TOPK / CDF arguments shared by the pooled selection entry points.
+int check_pooled_select(const bsgm::Dims& d, const bsgm_select_params* params, const void* q,
+                        const void* k) {
+  if (!q || !k) return fail(BSGM_E_ARG, "TOPK and CDF need q and k");
+  if (params->mode == BSGM_SEL_CDF && !(params->cdf_tau > 0.f && params->cdf_tau <= 1.f))
+    return fail(BSGM_E_ARG, "cdf_tau must be in (0, 1]");
+  if (d.nb > bsgm::kSelectMaxBlocks)
+    return fail(BSGM_E_UNSUPPORTED, "pooled selection supports at most %d blocks per row",
+                bsgm::kSelectMaxBlocks);
+  return BSGM_OK;
+}
+
+// Pools Q and K into the workspace and selects (TOPK or CDF) from the means.
+int run_pooled_select(const bsgm::Dims& d, const bsgm::HeadBudget& hb, int dtype,
+                      const bsgm_select_params* params, const void* q, const void* k,
+                      int32_t* row_ptr, int32_t* col_idx, float* row_stat, float* scores_out,
+                      void* ws, const WsLayout& w, hipStream_t s) {
+  const int mode = params->mode;
+  char* base = static_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(base + w.qbar);
+  float* kbar = reinterpret_cast<float*>(base + w.kbar);
+  int32_t* counts = mode == BSGM_SEL_CDF ? reinterpret_cast<int32_t*>(base + w.counts) : nullptr;
+  uint32_t* bitmask =
+      mode == BSGM_SEL_CDF ? reinterpret_cast<uint32_t*>(base + w.bitmask) : nullptr;
+  const void* xs[2] = {q, k};
+  float* means[2] = {qbar, kbar};
+  hipError_t e = bsgm::launch_pool_n(d, dtype, 2, xs, means, s);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  e = bsgm::launch_select_pooled(d, hb, mode, params->cdf_tau,
+                                 params->force_frame_first_block ? 1 : 0, qbar, kbar, row_ptr,
+                                 col_idx, row_stat, scores_out, counts, bitmask, s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t bsgm_version(void) { return 10400; }
+int32_t bsgm_version(void) { return 10500; }
 
 const char* bsgm_last_error(void) { return g_err.c_str(); }
 
@@ -300,31 +336,14 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
     if (e != hipSuccess) return hip_fail(e, "drift select launch");
     return ok();
   }
-  if (!q || !k) return fail(BSGM_E_ARG, "TOPK and CDF need q and k");
-  if (mode == BSGM_SEL_CDF && !(params->cdf_tau > 0.f && params->cdf_tau <= 1.f))
-    return fail(BSGM_E_ARG, "cdf_tau must be in (0, 1]");
-  if (d.nb > bsgm::kSelectMaxBlocks)
-    return fail(BSGM_E_UNSUPPORTED, "pooled selection supports at most %d blocks per row",
-                bsgm::kSelectMaxBlocks);
+  st = check_pooled_select(d, params, q, k);
+  if (st != BSGM_OK) return st;
   if (!ws) return fail(BSGM_E_ARG, "ws must be non-NULL");
   const WsLayout w = ws_layout(d, mode);
   if (ws_bytes < w.total)
     return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
-  char* base = static_cast<char*>(ws);
-  float* qbar = reinterpret_cast<float*>(base + w.qbar);
-  float* kbar = reinterpret_cast<float*>(base + w.kbar);
-  int32_t* counts = mode == BSGM_SEL_CDF ? reinterpret_cast<int32_t*>(base + w.counts) : nullptr;
-  uint32_t* bitmask =
-      mode == BSGM_SEL_CDF ? reinterpret_cast<uint32_t*>(base + w.bitmask) : nullptr;
-  const void* xs[2] = {q, k};
-  float* means[2] = {qbar, kbar};
-  hipError_t e = bsgm::launch_pool_n(d, layout->dtype, 2, xs, means, s);
-  if (e != hipSuccess) return hip_fail(e, "pool launch");
-  e = bsgm::launch_select_pooled(d, hb, mode, params->cdf_tau,
-                                 params->force_frame_first_block ? 1 : 0, qbar, kbar, row_ptr,
-                                 col_idx, row_stat, scores_out, counts, bitmask, s);
-  if (e != hipSuccess) return hip_fail(e, "select launch");
-  return ok();
+  return run_pooled_select(d, hb, layout->dtype, params, q, k, row_ptr, col_idx, row_stat,
+                           scores_out, ws, w, s);
 }
 
 int bsgm_select_blocks_pooled(const bsgm_layout* layout, const bsgm_select_params* params,
@@ -544,6 +563,88 @@ int bsgm_sparse_attn_fwd_prepared(const bsgm_layout* layout, const void* q, cons
                                   const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                                   void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return attn_fwd(layout, q, k, v, row_ptr, col_idx, o, lse, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Selection with a library-held scratch array (bsgm_select_blocks_noalloc).
+//
+// The pooled means (and the CDF counts and bitmask) live in `scratch`, one
+// array per GPU that stays allocated until the process ends. Host code never
+// passes `scratch` itself to a kernel or copy: in host code the name is a
+// host-side stand-in, not the device array. Its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// kept in g_scratch_addr. Every call on a GPU shares that GPU's array, so calls
+// that overlap in time on one GPU race; the selection writes every word it
+// later reads, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[BSGM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = BSGM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of this GPU's `scratch` (the current device's).
+int scratch_addr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSGM_E_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(BSGM_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return BSGM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsgm_select_blocks_noalloc(const bsgm_layout* layout, const bsgm_select_params* params,
+                               const void* q, const void* k, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, float* row_stat, float* scores_out,
+                               void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  bsgm::HeadBudget hb;
+  st = check_budget(d, params, &hb);
+  if (st != BSGM_OK) return st;
+  const int mode = params->mode;
+  if (mode != BSGM_SEL_TOPK && mode != BSGM_SEL_CDF)
+    return fail(BSGM_E_UNSUPPORTED, "the scratch-array selection takes TOPK or CDF (got mode %d)",
+                mode);
+  if (!row_ptr || !col_idx) return fail(BSGM_E_ARG, "row_ptr and col_idx must be non-NULL");
+  const long long need = (long long)d.B * hb.per_batch;
+  if (need > 0x7FFFFFFFLL)
+    return fail(BSGM_E_UNSUPPORTED, "worst-case nnz %lld does not fit int32 CSR", need);
+  if (col_capacity < need)
+    return fail(BSGM_E_CAPACITY, "col_capacity %lld below worst-case nnz %lld",
+                (long long)col_capacity, need);
+  st = check_pooled_select(d, params, q, k);
+  if (st != BSGM_OK) return st;
+  const WsLayout w = ws_layout(d, mode);
+  if (w.total > kNoAllocScratchBytes)
+    return fail(BSGM_E_WORKSPACE, "layout needs %zu bytes of scratch; the library's array holds %zu",
+                w.total, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = scratch_addr(&ws);
+  if (st != BSGM_OK) return st;
+  return run_pooled_select(d, hb, layout->dtype, params, q, k, row_ptr, col_idx, row_stat,
+                           scores_out, ws, w, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -296,6 +296,38 @@ int bsgm_sparse_attn_fwd_prepared(const bsgm_layout* layout, const void* q, cons
  * (see bsgm_last_error). */
 size_t bsgm_attn_workspace_bytes(const bsgm_layout* layout);
 
+/* Bytes of the scratch array that bsgm_select_blocks_noalloc keeps on every
+ * GPU it runs on (16 MiB). */
+#define BSGM_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* TOPK or CDF selection as bsgm_select_blocks, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): it takes no workspace. Its pooled means
+ * (and the CDF counts and flags) go to a scratch array of
+ * BSGM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it is called
+ * on, from its first call there until the process ends; the call itself
+ * allocates and frees nothing. The results are those of bsgm_select_blocks
+ * with the same arguments, bit for bit (same kernels).
+ * The array is that of the current device, which must be the device of
+ * `stream`. Every call on one GPU shares its array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give undefined results;
+ * order them (one stream, or events). Nothing in the array needs clearing: each
+ * call writes every word it later reads.
+ *   params     mode BSGM_SEL_TOPK or BSGM_SEL_CDF (BSGM_E_UNSUPPORTED otherwise);
+ *              the other fields as bsgm_select_blocks
+ *   q, k, row_ptr, col_idx, col_capacity, row_stat, scores_out
+ *              as bsgm_select_blocks
+ * Errors: those of bsgm_select_blocks; BSGM_E_WORKSPACE when the layout needs
+ * more scratch than the array holds (bsgm_workspace_bytes(layout, mode) >
+ * BSGM_NOALLOC_SCRATCH_BYTES; for example a 100-frame layer of 16 heads and
+ * blocks of 128 needs about 12 MiB in CDF mode), checked before anything is
+ * enqueued; BSGM_E_HIP if the array's device address cannot be looked up.
+ */
+int bsgm_select_blocks_noalloc(const bsgm_layout* layout, const bsgm_select_params* params,
+                               const void* q, const void* k, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, float* row_stat, float* scores_out,
+                               void* stream);
+
 /* Value-aware block selection with cross-layer pair memory ([VASC] 4.1-4.3,
  * A.1-A.5), one layer: selection from the memory, then the memory update.
  * Key blocks 2p and 2p+1 form pair p (an odd last block is a singleton).

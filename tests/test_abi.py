@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = bsgm.library()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert bsgm.version() == 10400
+    assert bsgm.version() == 10500
 
 
 class L:
@@ -172,6 +172,46 @@ def test_select_from_pooled_means_errors():
     assert call(mode=bsgm.CDF, tau=0.0) == -1
     assert call(mode=bsgm.CDF, ws=None) == -1
     assert call(mode=bsgm.CDF, wsb=10) == -4
+
+
+def test_noalloc_select_errors():
+    """The scratch-array selection checks everything on the host, the scratch
+    size first among the workspace checks, before any device call."""
+    lib = bsgm.library()
+
+    def call(lay, mode=0, keep=None, tau=0.9, q=16, k=16, rp=16, ci=16, cap=None):
+        c = _lib.c_layout(lay)
+        keep = [2] * lay.heads if keep is None else keep
+        P, arr = _lib.c_params(mode, keep, tau, False)
+        need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
+        cap = need if cap is None else cap
+        v = lambda x: None if x is None else ctypes.c_void_p(x)
+        return lib.bsgm_select_blocks_noalloc(ctypes.byref(c), ctypes.byref(P), v(q), v(k), v(rp),
+                                              v(ci), cap, None, None, None)
+
+    lay = L(batch=3)
+    assert call(lay, mode=bsgm.DRIFT) == -2
+    assert call(lay, mode=bsgm.VASC) == -2
+    assert call(lay, q=None) == -1
+    assert call(lay, k=None) == -1
+    assert call(lay, rp=None) == -1
+    assert call(lay, ci=None) == -1
+    assert call(lay, keep=(0, 2)) == -1
+    assert call(lay, cap=3 * 8 * 4 - 1) == -3
+    assert call(lay, mode=bsgm.CDF, tau=1.5) == -1
+    # 4 x 16 heads of a 100-frame layer: 4 * 16 * 1100 rows of two 256-byte means
+    big = L(batch=4, heads=16, frames=100, frame_len=1408, frame_valid=1374, block=128)
+    assert ws(big, bsgm.TOPK) > bsgm.NOALLOC_SCRATCH_BYTES
+    assert call(big) == -4
+    assert "scratch" in lib.bsgm_last_error().decode()
+    one = L(batch=1, heads=16, frames=100, frame_len=1408, frame_valid=1374, block=128)
+    assert ws(one, bsgm.CDF) <= bsgm.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "bsgm.h")).read()
+    m = re.search(r"#define BSGM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == bsgm.NOALLOC_SCRATCH_BYTES
 
 
 def test_col_capacity_and_errors():
