@@ -7,7 +7,8 @@ query rows run in the HIP kernels of libbsgm.so; this package is the thin
 ctypes binding to its C ABI (include/bsgm.h).
 """
 from ._lib import (  # noqa: F401
-    BF16, CDF, DRIFT, DROPPED_SUM, F32, RENORMALISED, TOPK, VASC, BsgmError, EXPORTS, LIB_PATH,
+    BEST_SWAP, BF16, CDF, DRIFT, DROPPED_SUM, F32, RENORMALISED, RERANK, RERANK_TRACK_BEST, TOPK,
+    VASC, BsgmError, EXPORTS, LIB_PATH,
     attn_prepare, attn_workspace_bytes, col_capacity, drift_scores, fused_workspace_bytes, library,
     NOALLOC_SCRATCH_BYTES, pool_blocks, select_blocks, select_blocks_fused, select_blocks_noalloc,
     select_blocks_pooled, sparse_attn_fwd, special_rows_dense_fwd, special_rows_workspace_bytes,

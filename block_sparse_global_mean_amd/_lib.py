@@ -20,6 +20,7 @@ TOPK, CDF, DRIFT, VASC = 0, 1, 2, 3
 # Drift objectives: the norm of the dropped blocks' summed contribution, or the
 # output shift after the kept blocks are renormalised.
 DROPPED_SUM, RENORMALISED = 0, 1
+BEST_SWAP, RERANK, RERANK_TRACK_BEST = 0, 1, 2
 
 STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_CAPACITY",
           -4: "BSGM_E_WORKSPACE", -5: "BSGM_E_HIP"}
@@ -49,7 +50,8 @@ class CLayout(ctypes.Structure):
 class CSelectParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("keep_per_head", ctypes.POINTER(ctypes.c_int32)),
                 ("cdf_tau", ctypes.c_float), ("force_frame_first_block", ctypes.c_int32),
-                ("swap_rounds", ctypes.c_int32), ("drift_objective", ctypes.c_int32)]
+                ("swap_rounds", ctypes.c_int32), ("drift_objective", ctypes.c_int32),
+                ("restoration", ctypes.c_int32)]
 
 
 _lib = None
@@ -115,9 +117,11 @@ def c_layout(layout) -> CLayout:
 
 
 def c_params(mode: int, keep: Sequence[int], cdf_tau: float = 0.9, force: bool = False,
-             swap_rounds: int = 0, objective: int = 0) -> Tuple[CSelectParams, ctypes.Array]:
+             swap_rounds: int = 0, objective: int = 0,
+             restoration: int = 0) -> Tuple[CSelectParams, ctypes.Array]:
     arr = (ctypes.c_int32 * len(keep))(*[int(x) for x in keep])
-    return CSelectParams(mode, arr, cdf_tau, 1 if force else 0, swap_rounds, objective), arr
+    return CSelectParams(mode, arr, cdf_tau, 1 if force else 0, swap_rounds, objective,
+                         restoration), arr
 
 
 def _check(code: int):
@@ -242,8 +246,12 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
                   cdf_tau: float = 0.9, force: bool = False, swap_rounds: int = 0,
                   objective: int = 0, zmass=None,
                   row_ptr=None, col_idx=None, row_stat=None, scores_out=None, swap_log=None,
-                  workspace=None, want_stat: bool = True, stream=None):
-    """Selected key blocks as CSR (row_ptr, col_idx) plus the per-row statistic."""
+                  workspace=None, want_stat: bool = True, stream=None, restoration: int = 0):
+    """Selected key blocks as CSR (row_ptr, col_idx) plus the per-row statistic.
+
+    restoration (DRIFT): BEST_SWAP, RERANK or RERANK_TRACK_BEST. swap_log holds
+    [rows, swap_rounds, 2] swaps for BEST_SWAP, [rows, swap_rounds + 1,
+    ceil(nb / 32)] kept bitmasks for the re-rank rules."""
     n, nb, rows = _dims(layout)
     dev = (q if q is not None else contrib).device
     if mode in (TOPK, CDF):
@@ -261,7 +269,8 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
     _opt(row_stat, "row_stat", torch.float32, (rows,))
     _opt(scores_out, "scores_out", torch.float32, (layout.batch, layout.heads, nb, nb))
     if swap_log is not None:
-        per_row = swap_rounds * 2
+        per_row = swap_rounds * 2 if restoration == BEST_SWAP else \
+            (swap_rounds + 1) * ((nb + 31) // 32)
         if not isinstance(swap_log, torch.Tensor) or not swap_log.is_cuda or \
                 swap_log.dtype != torch.int32 or not swap_log.is_contiguous() or \
                 swap_log.numel() < rows * per_row:
@@ -277,7 +286,7 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
     if workspace is None and mode != DRIFT:
         workspace = torch.empty(workspace_bytes(layout, mode), dtype=torch.uint8, device=dev)
     L = c_layout(layout)
-    P, _keep = c_params(mode, keep, cdf_tau, force, swap_rounds, objective)
+    P, _keep = c_params(mode, keep, cdf_tau, force, swap_rounds, objective, restoration)
     _check(library().bsgm_select_blocks(
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),

@@ -326,6 +326,20 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
       return fail(BSGM_E_ARG, "unknown drift objective %d", params->drift_objective);
     if (params->drift_objective == BSGM_DRIFT_RENORMALISED && !zmass)
       return fail(BSGM_E_ARG, "the renormalised drift objective needs zmass");
+    if (params->restoration != BSGM_RESTORE_BEST_SWAP &&
+        params->restoration != BSGM_RESTORE_RERANK &&
+        params->restoration != BSGM_RESTORE_RERANK_TRACK_BEST)
+      return fail(BSGM_E_ARG, "unknown restoration rule %d", params->restoration);
+    if (params->restoration != BSGM_RESTORE_BEST_SWAP) {
+      if (params->drift_objective != BSGM_DRIFT_DROPPED_SUM)
+        return fail(BSGM_E_UNSUPPORTED, "re-rank restoration takes the dropped-sum objective");
+      hipError_t e = bsgm::launch_select_drift_rerank(
+          d, hb, params->force_frame_first_block ? 1 : 0, params->swap_rounds,
+          params->restoration == BSGM_RESTORE_RERANK_TRACK_BEST ? 1 : 0, contrib, row_ptr,
+          col_idx, row_stat, swap_log, s);
+      if (e != hipSuccess) return hip_fail(e, "drift re-rank select launch");
+      return ok();
+    }
     if (d.nb > bsgm::kDriftMaxBlocks)
       return fail(BSGM_E_UNSUPPORTED, "DRIFT supports at most %d blocks per row (got %d)",
                   bsgm::kDriftMaxBlocks, d.nb);

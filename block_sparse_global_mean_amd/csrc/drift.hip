@@ -617,3 +617,202 @@ hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, i
 }
 
 }  // namespace bsgm
+
+namespace bsgm {
+
+// ---------------------------------------------------------------------------
+// Drift selection by re-rank rounds, dropped-sum objective ([ReSS] abstract
+// and Fig. 3(c): the drop set is refined as a whole; Fig. 3(b): the initial
+// set is the top drift scores; Table S3: keeping the best set seen). A round
+// scores every block j against the residual of the current drop set D,
+// r = sum_{D} c_j:
+//   g_j = ||r_j + c_j||^2 - ||r_j||^2 = 2 <r, c_j> -/+ ||c_j||^2
+// (minus when j is in D, since then r_j = r - c_j; plus otherwise), and keeps
+// the forced blocks plus the top g (ties: lower block), all blocks at once.
+// The initial set is the same rule with r = 0. With track-best the result is
+// the set of least J = ||r|| among the initial set and every round's set
+// (ties: the earlier), else the last one.
+//
+// One workgroup of 256 threads per row. Lane group g (16 lanes, a float4 of the
+// 64-float contribution each) takes blocks g, g + 16, ...; the row is read from
+// global memory (L2) once per pass. Kept sets are bitmasks in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kRrThreads = 256;
+
+__host__ __device__ inline size_t align_up16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+struct DriftRerankArgs {
+  Dims d;
+  HeadBudget hb;
+  int force;
+  int rounds;
+  int track_best;
+  const float* contrib;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  float* row_stat;
+  int32_t* set_log;   // [rows, rounds + 1, ceil(nb / 32)] or null
+};
+
+__host__ __device__ inline size_t rerank_lds_bytes(int nb) {
+  const size_t words = (size_t)(nb + 63) / 64 * 2;   // whole 64-block ballots
+  return align_up16((size_t)nb * 4) * 2 + (size_t)nb * 8 + 2 * words * 4;
+}
+
+__global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char rsm[];
+  const Dims& d = a.d;
+  const int nb = d.nb, W = (nb + 31) >> 5, WP = (nb + 63) / 64 * 2;
+  const int r = blockIdx.x;
+  const int bh = r / nb, i = r - bh * nb;
+  const int h = bh % d.H, b = bh / d.H;
+  const int k = a.hb.keep[h];
+  float* cc = reinterpret_cast<float*>(rsm);                                   // ||c_j||^2
+  float* g = reinterpret_cast<float*>(rsm + align_up16((size_t)nb * 4));      // scores
+  unsigned long long* keys =
+      reinterpret_cast<unsigned long long*>(rsm + 2 * align_up16((size_t)nb * 4));
+  uint32_t* cur = reinterpret_cast<uint32_t*>(keys + nb);   // kept flags, WP words
+  uint32_t* best = cur + WP;
+  __shared__ __attribute__((aligned(16))) float rv[64];
+  __shared__ __attribute__((aligned(16))) float part[kRrThreads / 64][64];
+  __shared__ float red[kRrThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, grp = t >> 4, c4 = t & 15;
+  const float4* row =
+      reinterpret_cast<const float4*>(a.contrib + ((size_t)bh * nb + i) * (size_t)nb * 64);
+  auto kept = [&](const uint32_t* m, int j) { return ((m[j >> 5] >> (j & 31)) & 1u) != 0; };
+  auto sum16 = [&](float s) {
+    s += __shfl_xor(s, 8, 64);
+    s += __shfl_xor(s, 4, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 1, 64);
+    return s;
+  };
+
+  for (int j = grp; j < nb; j += kRrThreads / 16) {
+    const float4 x = row[(size_t)j * 16 + c4];
+    const float s = sum16(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
+    if (c4 == 0) cc[j] = s;
+  }
+  __syncthreads();
+
+  // cur := the forced blocks plus the top k of score (ties: lower block)
+  auto select = [&](const float* score) {
+    for (int j = t; j < nb; j += kRrThreads) {
+      const bool f = a.force && block_forced(d, j);
+      const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(score[j]);
+      keys[j] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
+    }
+    __syncthreads();
+    for (int j0 = 64 * w; j0 < WP * 32; j0 += kRrThreads) {
+      const int j = j0 + lane;
+      bool in = false;
+      if (j < nb) {
+        const unsigned long long kj = keys[j];
+        int rank = 0;
+        for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
+        in = rank < k;
+      }
+      const unsigned long long m = __ballot(in);
+      if (lane == 0) {
+        cur[j0 >> 5] = (uint32_t)m;
+        cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
+      }
+    }
+    __syncthreads();
+  };
+  // rv := r, the sum of the dropped contributions; returns ||r||^2 (every thread)
+  auto residual = [&]() {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = grp; j < nb; j += kRrThreads / 16)
+      if (!kept(cur, j)) {
+        const float4 x = row[(size_t)j * 16 + c4];
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+      }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      acc.x += __shfl_xor(acc.x, o, 64); acc.y += __shfl_xor(acc.y, o, 64);
+      acc.z += __shfl_xor(acc.z, o, 64); acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    if (lane < 16) *reinterpret_cast<float4*>(&part[w][4 * lane]) = acc;
+    __syncthreads();
+    if (t < 64) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < kRrThreads / 64; ++q) s += part[q][t];
+      rv[t] = s;
+      s = wave_sum(s * s);
+      if (t == 0) red[0] = s;
+    }
+    __syncthreads();
+    return red[0];
+  };
+  auto log_set = [&](int round) {
+    if (a.set_log)
+      for (int x = t; x < W; x += kRrThreads)
+        a.set_log[((size_t)r * (a.rounds + 1) + round) * W + x] = (int32_t)cur[x];
+  };
+
+  select(cc);
+  float rr = residual();
+  log_set(0);
+  float best_rr = rr;
+  for (int x = t; x < WP; x += kRrThreads) best[x] = cur[x];
+  for (int round = 1; round <= a.rounds; ++round) {
+    const float4 r4 = reinterpret_cast<const float4*>(rv)[c4];
+    for (int j = grp; j < nb; j += kRrThreads / 16) {
+      const float4 x = row[(size_t)j * 16 + c4];
+      const float s = sum16(x.x * r4.x + x.y * r4.y + x.z * r4.z + x.w * r4.w);
+      if (c4 == 0) g[j] = 2.f * s + (kept(cur, j) ? cc[j] : -cc[j]);
+    }
+    __syncthreads();
+    select(g);
+    rr = residual();
+    log_set(round);
+    if (rr < best_rr) {   // uniform: every thread holds the same rr and best_rr
+      best_rr = rr;
+      for (int x = t; x < WP; x += kRrThreads) best[x] = cur[x];
+    }
+  }
+  __syncthreads();
+  const uint32_t* out = a.track_best ? best : cur;
+  if (t == 0 && a.row_stat) a.row_stat[r] = sqrtf(a.track_best ? best_rr : rr);
+  const long long base = (long long)b * a.hb.per_batch + a.hb.head_off[h] + (long long)i * k;
+  if (t == 0) {
+    a.row_ptr[r] = (int32_t)base;
+    if (r == d.rows - 1) a.row_ptr[d.rows] = (int32_t)(base + k);
+  }
+  // kept blocks in ascending order: wave 0 walks the words 64 at a time
+  if (w == 0) {
+    int off = 0;
+    for (int x0 = 0; x0 < W; x0 += 64) {
+      const int x = x0 + lane;
+      const uint32_t m = x < W ? out[x] : 0u;
+      const int n = __popc(m);
+      int incl = n;   // inclusive scan of the counts over the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int pos = off + incl - n;
+      for (uint32_t mm = m; mm; mm &= mm - 1) a.col_idx[base + pos++] = 32 * x + __ffs(mm) - 1;
+      off += __shfl(incl, 63, 64);
+    }
+  }
+}
+
+hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int force, int rounds,
+                                      int track_best, const float* contrib, int32_t* row_ptr,
+                                      int32_t* col_idx, float* row_stat, int32_t* set_log,
+                                      hipStream_t s) {
+  DriftRerankArgs a{d, hb, force, rounds, track_best, contrib, row_ptr, col_idx, row_stat,
+                    set_log};
+  const size_t lds = rerank_lds_bytes(d.nb);
+  hipError_t e = hipFuncSetAttribute((const void*)k_select_drift_rerank,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select_drift_rerank, dim3(d.rows), dim3(kRrThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsgm

@@ -80,6 +80,14 @@ hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, i
                                int32_t* row_ptr, int32_t* col_idx, float* row_stat,
                                int32_t* swap_log, hipStream_t s);
 
+// Drift selection by re-rank rounds (dropped-sum objective), optionally
+// returning the least-J set seen (track_best). set_log: [rows, rounds + 1,
+// ceil(nb / 32)] kept bitmasks or null.
+hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int force, int rounds,
+                                      int track_best, const float* contrib, int32_t* row_ptr,
+                                      int32_t* col_idx, float* row_stat, int32_t* set_log,
+                                      hipStream_t s);
+
 // Block-sparse attention forward. ws: attn_workspace_bytes(d) bytes of device
 // scratch (enables the fp16 logits: an fp16 copy of K, a range flag per
 // (b, h, key block) and a fallback flag per row), or null (bf16 logits only).

@@ -83,6 +83,13 @@ typedef enum {
                                          - sum_{all} contrib || (output shift)        */
 } bsgm_drift_objective;
 
+typedef enum {
+  BSGM_RESTORE_BEST_SWAP = 0,         /* one best-improvement swap per round          */
+  BSGM_RESTORE_RERANK = 1,            /* re-rank every block per round, keep the last */
+  BSGM_RESTORE_RERANK_TRACK_BEST = 2  /* re-rank every block per round, keep the set
+                                         of least J seen                            */
+} bsgm_restoration;
+
 typedef struct {
   int32_t mode;                   /* bsgm_sel_mode                                    */
   const int32_t* keep_per_head;   /* HOST array [heads]: kept blocks per query block
@@ -93,6 +100,7 @@ typedef struct {
                                      the budget                                       */
   int32_t swap_rounds;            /* DRIFT only: restoration rounds, >= 0             */
   int32_t drift_objective;        /* DRIFT only: bsgm_drift_objective                 */
+  int32_t restoration;            /* DRIFT only: bsgm_restoration                     */
 } bsgm_select_params;
 
 /* Version of this ABI (major*10000 + minor*100 + patch). */
@@ -149,14 +157,25 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
  *          cdf_tau (all blocks if it never does), at most keep_per_head[h],
  *          at least one and at least the forced blocks.
  *   DRIFT: score = ||contrib_ij||; start from the first keep_per_head[h]; then
- *          up to swap_rounds rounds, each making the single swap (restore a
- *          dropped block a, drop a kept non-forced block b) that minimises the
- *          drift J of the resulting set (ties: lower a, then lower b) if it
- *          lowers J, stopping otherwise. J is chosen by drift_objective:
+ *          swap_rounds rounds of restoration ([ReSS] abstract and Fig. 3(c): the
+ *          drop set is refined as a whole at a fixed budget), by `restoration`:
+ *          BEST_SWAP: each round makes the single swap (restore a dropped block
+ *          a, drop a kept non-forced block b) that minimises the drift J of the
+ *          resulting set (ties: lower a, then lower b) if it lowers J, stopping
+ *          otherwise. J is chosen by drift_objective:
  *          DROPPED_SUM  J = ||sum_{dropped} contrib||;
  *          RENORMALISED J = ||sum_{kept} contrib / sum_{kept} zmass - sum_{all} contrib||,
  *          the shift of the pooled query's attention output once the dropped
  *          blocks are removed and the kept weights renormalised ([ReSS] Fig. 3(a)).
+ *          RERANK, RERANK_TRACK_BEST (DROPPED_SUM only, else BSGM_E_UNSUPPORTED):
+ *          each round scores every block j against the residual r of the current
+ *          drop set D, g_j = ||r_j + contrib_j||^2 - ||r_j||^2 with r_j = r minus
+ *          contrib_j for j in D (else r), and keeps the forced blocks plus the
+ *          highest g (ties: lower block), all blocks at once, for every one of the
+ *          swap_rounds rounds. A round may raise J; TRACK_BEST returns the set of
+ *          least J among the initial set and every round's set (ties: the
+ *          earlier; [ReSS] Table S3), RERANK the last one. Rows of any number of
+ *          blocks (BEST_SWAP: at most 512).
  *   q, k       device [B,H,N,D] (TOPK, CDF; may be NULL for DRIFT)
  *   contrib    device float [B,H,Nb,Nb,D] from bsgm_drift_scores (DRIFT only)
  *   zmass      device float [B,H,Nb,Nb] from bsgm_drift_scores (RENORMALISED only)
@@ -166,8 +185,11 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
  *   row_stat   device float [B*H*Nb] or NULL: kept pooled mass sum_{kept} P
  *              (TOPK, CDF) or the final drift J under the objective (DRIFT)
  *   scores_out device float [B,H,Nb,Nb] or NULL: the pooled logits (TOPK, CDF)
- *   swap_log   device int32 [B*H*Nb, swap_rounds, 2] or NULL: the (a, b) of each
- *              round, (-1, -1) once restoration has stopped (DRIFT)
+ *   swap_log   device int32 or NULL (DRIFT). BEST_SWAP: [B*H*Nb, swap_rounds, 2],
+ *              the (a, b) of each round, (-1, -1) once restoration has stopped.
+ *              RERANK modes: [B*H*Nb, swap_rounds + 1, ceil(Nb / 32)], the kept
+ *              set of the initial selection and of each round as bitmask words
+ *              (bit j % 32 of word j / 32 set iff block j is kept)
  *   ws         device, >= bsgm_workspace_bytes(layout, mode) bytes
  */
 int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* params,

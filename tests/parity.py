@@ -10,7 +10,11 @@ up to a score gap of 1e-4, measured on the oracle's float64 values:
     of 1e-4, and every logged swap is optimal, and every stop justified, up to
     a relative 1e-4 in J (2e-4 in J^2) when replayed on the oracle's
     contributions, under the objective the selection used (for the renormalised
-    one with an absolute allowance for float32 rounding, see drift_valid).
+    one with an absolute allowance for float32 rounding, see drift_valid);
+  * drift by re-rank rounds: the initial set and every logged round's set are
+    top-k sets of their scores up to a gap of 1e-4 of the largest |score|, and
+    the returned set is the last one or, with track-best, one of least J up to
+    a relative 2e-4 (see rerank_valid).
 Outputs: fp32 max |O - O_ref| <= 1e-3; bf16 max_d |O - O_ref| <= 2e-2 * RMS_d(O_ref)
 for every real query row (see output_check).
 """
@@ -178,3 +182,51 @@ def output_check(o_gpu: np.ndarray, o_ref: np.ndarray, valid: np.ndarray, dtype:
         worst = float((err.max(axis=-1) / np.maximum(allow, 1e-300)).max())
         worst = 0.0 if not np.isfinite(worst) and float(err.max()) == 0 else worst
     return worst <= 1.0, worst, float(err.max())
+
+
+def mask_words_to_set(words, nb: int):
+    """Kept blocks of a bitmask row (bit j % 32 of word j // 32)."""
+    w = np.asarray(words, dtype=np.int64) & 0xFFFFFFFF
+    return [j for j in range(nb) if (w[j >> 5] >> (j & 31)) & 1]
+
+
+def rerank_valid(sets, final, chat: np.ndarray, k: int, forced: Sequence[int], track_best: bool,
+                 gap: float = GAP) -> tuple:
+    """Checks a GPU re-rank run, given the kept set it logged for the initial
+    selection and every round, and the set it returned, on the oracle's
+    contributions: the initial set is a top-k by drift score and each round's
+    set a top-k by the round's scores against the previous logged set, both up
+    to a relative gap; the returned set is the last one, or with track-best one
+    of least J up to a relative 2 * gap. Returns (ok, reason)."""
+    nb = chat.shape[0]
+    fset = set(forced)
+    d2 = (chat * chat).sum(axis=1)
+
+    def topk_ok(s, score):
+        s = set(s)
+        if len(s) != k or not fset <= s:
+            return False
+        kept_nf = [score[j] for j in s if j not in fset]
+        dropped = [score[j] for j in range(nb) if j not in s]
+        if not kept_nf or not dropped:
+            return True
+        return max(dropped) <= min(kept_nf) + gap * float(np.abs(score).max())
+
+    if not topk_ok(sets[0], d2):
+        return False, "initial set is not the top-k by drift score"
+    for x in range(1, len(sets)):
+        prev = set(sets[x - 1])
+        drop = [j for j in range(nb) if j not in prev]
+        r = chat[drop].sum(axis=0) if drop else np.zeros(chat.shape[1])
+        g = np.array([2.0 * float(r @ chat[j]) + (d2[j] if j in prev else -d2[j])
+                      for j in range(nb)])
+        if not topk_ok(sets[x], g):
+            return False, f"round {x} is not the top-k of its scores"
+    js = [oracle.drift_j(chat, s) for s in sets]
+    if not track_best:
+        return (list(final) == list(sets[-1])), "returned set is not the last round's"
+    if list(final) not in [list(s) for s in sets]:
+        return False, "returned set is not one of the logged sets"
+    if oracle.drift_j(chat, final) > min(js) * (1 + 2 * gap) + 1e-30:
+        return False, "returned set is not of least J"
+    return True, ""

@@ -1233,6 +1233,86 @@ def test_drift_layer16_full_size_sampled(dev):
     check_sampled_attention(lay, data, o, rpn, cin, sample)
 
 
+def check_rerank(lay, vals, keep, rounds, track_best, force, contrib_g, rpn, cin, stat_g, log_g,
+                 rows_to_check):
+    """Every checked row: the logged sets replay as top-k choices on the
+    oracle's contributions, the returned set is the last one (or of least J),
+    and the reported J is the oracle's J of the returned set."""
+    q, k, v = vals
+    nb = lay.nblocks
+    forced = oracle.forced_blocks(lay, force)
+    rows = parity.csr_rows(rpn, cin)
+    words = (nb + 31) // 32
+    qbar_cache = {}
+    differ = 0
+    for (h, i) in rows_to_check:
+        if h not in qbar_cache:
+            qbar_cache[h] = oracle.pool(q[:, h:h + 1], lay)[0, 0]
+        chat, _, _ = oracle.drift_row(qbar_cache[h][i], k[0, h], v[0, h], lay)
+        r = h * nb + i
+        lg = log_g[r].reshape(rounds + 1, words)
+        sets = [parity.mask_words_to_set(lg[x], nb) for x in range(rounds + 1)]
+        ok, why = parity.rerank_valid(sets, rows[r], chat, int(keep[h]), forced, track_best)
+        assert ok, f"row {(h, i)}: {why}"
+        jref = oracle.drift_j(chat, rows[r])
+        assert abs(stat_g[r] - jref) <= 1e-4 * max(jref, 1e-30), (h, i, stat_g[r], jref)
+        kept_ref, _, _, _ = oracle.rerank_row(chat, int(keep[h]), rounds, forced, track_best)
+        differ += kept_ref != rows[r]
+    return differ
+
+
+def run_rerank(dev, lay, host, vals, keep, rounds, track_best, force, rows_to_check, label):
+    q, k, v = (to_dev(x, dev) for x in host)
+    contrib, score = bsgm.drift_scores(lay, q, k, v)
+    nb = lay.nblocks
+    rows = lay.batch * lay.heads * nb
+    log = torch.full((rows, rounds + 1, (nb + 31) // 32), -7, dtype=torch.int32, device=dev)
+    rule = bsgm.RERANK_TRACK_BEST if track_best else bsgm.RERANK
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    force=force, swap_log=log, restoration=rule)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    assert rpn[-1] == lay.batch * nb * int(np.sum(keep))
+    differ = check_rerank(lay, vals, keep, rounds, track_best, force, contrib.cpu().numpy(), rpn,
+                          cin, st.cpu().numpy(), log.cpu().numpy(), rows_to_check)
+    say(f"{label}: {len(rows_to_check)} rows checked, {differ} with sets other than the oracle's")
+    return rp, ci
+
+
+@pytest.mark.parametrize("rounds,track_best,force", [(5, True, False), (5, False, False),
+                                                     (10, True, True), (10, False, False)])
+def test_drift_rerank_layer16(dev, rounds, track_best, force):
+    """16 frames, 2 heads (176 key blocks, keep 35): re-rank rounds at 5 and 10
+    rounds with and without track-best (ReSS Table S3's arms); every row of
+    head 0 and the XCD boundary rows of head 1."""
+    w, data = preset(4, heads=2)
+    lay = w.layout
+    host = [data[n + "_bits"] for n in ("q", "k", "v")]
+    vals = (data["q"], data["k"], data["v"])
+    keep = data["keep"]
+    if force:
+        keep = np.maximum(keep, lay.frames + 3).astype(np.int32)
+    rows = [(0, i) for i in range(lay.nblocks)] + [(1, i) for i in xcd_boundary_rows(lay.nblocks)]
+    run_rerank(dev, lay, host, vals, keep, rounds, track_best, force, rows,
+               f"re-rank 16 frames, {rounds} rounds, track-best {track_best}, force {force}")
+
+
+@pytest.mark.parametrize("nb,frames", [(1100, 100), (61, 1)])
+def test_drift_rerank_wide_and_small_rows(dev, nb, frames):
+    """Rows of 1100 key blocks (a 100-frame layer's width, beyond what the
+    best-swap search holds) and a single ragged frame of 61 blocks of 64."""
+    if nb == 1100:
+        lay = custom_layout(frames, 1408, 1374, 128, heads=1)
+    else:
+        lay = custom_layout(1, 61 * 64, 61 * 64 - 40, 64, heads=1, dtype="f32")
+    assert lay.nblocks == nb
+    host, vals = random_inputs(lay, 55 + nb)
+    keep = np.array([max(4, nb // 5)], dtype=np.int32)
+    rows = [(0, i) for i in spread_rows(nb, 24)]
+    run_rerank(dev, lay, host, vals, keep, 5, True, False, rows, f"re-rank rows of {nb} blocks")
+
+
 # --------------------------------------------------------------------------
 # dense camera/register query rows
 # --------------------------------------------------------------------------

@@ -109,3 +109,32 @@ def test_objectives_disagree_somewhere():
         if not ok:
             return
     pytest.fail("renormalised runs all pass the dropped-sum rule")
+
+
+def test_rerank_rule_accepts_the_oracle_and_rejects_planted_mistakes():
+    rng = np.random.default_rng(44)
+    chat = rng.standard_normal((9, 3))
+    k = 4
+    for tb in (True, False):
+        kept, j, sets, js = oracle.rerank_row(chat, k, 5, (), track_best=tb)
+        ok, why = parity.rerank_valid(sets, kept, chat, k, (), tb)
+        assert ok, why
+    kept, j, sets, js = oracle.rerank_row(chat, k, 5, (), track_best=True)
+    # a round whose set is not its top-k: swap one kept block for a dropped one
+    bad = [list(s) for s in sets]
+    drop = [x for x in range(9) if x not in bad[2]]
+    bad[2] = sorted(bad[2][1:] + [drop[0]])
+    ok, _ = parity.rerank_valid(bad, bad[-1], chat, k, (), False)
+    assert not ok
+    # track-best returning the last set when an earlier one is better
+    worst = max(range(len(sets)), key=lambda x: js[x])
+    if js[worst] > min(js) * (1 + 1e-3):
+        ok, _ = parity.rerank_valid(sets, sets[worst], chat, k, (), True)
+        assert not ok
+    # the planted row of the oracle pins: J rises, track-best keeps round 1
+    from test_oracle_drift import PLANTED_RERANK
+    kept, j, sets, js = oracle.rerank_row(PLANTED_RERANK, 2, 3, track_best=True)
+    assert parity.rerank_valid(sets, kept, PLANTED_RERANK, 2, (), True)[0]
+    assert not parity.rerank_valid(sets, sets[-1], PLANTED_RERANK, 2, (), True)[0]
+    words = [sum(1 << j for j in s) for s in sets]
+    assert [parity.mask_words_to_set([w], 4) for w in words] == sets
