@@ -34,7 +34,10 @@ back ("cache_warm_gbs": the inputs may still sit in the L2 and Infinity
 caches) and after a 512 MiB write ("cold_hbm_gbs", the figure that speaks for
 HBM), each against its algorithmic bytes (real-token inputs read once, outputs
 written once); `workspace_mib` gives the device scratch of each call.
-`detail.attn_prepare_ms` is the fp16 copy of K alone (it runs beside the
+`detail.drift_100_frames` runs drift selection on the 100-frame layer (1 100
+key blocks per row): contributions materialised, five re-rank rounds with
+track-best, attention; the 16-frame drift layer also times re-rank rounds at
+5 and 10 rounds. `detail.attn_prepare_ms` is the fp16 copy of K alone (it runs beside the
 selection in the step), `attn_with_prepare_frac` the attention's roofline
 fraction with that time charged too, and `attn_rows_bf16_form` the rows the
 fp16-logit form handed to the bf16 form. `cpu_baseline` times the oracle on
@@ -364,6 +367,7 @@ def main():
             name: side_config(bsgm, workloads, torch, dev, name, flush=flush)
             for name in ("tiny_f32_1024tok", "vggt_layer_8f_s50", "vggt_layer_32f_s75",
                          "vggt_layer_100f_cdf", "vggt_layer_16f_drift")}
+        detail["drift_100_frames"] = drift_wide_layer(bsgm, workloads, torch, dev)
 
     out = {
         "metric": "block-sparse global attn effective TFLOP/s + ms/layer, 32 frames, 75% sparse",
@@ -508,6 +512,53 @@ def mib(nbytes: float) -> float:
     return round(nbytes / (1 << 20), 2)
 
 
+def drift_wide_layer(bsgm, workloads, torch, dev, reps: int = 3):
+    """Drift selection on the 100-frame layer (1 100 key blocks per row, 16 heads,
+    keep 220 = 80 % sparsity): contributions materialised in HBM, then five
+    re-rank rounds with track-best (the best-swap search holds rows of up to 512
+    blocks), then the attention over the kept blocks."""
+    w = workloads.config("vggt_layer_100f_cdf")
+    lay = w.layout
+    log("generating the 100-frame layer for drift selection")
+    data = workloads.generate(w)
+    q, k, v = (to_dev(data[n + "_bits"], dev) for n in ("q", "k", "v"))
+    del data
+    nb, rows = lay.nblocks, lay.batch * lay.heads * lay.nblocks
+    keep = [nb - int(round(0.8 * nb))] * lay.heads
+    contrib = torch.empty((lay.batch, lay.heads, nb, nb, 64), dtype=torch.float32, device=dev)
+    score = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsgm.workspace_bytes(lay, bsgm.DRIFT), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(bsgm.col_capacity(lay, bsgm.DRIFT, keep), dtype=torch.int32, device=dev)
+    aws = torch.empty(bsgm.attn_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+
+    def scores():
+        bsgm.drift_scores(lay, q, k, v, contrib=contrib, score=score, workspace=ws)
+
+    def select():
+        bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=5,
+                           row_ptr=row_ptr, col_idx=col_idx, want_stat=False,
+                           restoration=bsgm.RERANK_TRACK_BEST)
+
+    def attend():
+        bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o, workspace=aws)
+    sc_ms = gpu_ms(torch, scores, reps)
+    sel_ms = gpu_ms(torch, select, reps)
+    at_ms = gpu_ms(torch, attend, reps)
+    executed = int(row_ptr[-1].item())
+    out = {"keep_per_query_block": keep[0], "rounds": 5, "restoration": "re-rank, track-best",
+           "drift_scores_ms": round(sc_ms, 4), "drift_select_ms": round(sel_ms, 4),
+           "attn_ms": round(at_ms, 4), "ms_per_layer": round(sc_ms + sel_ms + at_ms, 4),
+           "executed_block_pairs": executed,
+           "scoring_memory_mib": mib(contrib.numel() * 4 + score.numel() * 4 + ws.numel()),
+           "attn_effective_tflops": round(executed * 4.0 * 128 * 128 * 64 / (at_ms * 1e-3) / 1e12,
+                                          2)}
+    del contrib, score, q, k, v, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5, flush=None):
     """Per-layer times of a preset: selection (drift scores + restoration for the
     drift preset) and attention, each timed over back-to-back launches. The
@@ -578,6 +629,15 @@ def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5, flush=Non
         out["drift_scores_ms"] = round(phase(
             "drift_scores", scores, 3 * tensor_real + chat_bytes + rows * nb * 4), 4)
         out["drift_select_ms"] = round(phase("drift_select", select, chat_bytes + csr_bytes), 4)
+        # the re-rank restoration rule at the round counts of ReSS Table S3
+        for rr_rounds in (5, 10):
+            def select_rr(rounds=rr_rounds):
+                bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                   force=w.force_frame_first_block, row_ptr=row_ptr,
+                                   col_idx=col_idx, want_stat=False,
+                                   restoration=bsgm.RERANK_TRACK_BEST)
+            out[f"rerank_track_best_{rr_rounds}_rounds_select_ms"] = round(
+                gpu_ms(torch, select_rr, reps), 4)
         sel = out["drift_scores_ms"] + out["drift_select_ms"]
         out["workspace_mib"] = {"drift_scores": mib(ws_bytes),
                                 "contributions_and_scores": mib(chat_bytes + 2 * rows * nb * 4)}
