@@ -81,7 +81,7 @@ int check_layout(const bsgm_layout* L, bsgm::Dims* d) {
 using bsgm::align256;
 
 struct WsLayout {
-  size_t qbar, kbar, counts, bitmask, stats, mz, vbar, fac, mhat, pdem, pexe, total;
+  size_t qbar, kbar, counts, bitmask, stats, mz, qsplit, vbar, fac, mhat, pdem, pexe, total;
 };
 
 int vasc_pairs(const bsgm::Dims& d) { return (d.nb + 1) / 2; }
@@ -130,6 +130,8 @@ WsLayout ws_layout(const bsgm::Dims& d, int mode) {
     off += align256((size_t)d.rows * d.nb * 2 * sizeof(float));
     w.mz = off;
     off += align256((size_t)d.rows * 2 * sizeof(float));
+    w.qsplit = off;   // bf16 hi, mid, lo terms of qbar
+    off += align256((size_t)d.rows * 3 * 64 * 2);
   }
   if (mode == BSGM_SEL_CDF) {
     w.counts = off;
@@ -252,7 +254,8 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   if (layout->dtype == BSGM_BF16) {
     char* base = static_cast<char*>(ws);
-    e = bsgm::launch_drift_contrib_bf16(d, qbar, k, v, reinterpret_cast<float2*>(base + w.stats),
+    e = bsgm::launch_drift_contrib_bf16(d, qbar, base + w.qsplit, k, v,
+                                        reinterpret_cast<float2*>(base + w.stats),
                                         reinterpret_cast<float2*>(base + w.mz), contrib, score,
                                         zmass, s);
   } else {

@@ -186,8 +186,11 @@ hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, con
 // LDS holds the contributions of D and S in slot order (D slots first, then S
 // slots; forced blocks never move and are not needed). A swap exchanges the two
 // slots' rows and updates r by -c_a + c_b. G over D x S does not depend on r:
-// when it fits it is computed once per row into LDS and a swap refreshes one
-// row and one column of it; otherwise every round recomputes the dot products.
+// when it fits it is computed once per row into LDS, on the matrix cores with
+// fp32 accuracy, and a swap refreshes one row and one column of it; g is then
+// updated in place (g'_j = g_j - <c_a, c_j> + <c_b, c_j>, all of whose terms
+// are old entries of G or products of the refresh). Otherwise every round
+// recomputes g and the pair products on the vector ALU.
 // ---------------------------------------------------------------------------
 struct DriftSelArgs {
   Dims d;
@@ -230,15 +233,17 @@ __device__ __forceinline__ float dot64(const P* x, const float* y) {
 
 // LDS carve-up of one row (byte offsets).
 struct DriftSelLds {
-  size_t cs, slot, keys, slot_of, zb, G, total;
+  size_t cs, slot, gs, keys, slot_of, zb, G, total;
 };
 
 __host__ __device__ inline DriftSelLds drift_sel_lds(int nb, int nslots, size_t gfloats) {
   DriftSelLds L;
   size_t o = 0;
   L.cs = o;      o += (size_t)nslots * kCs * 4;  // slot rows
-  L.slot = o;    o += (size_t)nslots * 16;       // per slot: |c|^2, weight, block, -
-  L.keys = o;    o += (size_t)nb * 8;            // priority keys by block
+  L.slot = o;    o += (size_t)nslots * 16;       // per slot: |c|^2, weight, block, mass
+  L.gs = o;      o += (size_t)nslots * 4;        // per slot: g = <r, x>
+  o = (o + 15) & ~(size_t)15;
+  L.keys = o;    o += (size_t)((nb + 1) & ~1) * 8;   // priority keys by block (even count)
   L.slot_of = o; o += (size_t)nb * 4;            // slot of each block (-1: forced)
   L.zb = o;      o += (size_t)nb * 4;            // normalised block mass (renorm)
   o = (o + 15) & ~(size_t)15;
@@ -259,6 +264,77 @@ __device__ __forceinline__ float renorm_j2(float rr, float dlt, float zs) {
   return zs > 0.f ? fmaxf(rr + dlt, 0.f) / (zs * zs) : INFINITY;
 }
 
+// Least 64-bit key over the wave (all lanes active), on the DPP and lane-swap
+// paths: every lane gets the minimum.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_min_u64(unsigned long long x) {
+  const uint32_t lo = dpp_mov_u<CTRL>((uint32_t)x), hi = dpp_mov_u<CTRL>((uint32_t)(x >> 32));
+  const unsigned long long y = ((unsigned long long)hi << 32) | lo;
+  return y < x ? y : x;
+}
+__device__ __forceinline__ unsigned long long wave_allmin_u64(unsigned long long x) {
+  x = dpp_min_u64<0xB1>(x);    // quad_perm [1,0,3,2]
+  x = dpp_min_u64<0x4E>(x);    // quad_perm [2,3,0,1]
+  x = dpp_min_u64<0x141>(x);   // row_half_mirror
+  x = dpp_min_u64<0x140>(x);   // row_mirror
+  {
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    const unsigned long long u = ((unsigned long long)h[0] << 32) | l[0];
+    const unsigned long long v = ((unsigned long long)h[1] << 32) | l[1];
+    x = u < v ? u : v;
+  }
+  {
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    const unsigned long long u = ((unsigned long long)h[0] << 32) | l[0];
+    const unsigned long long v = ((unsigned long long)h[1] << 32) | l[1];
+    x = u < v ? u : v;
+  }
+  return x;
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 sel_bf16x2;
+typedef __attribute__((ext_vector_type(2))) float sel_f32x2;
+
+// x = hi + mid + lo exactly, each a bf16 (barring subnormal residuals).
+__device__ __forceinline__ void sel_split3(const float (&x)[8], bf16x8& hi, bf16x8& mid,
+                                           bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const sel_f32x2 v = {x[2 * e], x[2 * e + 1]};
+    const sel_bf16x2 h = __builtin_convertvector(v, sel_bf16x2);
+    const sel_f32x2 r1 = v - __builtin_convertvector(h, sel_f32x2);
+    const sel_bf16x2 m = __builtin_convertvector(r1, sel_bf16x2);
+    const sel_f32x2 r2 = r1 - __builtin_convertvector(m, sel_f32x2);
+    const sel_bf16x2 l = __builtin_convertvector(r2, sel_bf16x2);
+    hi[2 * e] = h[0];
+    hi[2 * e + 1] = h[1];
+    mid[2 * e] = m[0];
+    mid[2 * e + 1] = m[1];
+    lo[2 * e] = l[0];
+    lo[2 * e + 1] = l[1];
+  }
+}
+
+// Head dims 32 ks + 8 (lane / 16) .. +7 of LDS slot row `row` (zeros when the
+// row is past `nrows`), split in three bf16 terms: one operand fragment of
+// v_mfma_f32_16x16x32_bf16 (lane l gives row or column l % 16).
+__device__ __forceinline__ void sel_frag(const float* cs, int row, int nrows, int ks, int lane,
+                                         bf16x8& h, bf16x8& m, bf16x8& l) {
+  float x[8];
+  if (row < nrows) {
+    const float4* p = reinterpret_cast<const float4*>(cs + row * kCs + 32 * ks + 8 * (lane >> 4));
+    const float4 u = p[0], v = p[1];
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+  sel_split3(x, h, m, l);
+}
+
 template <bool CACHE, int RR>
 __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
@@ -272,6 +348,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
   const DriftSelLds L = drift_sel_lds(nb, nsl, CACHE ? (size_t)nd * ns : 0);
   float* cs = reinterpret_cast<float*>(dsm + L.cs);
   SlotRec* slot = reinterpret_cast<SlotRec*>(dsm + L.slot);
+  float* gs = reinterpret_cast<float*>(dsm + L.gs);
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(dsm + L.keys);
   int* slot_of = reinterpret_cast<int*>(dsm + L.slot_of);
   float* zb = reinterpret_cast<float*>(dsm + L.zb);
@@ -315,18 +392,41 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
       }
     }
   }
+  if ((nb & 1) && t == 0) keys[nb] = 0ull;   // the even-count pad sorts below every key
   __syncthreads();
-  // initial kept set: the k keys of highest priority (keys are distinct)
+  // Initial kept set: the k keys of highest priority (forced, then norm, then
+  // lower block; keys are distinct). Block j is ranked against every key by
+  // threads j and j + 256 (half the keys each, two keys per LDS read) when
+  // nb <= 256, else by thread j alone.
   bool kept_j = false, forced_j = false;
   float cc_j = 0.f;
-  if (t < nb) {
-    const unsigned long long kj = keys[t];
+  {
+    const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(keys);
+    const int npair = (nb + 1) >> 1;
+    const bool split = nb <= kSelThreads / 2;
+    const int jr = split ? (t & (kSelThreads / 2 - 1)) : t;
+    const int q0 = split && t >= kSelThreads / 2 ? npair / 2 : 0;
+    const int q1 = split && t < kSelThreads / 2 ? npair / 2 : npair;
     int rank = 0;
-#pragma unroll 8
-    for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
-    kept_j = rank < k;
-    forced_j = a.force && block_forced(d, t);
-    cc_j = __int_as_float(slot_of[t]);
+    if (jr < nb) {
+      const unsigned long long kj = keys[jr];
+#pragma unroll 4
+      for (int q = q0; q < q1; ++q) {
+        const ulonglong2 p = k2[q];
+        rank += (p.x > kj ? 1 : 0) + (p.y > kj ? 1 : 0);
+      }
+    }
+    if (split) {
+      int* half = reinterpret_cast<int*>(&part[0][0]);
+      if (t >= kSelThreads / 2 && jr < nb) half[jr] = rank;
+      __syncthreads();
+      if (t < nb) rank += half[t];
+    }
+    if (t < nb) {
+      kept_j = rank < k;
+      forced_j = a.force && block_forced(d, t);
+      cc_j = __int_as_float(slot_of[t]);
+    }
   }
   // slots: dropped blocks ascending, then kept non-forced blocks ascending
   {
@@ -412,8 +512,9 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
     z_s = ztot - zd;
   }
 
-  // kTa x kTb tiles of <c_a, c_b>. Tile (ta, tb) takes D slots ta + x NTA and S
-  // slots tb + y NTB, so that neighbouring lanes read neighbouring LDS rows.
+  // kTa x kTb tiles of <c_a, c_b> on the vector ALU (rows too wide for the
+  // cached products). Tile (ta, tb) takes D slots ta + x NTA and S slots
+  // tb + y NTB, so that neighbouring lanes read neighbouring LDS rows.
   const int NTA = (nd + kTa - 1) / kTa, NTB = (ns + kTb - 1) / kTb, ntiles = NTA * NTB;
   auto tiles = [&](auto&& consume) {
     for (int tile = t; tile < ntiles; tile += kSelThreads) {
@@ -452,35 +553,83 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
     }
   };
 
-  // r = sum of the dropped contributions; G once per row when cached
+  // r = sum of the dropped rows; the cached G = <x_D, x_S> on the matrix cores:
+  // 16 x 16 tiles, each operand split into three bf16 terms (the six products
+  // above 2^-24 relative are summed in fp32). Wave w takes a contiguous run of
+  // the (S tile, D tile) pairs, S tile major, and rebuilds the S operand only
+  // when its S tile changes.
   {
-    float s = 0.f;
-    for (int x = w; x < nd; x += kSelWaves) s += cs[x * kCs + lane];
-    part[w][lane] = s;
+    float sacc = 0.f;
+    for (int x = w; x < nd; x += kSelWaves) sacc += cs[x * kCs + lane];
+    part[w][lane] = sacc;
   }
-  if (CACHE) tiles([&](int ai, int bi, float v) { G[ai * ns + bi] = v; });
+  if (CACHE) {
+    const int NTD = (nd + 15) >> 4, NTS = (ns + 15) >> 4, np = NTD * NTS;
+    const int p0 = w * np / kSelWaves, p1 = (w + 1) * np / kSelWaves;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    int cur = -1;
+    bf16x8 bh[2], bm[2], bl[2];
+    for (int p = p0; p < p1; ++p) {
+      const int tb = p / NTD, ta = p - tb * NTD;
+      if (tb != cur) {
+        cur = tb;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          sel_frag(cs + nd * kCs, 16 * tb + r16, ns, ks, lane, bh[ks], bm[ks], bl[ks]);
+      }
+      bf16x8 ah[2], am[2], al[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) sel_frag(cs, 16 * ta + r16, nd, ks, lane, ah[ks], am[ks], al[ks]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[ks], bm[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[ks], bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bm[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh[ks], acc, 0, 0, 0);
+      }
+      // lane l holds rows 4 (l / 16) + x of the D tile, column l % 16 of the S tile
+      const int bi = 16 * tb + r16;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int ai = 16 * ta + 4 * g4 + x;
+        if (ai < nd && bi < ns) G[ai * ns + bi] = acc[x];
+      }
+    }
+  }
   __syncthreads();
   if (t < 64) {
-    float s = 0.f;
+    float sacc = 0.f;
 #pragma unroll
-    for (int q = 0; q < kSelWaves; ++q) s += part[q][t];
-    rv[t] = renorm ? fmaf(1.f - ztot, ob[t], s) : s;
+    for (int q = 0; q < kSelWaves; ++q) sacc += part[q][t];
+    rv[t] = renorm ? fmaf(1.f - ztot, ob[t], sacc) : sacc;
   }
+  __syncthreads();
+
+  // g = <r, x> and the slot weights |x|^2 - 2 g (D) or |x|^2 + 2 g (S). With
+  // the cached G, later rounds update g in place: after restoring a and
+  // dropping b, r' = r - x_a + x_b, so g'_j = g_j - <x_a, x_j> + <x_b, x_j>,
+  // every term of which is an old entry of G or a product of the refresh.
+  auto weights = [&]() {
+    for (int sl = t; sl < nsl; sl += kSelThreads) {
+      const float g = dot64(rv, cs + sl * kCs);
+      gs[sl] = g;
+      slot[sl].wgt = sl < nd ? fmaf(-2.f, g, slot[sl].cc) : fmaf(2.f, g, slot[sl].cc);
+    }
+  };
+  weights();
   __syncthreads();
 
   float rr = 0.f;
   for (int round = 0;; ++round) {
-    {
-      const float x = rv[lane];
-      rr = wave_sum(x * x);
-    }
+    rr = wave_allsum(rv[lane] * rv[lane]);
     if (round == a.rounds) break;
-
-    for (int sl = t; sl < nsl; sl += kSelThreads) {
-      const float g = dot64(rv, cs + sl * kCs);
-      slot[sl].wgt = sl < nd ? slot[sl].cc - 2.f * g : slot[sl].cc + 2.f * g;
+    if (!CACHE && round > 0) {
+      weights();
+      __syncthreads();
     }
-    __syncthreads();
 
     // candidates ordered by (delta, a, b) as one 64-bit key
     unsigned long long best = ~0ull;
@@ -511,11 +660,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
         best = key < best ? key : best;
       });
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned long long other = __shfl_xor(best, o, 64);
-      best = other < best ? other : best;
-    }
+    best = wave_allmin_u64(best);
     if (lane == 0) bkey[w] = best;
     __syncthreads();
     best = bkey[0];
@@ -547,28 +692,61 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
         }
       break;   // r and rr describe the final drop set
     }
-    // restore ba (D slot pa) and drop bb (S slot sb): exchange the slots' rows
-    const int pa = slot_of[ba], sb = slot_of[bb], pb = sb - nd;
-    if (renorm) z_s += slot[pa].z - slot[sb].z;
-    __syncthreads();   // every wave is done with bkey, slot weights and G of this round
-    if (t < 64) {
-      const float ra = cs[pa * kCs + t], rb = cs[sb * kCs + t];
-      rv[t] = (rv[t] - ra) + rb;
-      cs[pa * kCs + t] = rb;
-      cs[sb * kCs + t] = ra;
-    } else if (t == 64) {
-      const SlotRec x = slot[pa];
-      slot[pa] = slot[sb];
-      slot[sb] = x;
-      slot_of[ba] = sb;
-      slot_of[bb] = pa;
+    // Restore ba (D slot pa) and drop bb (S slot sb): wave 0 exchanges the two
+    // slots' rows, records and g, and updates r by -x_a + x_b. No other wave
+    // reads slot_of, the rows or the records until the barrier below; after it
+    // ba sits in slot sb and bb in slot pa.
+    if (w == 0) {
+      const int pa = slot_of[ba], sb = slot_of[bb];
+      const float ra = cs[pa * kCs + lane], rb = cs[sb * kCs + lane];
+      rv[lane] = (rv[lane] - ra) + rb;
+      cs[pa * kCs + lane] = rb;
+      cs[sb * kCs + lane] = ra;
+      if (lane == 0) {
+        const SlotRec x = slot[pa];
+        slot[pa] = slot[sb];
+        slot[sb] = x;
+        const float gx = gs[pa];
+        gs[pa] = gs[sb];
+        gs[sb] = gx;
+        slot_of[ba] = sb;
+        slot_of[bb] = pa;
+      }
     }
     __syncthreads();
-    if (CACHE)
+    const int pa = slot_of[bb], sbs = slot_of[ba], pb = sbs - nd;
+    if (renorm) z_s += slot[sbs].z - slot[pa].z;
+    if (CACHE && round + 1 < a.rounds) {
+      // refresh row pa (now x_b) and column pb (now x_a) of G, and every g
+      // (not after the last round, whose products nothing reads)
       for (int x = t; x < ns + nd; x += kSelThreads) {
-        if (x < ns) G[pa * ns + x] = dot64(cs + pa * kCs, cs + (nd + x) * kCs);
-        else if (x - ns != pa) G[(x - ns) * ns + pb] = dot64(cs + (x - ns) * kCs, cs + sb * kCs);
+        if (x < ns) {
+          const int sl = nd + x;
+          const float nw = dot64(cs + pa * kCs, cs + sl * kCs);   // <x_b, x_s>
+          const float old = G[pa * ns + x];                       // <x_a, x_s>
+          G[pa * ns + x] = nw;
+          float g = gs[sl];
+          g = x == pb ? (g - slot[sl].cc) + old : (g - old) + nw;
+          gs[sl] = g;
+          slot[sl].wgt = fmaf(2.f, g, slot[sl].cc);
+        } else {
+          const int y = x - ns;
+          float g = gs[y];
+          if (y == pa) {
+            const float ab = dot64(cs + pa * kCs, cs + sbs * kCs);  // <x_b, x_a>
+            g = (g - ab) + slot[y].cc;
+          } else {
+            const float nw = dot64(cs + y * kCs, cs + sbs * kCs);   // <x_y, x_a>
+            const float old = G[y * ns + pb];                       // <x_y, x_b>
+            G[y * ns + pb] = nw;
+            g = (g - nw) + old;
+          }
+          gs[y] = g;
+          slot[y].wgt = fmaf(-2.f, g, slot[y].cc);
+        }
       }
+      __syncthreads();
+    }
   }
   if (t == 0 && a.row_stat) a.row_stat[r] = renorm ? sqrtf(rr) / z_s : sqrtf(rr);
 

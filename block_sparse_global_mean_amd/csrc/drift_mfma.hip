@@ -10,14 +10,18 @@
 // fp32 operand (qbar in the logits, the weights in the value sum) is split into
 // three bf16 terms whose sum is exactly the fp32 value (8 + 8 + 8 significant
 // bits), and K and V are bf16 already, so every product is exact and only the
-// fp32 accumulation rounds. Three launches:
+// fp32 accumulation rounds. Four launches:
+//   k_qbar_split    qbar as its three bf16 terms, once per row;
 //   k_drift_stats   per (query row i, key block j): block max m_ij and
 //                   z_ij = sum_{u in j} exp(l_iu - m_ij);
 //   k_drift_norm    per row: M_i = max_j m_ij, Z_i = sum_j z_ij exp(m_ij - M_i);
 //   k_drift_contrib per (i, j): the weights exp(l_iu - M_i) / Z_i, then
 //                   contrib = weights x V and its norm.
-// A workgroup owns two key blocks of one (b, h), stages their K (and V) tiles
-// in LDS once, and its four waves take the 32-row query tiles x key blocks.
+// In the second and fourth, one wave owns one key block of one (b, h) and a run
+// of 32-row query tiles: it loads the block's K fragments into registers once
+// (and, for the value sums, its V tile into a private LDS slice), then walks
+// its query tiles with no barrier, so the launches need no workgroup-wide
+// staging and the waves of a CU run independently.
 #include "device_util.h"
 
 namespace bsgm {
@@ -25,6 +29,7 @@ namespace bsgm {
 struct DriftMfmaArgs {
   Dims d;
   const float* qbar;     // [B*H*nb, 64]
+  __bf16* qsplit;        // [B*H*nb, 3, 64]: qbar as hi, mid, lo bf16 terms
   const __bf16* k;       // [B, H, N, 64]
   const __bf16* v;
   float2* stats;         // [B*H*nb, nb]: (m_ij, z_ij)
@@ -34,71 +39,101 @@ struct DriftMfmaArgs {
   float* zmass;          // [B*H*nb, nb] or null: sum over the block of exp(l - M) / Z
 };
 
-constexpr int kDriftBlocksPerWg = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// x = hi + mid + lo exactly, each a bf16 (barring subnormal residuals).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// x = hi + mid + lo exactly, each a bf16 (barring subnormal residuals): hi is x
+// rounded to bf16, mid the rounded remainder, lo what is left (at most 8
+// significant bits, so exact). Pairs of values convert in one instruction.
 __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = (__bf16)x[e];
-    const float r1 = x[e] - (float)h;
-    const __bf16 m = (__bf16)r1;
-    const float r2 = r1 - (float)m;
-    hi[e] = h;
-    mid[e] = m;
-    lo[e] = (__bf16)r2;
+  for (int e = 0; e < 4; ++e) {
+    const f32x2 v = {x[2 * e], x[2 * e + 1]};
+    const bf16x2 h = __builtin_convertvector(v, bf16x2);
+    const f32x2 r1 = v - __builtin_convertvector(h, f32x2);
+    const bf16x2 m = __builtin_convertvector(r1, bf16x2);
+    const f32x2 r2 = r1 - __builtin_convertvector(m, f32x2);
+    const bf16x2 l = __builtin_convertvector(r2, bf16x2);
+    hi[2 * e] = h[0];
+    hi[2 * e + 1] = h[1];
+    mid[2 * e] = m[0];
+    mid[2 * e + 1] = m[1];
+    lo[2 * e] = l[0];
+    lo[2 * e + 1] = l[1];
   }
 }
 
-// Copies BLK key rows (128 bytes each) of `src` into a swizzled LDS tile.
-template <int BLK, int NT>
-__device__ __forceinline__ void stage_tile(unsigned char* dst, const __bf16* src) {
+// qsplit rows: thread (row, c) splits head dims 8c .. 8c + 7 of qbar once, for
+// both per-(i, j) kernels.
+__global__ __launch_bounds__(256) void k_qbar_split(DriftMfmaArgs a) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= a.d.rows * 8) return;
+  const int row = x >> 3, c = x & 7;
+  const float4* p = reinterpret_cast<const float4*>(a.qbar + (size_t)row * 64 + 8 * c);
+  const float4 u = p[0], w = p[1];
+  const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+  bf16x8 h, m, l;
+  split3(v, h, m, l);
+  bf16x8* o = reinterpret_cast<bf16x8*>(a.qsplit + (size_t)row * 192 + 8 * c);
+  o[0] = h;
+  o[8] = m;
+  o[16] = l;
+}
+
+// K fragments of key block j, straight from global memory into registers: for
+// sub-tile t and head-dim step ks, lane l holds the 8 head dims 16 ks + 8 (l / 32)
+// .. +7 of key row 32 t + key_perm(l % 32) (the A operand of S^T = K Qbar^T,
+// the layout k_frag reads from an LDS tile).
+template <int KT>
+__device__ __forceinline__ void load_k_frags(const __bf16* kblk, int lane, bf16x8 (&kf)[KT][4]) {
 #pragma unroll
-  for (int q = threadIdx.x; q < BLK * 8; q += NT) {
-    const int row = q >> 3, pc = q & 7;
-    *reinterpret_cast<uint4*>(dst + row * 128 + ((pc ^ swz(row)) << 4)) =
-        *reinterpret_cast<const uint4*>(src + (size_t)row * 64 + pc * 8);
+  for (int t = 0; t < KT; ++t) {
+    const __bf16* rowp = kblk + (size_t)(32 * t + key_perm(lane & 31)) * 64 + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[t][ks] = *reinterpret_cast<const bf16x8*>(rowp + 16 * ks);
   }
 }
 
 // B operand of S^T = K Qbar^T for the query tile starting at row i0: lane l holds
-// query i0 + l % 32 and head dims 16 ks + 8 (l / 32) .. +7, split in three terms.
-__device__ __forceinline__ void load_qbar(const float* qbar_bh, int nb, int i0, int lane,
-                                          bf16x8 (&qh)[4], bf16x8 (&qm)[4], bf16x8 (&ql)[4]) {
+// query i0 + l % 32 and head dims 16 ks + 8 (l / 32) .. +7, as three bf16 terms.
+__device__ __forceinline__ void load_qsplit(const __bf16* qs_bh, int nb, int i0, int lane,
+                                            bf16x8 (&qh)[4], bf16x8 (&qm)[4], bf16x8 (&ql)[4]) {
   const int i = i0 + (lane & 31);
-  const bool ok = i < nb;
+  if (i < nb) {
+    const __bf16* p = qs_bh + (size_t)i * 192 + 8 * (lane >> 5);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    float x[8];
-    if (ok) {
-      const float4* p = reinterpret_cast<const float4*>(qbar_bh + (size_t)i * 64 + 16 * ks +
-                                                        8 * (lane >> 5));
-      const float4 a = p[0], b = p[1];
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int ks = 0; ks < 4; ++ks) {
+      qh[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks);
+      qm[ks] = *reinterpret_cast<const bf16x8*>(p + 64 + 16 * ks);
+      ql[ks] = *reinterpret_cast<const bf16x8*>(p + 128 + 16 * ks);
     }
-    split3(x, qh[ks], qm[ks], ql[ks]);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qh[ks][e] = (__bf16)0.f;
+        qm[ks][e] = (__bf16)0.f;
+        ql[ks][e] = (__bf16)0.f;
+      }
+    }
   }
 }
 
 // Raw dot products <qbar_i, k_u> of the 32 keys of sub-tile t (register x of
 // lane l: key 16 (x / 8) + 8 (l / 32) + x % 8, query l % 32).
-__device__ __forceinline__ f32x16 qk_tile(const unsigned char* kb, int t, int lane,
-                                          const bf16x8 (&qh)[4], const bf16x8 (&qm)[4],
-                                          const bf16x8 (&ql)[4]) {
+__device__ __forceinline__ f32x16 qk_tile(const bf16x8 (&kt)[4], const bf16x8 (&qh)[4],
+                                          const bf16x8 (&qm)[4], const bf16x8 (&ql)[4]) {
   f32x16 s;
 #pragma unroll
   for (int x = 0; x < 16; ++x) s[x] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 ka = k_frag(kb, t, ks, lane);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ql[ks], s, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qm[ks], s, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qh[ks], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks], ql[ks], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks], qm[ks], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks], qh[ks], s, 0, 0, 0);
   }
   return s;
 }
@@ -107,61 +142,101 @@ __device__ __forceinline__ int tile_key(int t, int x, int lane) {
   return 32 * t + 16 * (x >> 3) + 8 * (lane >> 5) + (x & 7);
 }
 
-template <int BLK>
-__global__ __launch_bounds__(256, 4) void k_drift_stats(DriftMfmaArgs a) {
-  constexpr int KT = BLK / 32, TB = BLK * 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kDriftBlocksPerWg * TB];
-  const Dims& d = a.d;
-  const int bh = blockIdx.y, j0 = kDriftBlocksPerWg * blockIdx.x;
-  const int nj = min(kDriftBlocksPerWg, d.nb - j0);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const size_t hoff = (size_t)bh * d.N * 64;
-  for (int jj = 0; jj < nj; ++jj)
-    stage_tile<BLK, 256>(smem + jj * TB, a.k + hoff + (size_t)(j0 + jj) * BLK * 64);
-  __syncthreads();
+// Work split of the two per-(i, j) kernels: one wave per (b, h, key block, run
+// of `rtpw` consecutive 32-row query tiles), so that a wave loads its key block
+// once and keeps it for all its query tiles. Waves are numbered
+// ((b*H + h) * nb + j) * nsplit + s; there is no barrier, and a wave past the
+// last item returns at once.
+struct WaveItem {
+  int bh, j, rt0, rt1;
+};
 
-  const float* qbar_bh = a.qbar + (size_t)bh * d.nb * 64;
-  const int nrt = (d.nb + 31) / 32;
-  for (int u = w; u < nrt * nj; u += 4) {
-    const int rt = u / nj, jj = u - rt * nj, j = j0 + jj;
-    bf16x8 qh[4], qm[4], ql[4];
-    load_qbar(qbar_bh, d.nb, 32 * rt, lane, qh, qm, ql);
-    const int vlen = block_vlen(d, j);
-    // one 32-key sub-tile at a time, merged online: (mx, z) over the real keys
-    const float c2 = d.scale * kLog2e;
-    float mx = -INFINITY, z = 0.f;
+__device__ __forceinline__ bool wave_item(const Dims& d, int rtpw, WaveItem& it) {
+  const int nrt = (d.nb + 31) / 32, nsplit = (nrt + rtpw - 1) / rtpw;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= d.B * d.H * d.nb * nsplit) return false;
+  const int s = gw % nsplit, bj = gw / nsplit;
+  it.bh = bj / d.nb;
+  it.j = bj - it.bh * d.nb;
+  it.rt0 = s * rtpw;
+  it.rt1 = min(nrt, it.rt0 + rtpw);
+  return true;
+}
+
+// Sets the scores of the padding keys of sub-tile t to -inf, when the sub-tile
+// straddles the end of the real keys (a wave-uniform test).
+__device__ __forceinline__ void mask_padding(f32x16& s, int t, int vlen, int lane) {
+  if (32 * t + 32 > vlen) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      if (32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
-      const f32x16 s = qk_tile(smem + jj * TB, t, lane, qh, qm, ql);
-      float mt = -INFINITY;
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (tile_key(t, x, lane) < vlen) mt = fmaxf(mt, s[x]);
-      {
-        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                         false, false);
-        mt = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-      }
-      const float mb = mt * c2;
-      float zt = 0.f;
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (tile_key(t, x, lane) < vlen) zt += __builtin_amdgcn_exp2f(fmaf(s[x], c2, -mb));
-      {
-        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(zt), __float_as_uint(zt),
-                                                         false, false);
-        zt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-      }
-      // every sub-tile before vlen holds a real key, so mt is finite
-      const float mn = fmaxf(mx, mt);
-      z = z * __builtin_amdgcn_exp2f((mx - mn) * c2) + zt * __builtin_amdgcn_exp2f((mt - mn) * c2);
-      mx = mn;
-    }
-    const int i = 32 * rt + (lane & 31);
-    if (lane < 32 && i < d.nb)
-      a.stats[((size_t)bh * d.nb + i) * d.nb + j] = make_float2(mx * d.scale, z);
+    for (int x = 0; x < 16; ++x) s[x] = tile_key(t, x, lane) < vlen ? s[x] : -INFINITY;
   }
+}
+
+// (m_ij, z_ij) of one 32-row query tile against the wave's key block. FULL:
+// the block has no padding keys; the products of the next 32-key sub-tile are
+// then issued before this sub-tile's softmax work, in one branch-free block,
+// so that the two overlap.
+template <int KT, bool FULL>
+__device__ __forceinline__ void stats_tile(const DriftMfmaArgs& a, const WaveItem& it, int rt,
+                                           int vlen, int lane, const bf16x8 (&kf)[KT][4]) {
+  const Dims& d = a.d;
+  bf16x8 qh[4], qm[4], ql[4];
+  load_qsplit(a.qsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  const float c2 = d.scale * kLog2e;
+  // one 32-key sub-tile at a time, merged online: (mx, z) over the real keys
+  float mx = -INFINITY, z = 0.f;
+  f32x16 s = qk_tile(kf[0], qh, qm, ql);
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (!FULL && 32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
+    f32x16 sn;
+    if (FULL && t + 1 < KT) sn = qk_tile(kf[t + 1], qh, qm, ql);
+    if (!FULL) {
+      if (t > 0) s = qk_tile(kf[t], qh, qm, ql);
+      mask_padding(s, t, vlen, lane);
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) mt = fmaxf(mt, s[x]);
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    }
+    const float mb = mt * c2;
+    float zt = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) zt += __builtin_amdgcn_exp2f(fmaf(s[x], c2, -mb));
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(zt), __float_as_uint(zt),
+                                                       false, false);
+      zt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    }
+    // every sub-tile before vlen holds a real key, so mt is finite
+    const float mn = fmaxf(mx, mt);
+    z = z * __builtin_amdgcn_exp2f((mx - mn) * c2) + zt * __builtin_amdgcn_exp2f((mt - mn) * c2);
+    mx = mn;
+    if (FULL && t + 1 < KT) s = sn;
+  }
+  const int i = 32 * rt + (lane & 31);
+  if (lane < 32 && i < d.nb)
+    a.stats[((size_t)it.bh * d.nb + i) * d.nb + it.j] = make_float2(mx * d.scale, z);
+}
+
+template <int BLK>
+__global__ __launch_bounds__(256, 3) void k_drift_stats(DriftMfmaArgs a, int rtpw) {
+  constexpr int KT = BLK / 32;
+  const Dims& d = a.d;
+  WaveItem it;
+  if (!wave_item(d, rtpw, it)) return;
+  const int lane = threadIdx.x & 63;
+  bf16x8 kf[KT][4];
+  load_k_frags<KT>(a.k + ((size_t)it.bh * d.N + (size_t)it.j * BLK) * 64, lane, kf);
+  const int vlen = block_vlen(d, it.j);
+  if (vlen == BLK)
+    for (int rt = it.rt0; rt < it.rt1; ++rt) stats_tile<KT, true>(a, it, rt, vlen, lane, kf);
+  else
+    for (int rt = it.rt0; rt < it.rt1; ++rt) stats_tile<KT, false>(a, it, rt, vlen, lane, kf);
 }
 
 // One wave per pooled query row.
@@ -182,130 +257,225 @@ __global__ __launch_bounds__(256) void k_drift_norm(DriftMfmaArgs a) {
   if (lane == 0) a.mz[r] = make_float2(m * kLog2e, 1.f / z);
 }
 
-template <int BLK>
-__global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a) {
-  constexpr int KT = BLK / 32, TB = BLK * 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kDriftBlocksPerWg * 2 * TB];
+// contrib, score (and zmass when ZM) of one 32-row query tile against the
+// wave's key block, whose V tile sits in LDS at vb. FULL: the block has no
+// padding keys, and the score products of the next sub-tile are issued before
+// this sub-tile's weights, as in stats_tile. Otherwise sub-tiles that hold only
+// padding keys (weights all zero) are skipped.
+template <int KT, bool ZM, bool FULL>
+__device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveItem& it, int rt,
+                                             int vlen, int lane, const bf16x8 (&kf)[KT][4],
+                                             const unsigned char* vb) {
   const Dims& d = a.d;
-  const int bh = blockIdx.y, j0 = kDriftBlocksPerWg * blockIdx.x;
-  const int nj = min(kDriftBlocksPerWg, d.nb - j0);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
-  const size_t hoff = (size_t)bh * d.N * 64;
-  for (int jj = 0; jj < nj; ++jj) {
-    stage_tile<BLK, 256>(smem + (2 * jj) * TB, a.k + hoff + (size_t)(j0 + jj) * BLK * 64);
-    stage_tile<BLK, 256>(smem + (2 * jj + 1) * TB, a.v + hoff + (size_t)(j0 + jj) * BLK * 64);
-  }
-  __syncthreads();
-
-  const float* qbar_bh = a.qbar + (size_t)bh * d.nb * 64;
+  const int i = 32 * rt + n;
+  const int j = it.j, bh = it.bh;
+  bf16x8 qh[4], qm[4], ql[4];
+  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  const float2 mz = i < d.nb ? a.mz[(size_t)bh * d.nb + i] : make_float2(0.f, 0.f);
   const float c2 = d.scale * kLog2e;
-  const int nrt = (d.nb + 31) / 32;
-  for (int u = w; u < nrt * nj; u += 4) {
-    const int rt = u / nj, jj = u - rt * nj, j = j0 + jj;
-    const unsigned char* kb = smem + (2 * jj) * TB;
-    const unsigned char* vb = kb + TB;
-    const int i = 32 * rt + n;
-    bf16x8 qh[4], qm[4], ql[4];
-    load_qbar(qbar_bh, d.nb, 32 * rt, lane, qh, qm, ql);
-    const float2 mz = i < d.nb ? a.mz[(size_t)bh * d.nb + i] : make_float2(0.f, 0.f);
-    const int vlen = block_vlen(d, j);
 
-    // c[mt]: rows = queries 8 (x / 4) + 4 (l / 32) + x % 4 of the tile, column =
-    // head dim 32 mt + l % 32.
-    f32x16 c[2];
+  // c[mt]: rows = queries 8 (x / 4) + 4 (l / 32) + x % 4 of the tile, column =
+  // head dim 32 mt + l % 32.
+  f32x16 c[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
-    float wsum = 0.f;
+    for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
+  float wsum = 0.f;
+  f32x16 s = qk_tile(kf[0], qh, qm, ql);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const f32x16 s = qk_tile(kb, t, lane, qh, qm, ql);
+  for (int t = 0; t < KT; ++t) {
+    if (!FULL && 32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
+    f32x16 sn;
+    if (FULL && t + 1 < KT) sn = qk_tile(kf[t + 1], qh, qm, ql);
+    if (!FULL) {
+      if (t > 0) s = qk_tile(kf[t], qh, qm, ql);
+      mask_padding(s, t, vlen, lane);   // exp2(-inf) = 0: padding keys weigh nothing
+    }
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float p[8];
+    for (int e = 0; e < 2; ++e) {
+      float p[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float wgt = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mz.x)) * mz.y;
-          p[x] = tile_key(t, 8 * e + x, lane) < vlen ? wgt : 0.f;
-          wsum += p[x];
-        }
-        bf16x8 ph, pm, pl;
-        split3(p, ph, pm, pl);
+      for (int x = 0; x < 8; ++x) {
+        p[x] = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mz.x)) * mz.y;
+        if (ZM) wsum += p[x];
+      }
+      bf16x8 ph, pm, pl;
+      split3(p, ph, pm, pl);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 vf = v_frag(vb, 32 * t + 16 * e, mt, lane);
-          c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vf, c[mt], 0, 0, 0);
-          c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, vf, c[mt], 0, 0, 0);
-          c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, vf, c[mt], 0, 0, 0);
-        }
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 vf = v_frag(vb, 32 * t + 16 * e, mt, lane);
+        c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vf, c[mt], 0, 0, 0);
+        c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, vf, c[mt], 0, 0, 0);
+        c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, vf, c[mt], 0, 0, 0);
       }
     }
+    if (FULL && t + 1 < KT) s = sn;
+  }
 
-    // contrib rows: lanes 0-31 write 128 contiguous bytes of one query row,
-    // lanes 32-63 those of the row 4 below.
-    float* out = a.contrib + (((size_t)bh * d.nb) * d.nb + j) * 64;
-    const size_t rs = (size_t)d.nb * 64;
+  // contrib rows: lanes 0-31 write 128 contiguous bytes of one query row,
+  // lanes 32-63 those of the row 4 below. The (b, h, j) base is wave-uniform
+  // and one (b, h)'s rows span nb^2 * 64 floats (< 2^30 for nb < 4096), so
+  // lanes address with 32-bit offsets from it.
+  const uint32_t rs = (uint32_t)d.nb * 64u;
+  float* base = a.contrib + ((size_t)bh * d.nb * d.nb + j) * 64;
+  const uint32_t off0 = (uint32_t)(32 * rt + 4 * hh) * rs + (uint32_t)n;
+  if (32 * rt + 32 <= d.nb) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int qi = 32 * rt + 8 * (x >> 2) + 4 * hh + (x & 3);
-      if (qi < d.nb) {
-        out[qi * rs + n] = c[0][x];
-        out[qi * rs + 32 + n] = c[1][x];
+      const uint32_t o = off0 + (uint32_t)(8 * (x >> 2) + (x & 3)) * rs;
+      base[o] = c[0][x];
+      base[o + 32u] = c[1][x];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int r = 8 * (x >> 2) + (x & 3);
+      if (32 * rt + 4 * hh + r < d.nb) {
+        const uint32_t o = off0 + (uint32_t)r * rs;
+        base[o] = c[0][x];
+        base[o + 32u] = c[1][x];
       }
     }
+  }
 
-    // score: sum of squares over the 64 head dims (32 lanes x 2 tiles) of each
-    // of the 16 rows a lane holds. Halving exchanges leave lane n with the
-    // total of row x = 8 b4 + 4 b3 + 2 b2 + b1 (b_k = bit k of n).
-    float v[16];
+  // score: sum of squares over the 64 head dims (32 lanes x 2 tiles) of each
+  // of the 16 rows a lane holds. Halving exchanges leave lane n with the
+  // total of row x = 8 b4 + 4 b3 + 2 b2 + b1 (b_k = bit k of n).
+  float v[16];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) v[x] = c[0][x] * c[0][x] + c[1][x] * c[1][x];
+  for (int x = 0; x < 16; ++x) v[x] = c[0][x] * c[0][x] + c[1][x] * c[1][x];
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      const int msk = 16 >> step, half = 8 >> step;
-      const bool up = (n & msk) != 0;
+  for (int step = 0; step < 4; ++step) {
+    const int msk = 16 >> step, half = 8 >> step;
+    const bool up = (n & msk) != 0;
 #pragma unroll
-      for (int k2 = 0; k2 < half; ++k2) {
-        const float send = up ? v[k2] : v[k2 + half];
-        const float keep = up ? v[k2 + half] : v[k2];
-        v[k2] = keep + __shfl_xor(send, msk, 64);
-      }
+    for (int k2 = 0; k2 < half; ++k2) {
+      const float send = up ? v[k2] : v[k2 + half];
+      const float keep = up ? v[k2 + half] : v[k2];
+      v[k2] = keep + __shfl_xor(send, msk, 64);
     }
-    v[0] += __shfl_xor(v[0], 1, 64);
-    const int xr = (((n >> 4) & 1) << 3) | (((n >> 3) & 1) << 2) | (((n >> 2) & 1) << 1) |
-                   ((n >> 1) & 1);
-    const int qi = 32 * rt + 8 * (xr >> 2) + 4 * hh + (xr & 3);
-    if ((n & 1) == 0 && qi < d.nb)
-      a.score[((size_t)bh * d.nb + qi) * d.nb + j] = sqrtf(v[0]);
-    if (a.zmass) {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsum), __float_as_uint(wsum),
-                                                       false, false);
-      const float zt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-      if (hh == 0 && i < d.nb) a.zmass[((size_t)bh * d.nb + i) * d.nb + j] = zt;
-    }
+  }
+  v[0] += __shfl_xor(v[0], 1, 64);
+  const int xr = (((n >> 4) & 1) << 3) | (((n >> 3) & 1) << 2) | (((n >> 2) & 1) << 1) |
+                 ((n >> 1) & 1);
+  const int qi = 32 * rt + 8 * (xr >> 2) + 4 * hh + (xr & 3);
+  if ((n & 1) == 0 && qi < d.nb)
+    a.score[((size_t)bh * d.nb + qi) * d.nb + j] = sqrtf(v[0]);
+  if (ZM) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsum), __float_as_uint(wsum),
+                                                     false, false);
+    const float zt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    if (hh == 0 && i < d.nb) a.zmass[((size_t)bh * d.nb + i) * d.nb + j] = zt;
   }
 }
 
-hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, const void* k,
+// Each wave transposes its block's V through a private LDS tile (swizzled
+// 128-byte rows, read back with the transposing LDS reads of v_frag) and keeps
+// its K fragments in registers.
+template <int BLK, bool ZM>
+__global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a, int rtpw) {
+  constexpr int KT = BLK / 32, TB = BLK * 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+  const Dims& d = a.d;
+  WaveItem it;
+  if (!wave_item(d, rtpw, it)) return;
+  const int lane = threadIdx.x & 63;
+  unsigned char* vb = smem + (threadIdx.x >> 6) * TB;
+  const size_t tok0 = (size_t)it.bh * d.N + (size_t)it.j * BLK;
+  {
+    const __bf16* src = a.v + tok0 * 64;
+#pragma unroll
+    for (int m = 0; m < BLK / 8; ++m) {
+      const int q = lane + 64 * m, row = q >> 3, pc = q & 7;
+      *reinterpret_cast<uint4*>(vb + row * 128 + ((pc ^ swz(row)) << 4)) =
+          *reinterpret_cast<const uint4*>(src + (size_t)row * 64 + pc * 8);
+    }
+  }
+  bf16x8 kf[KT][4];
+  load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
+  const int vlen = block_vlen(d, it.j);
+  // (the pipelined form needs 16 more registers than the zmass variant has)
+  if (vlen == BLK && !ZM)
+    for (int rt = it.rt0; rt < it.rt1; ++rt) contrib_tile<KT, ZM, true>(a, it, rt, vlen, lane, kf, vb);
+  else
+    for (int rt = it.rt0; rt < it.rt1; ++rt) contrib_tile<KT, ZM, false>(a, it, rt, vlen, lane, kf, vb);
+}
+
+// Query tiles per wave for `slots` resident waves on the chip: among the
+// choices of least makespan (query tiles per slot, counting whole rounds of
+// resident waves), the most tiles per wave, which loads each key block the
+// fewest times.
+static int tiles_per_wave(const Dims& d, int slots) {
+  const int nrt = (d.nb + 31) / 32;
+  const long long bjs = (long long)d.B * d.H * d.nb;
+  long long best_span = -1;
+  int best = nrt;
+  for (int r = nrt; r >= 1; --r) {
+    const long long waves = bjs * ((nrt + r - 1) / r);
+    const long long span = ((waves + slots - 1) / slots) * r;
+    if (best_span < 0 || span < best_span) {
+      best_span = span;
+      best = r;
+    }
+  }
+  return best;
+}
+
+static int compute_units() {
+  static int cu = 0;
+  if (cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cu = n;
+    else
+      cu = 256;
+  }
+  return cu;
+}
+
+hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
                                      const void* v, float2* stats, float2* mz, float* contrib,
                                      float* score, float* zmass, hipStream_t s) {
-  DriftMfmaArgs a{d, qbar, (const __bf16*)k, (const __bf16*)v, stats, mz, contrib, score, zmass};
-  const dim3 grid((d.nb + kDriftBlocksPerWg - 1) / kDriftBlocksPerWg, d.B * d.H);
-  if (d.blk == 128)
-    hipLaunchKernelGGL(k_drift_stats<128>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_drift_stats<64>, grid, dim3(256), 0, s, a);
+  DriftMfmaArgs a{d, qbar, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, stats, mz, contrib,
+                  score, zmass};
+  const int nrt = (d.nb + 31) / 32;
+  const int cu = compute_units();
+  const long long bjs = (long long)d.B * d.H * d.nb;
+  hipLaunchKernelGGL(k_qbar_split, dim3((d.rows * 8 + 255) / 256), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    // stats: 3 waves per SIMD
+    const int r = tiles_per_wave(d, cu * 12);
+    const long long waves = bjs * ((nrt + r - 1) / r);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (d.blk == 128)
+      hipLaunchKernelGGL(k_drift_stats<128>, grid, dim3(256), 0, s, a, r);
+    else
+      hipLaunchKernelGGL(k_drift_stats<64>, grid, dim3(256), 0, s, a, r);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_drift_norm, dim3((d.rows + 3) / 4), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (d.blk == 128)
-    hipLaunchKernelGGL(k_drift_contrib_mfma<128>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_drift_contrib_mfma<64>, grid, dim3(256), 0, s, a);
+  {
+    // contributions: 2 waves per SIMD
+    const int r = tiles_per_wave(d, cu * 8);
+    const long long waves = bjs * ((nrt + r - 1) / r);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    const bool zm = zmass != nullptr;
+    if (d.blk == 128) {
+      if (zm) hipLaunchKernelGGL((k_drift_contrib_mfma<128, true>), grid, dim3(256), 0, s, a, r);
+      else hipLaunchKernelGGL((k_drift_contrib_mfma<128, false>), grid, dim3(256), 0, s, a, r);
+    } else {
+      if (zm) hipLaunchKernelGGL((k_drift_contrib_mfma<64, true>), grid, dim3(256), 0, s, a, r);
+      else hipLaunchKernelGGL((k_drift_contrib_mfma<64, false>), grid, dim3(256), 0, s, a, r);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, con
 
 // The same on the matrix cores for bf16 K and V (fp32-accurate via split
 // operands). stats: [rows, nb] float2 scratch; mz: [rows] float2 scratch.
-hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, const void* k,
+hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
                                      const void* v, float2* stats, float2* mz, float* contrib,
                                      float* score, float* zmass, hipStream_t s);
 

@@ -50,7 +50,10 @@ def test_workspace_sizes():
     assert ws(lay, bsgm.TOPK) == 2 * rows * 64 * 4
     nb = 8
     al = lambda x: (x + 255) // 256 * 256
-    assert ws(lay, bsgm.DRIFT) == rows * 64 * 4 + al(rows * nb * 8) + al(rows * 8)
+    # pooled q; per (row, block): max and mass; per row: M and 1/Z; per row: the
+    # three bf16 terms of the pooled query
+    assert ws(lay, bsgm.DRIFT) == (rows * 64 * 4 + al(rows * nb * 8) + al(rows * 8)
+                                   + al(rows * 3 * 64 * 2))
     assert ws(lay, bsgm.CDF) == 2 * rows * 64 * 4 + 256 + 256
     # pooled q, k, v; per (b, h) and pair: factor and memory copy; per row and
     # pair: demand and execution (4 pairs of 8 blocks)

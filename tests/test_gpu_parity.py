@@ -1127,6 +1127,39 @@ def test_drift_512_blocks_uncached_search(dev):
     say(f"drift 512: sampled rows whose final set differs from the oracle's own run: {differ}")
 
 
+@pytest.mark.parametrize("objective", [oracle.RAW, oracle.RENORM])
+def test_drift_wide_rows_cached_search(dev, objective):
+    """Rows of 333 key blocks (more than 256, an odd count), 60 kept of which
+    37 forced (one per frame), two heads: every block is ranked by one thread
+    against every key, and the D x S products (273 x 23, 25 KB) still fit in
+    LDS beside the rows, so they are computed once per row on the matrix cores
+    and refreshed after each swap."""
+    lay = custom_layout(37, 576, 550, 64, heads=2, dtype="bf16")
+    host, vals = random_inputs(lay, 67)
+    nb = lay.nblocks
+    assert nb == 333
+    keep = np.array([60, 60], dtype=np.int32)
+    rounds = 4
+    say(f"drift wide rows: nb {nb}, keep {keep.tolist()}, objective {objective}")
+    q, k, v = (to_dev(x, dev) for x in host)
+    zmass = None
+    if objective == oracle.RENORM:
+        zmass = torch.empty((1, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v, zmass=zmass)
+    log = torch.full((lay.heads * nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    force=True, objective=objective, zmass=zmass, swap_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    rows = [(h, i) for h in range(lay.heads) for i in (0, 1, 100, 255, 256, 257, 332)]
+    differ = check_drift(lay, vals, keep, rounds, True, contrib.cpu().numpy(),
+                         score.cpu().numpy(), rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows,
+                         objective=objective,
+                         zmass_g=None if zmass is None else zmass.cpu().numpy())
+    say(f"drift wide rows: sampled rows whose final set differs from the oracle's own run: {differ}")
+
+
 # renormalised objective: the output shift once dropped blocks are removed
 @pytest.mark.parametrize("dtype,block,force", [("bf16", 64, False), ("bf16", 128, True),
                                                ("f32", 64, True), ("f32", 128, False)])
