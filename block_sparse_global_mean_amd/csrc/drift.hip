@@ -852,8 +852,10 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
   uint32_t* cur = reinterpret_cast<uint32_t*>(keys + nb);   // kept flags, WP words
   uint32_t* best = cur + WP;
   __shared__ __attribute__((aligned(16))) float rv[64];
+  __shared__ __attribute__((aligned(16))) float tot[64];
   __shared__ __attribute__((aligned(16))) float part[kRrThreads / 64][64];
   __shared__ float red[kRrThreads / 64];
+  __shared__ int cnt[2][kRrThreads / 64];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, grp = t >> 4, c4 = t & 15;
   const float4* row =
       reinterpret_cast<const float4*>(a.contrib + ((size_t)bh * nb + i) * (size_t)nb * 64);
@@ -866,43 +868,120 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
     return s;
   };
 
-  for (int j = grp; j < nb; j += kRrThreads / 16) {
-    const float4 x = row[(size_t)j * 16 + c4];
-    const float s = sum16(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
-    if (c4 == 0) cc[j] = s;
+  // squared norms, and the total o = sum_j c_j of the row
+  {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = grp; j < nb; j += kRrThreads / 16) {
+      const float4 x = row[(size_t)j * 16 + c4];
+      const float s = sum16(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
+      if (c4 == 0) cc[j] = s;
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      acc.x += __shfl_xor(acc.x, o, 64); acc.y += __shfl_xor(acc.y, o, 64);
+      acc.z += __shfl_xor(acc.z, o, 64); acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    if (lane < 16) *reinterpret_cast<float4*>(&part[w][4 * lane]) = acc;
+    __syncthreads();
+    if (t < 64) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int q = 0; q < kRrThreads / 64; ++q) sacc += part[q][t];
+      tot[t] = sacc;
+    }
   }
   __syncthreads();
 
-  // cur := the forced blocks plus the top k of score (ties: lower block)
-  auto select = [&](const float* score) {
-    for (int j = t; j < nb; j += kRrThreads) {
-      const bool f = a.force && block_forced(d, j);
-      const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(score[j]);
-      keys[j] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
-    }
-    __syncthreads();
-    for (int j0 = 64 * w; j0 < WP * 32; j0 += kRrThreads) {
+  // cur := the forced blocks plus the top k of score (ties: lower block).
+  // Rows of up to 512 blocks count each block's rank against every key; wider
+  // rows find the k-th largest 32-bit priority T by an MSB-first search (one
+  // block-wide count per bit), then keep every block above T and the lowest
+  // blocks at T.
+  auto hikey = [&](const float* score, int j) -> uint32_t {
+    return (a.force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(score[j]);
+  };
+  int pass = 0;
+  // number of blocks whose priority is at least cand (every thread; one barrier)
+  auto count_ge = [&](const float* score, uint32_t cand) {
+    int c = 0;
+    for (int j0 = 64 * w; j0 < nb; j0 += kRrThreads) {
       const int j = j0 + lane;
-      bool in = false;
-      if (j < nb) {
-        const unsigned long long kj = keys[j];
-        int rank = 0;
-        for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
-        in = rank < k;
+      c += __popcll(__ballot(j < nb && hikey(score, j) >= cand));
+    }
+    if (lane == 0) cnt[pass & 1][w] = c;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int q = 0; q < kRrThreads / 64; ++q) total += cnt[pass & 1][q];
+    ++pass;
+    return total;
+  };
+  auto select = [&](const float* score) {
+    if (nb <= 512) {
+      for (int j = t; j < nb; j += kRrThreads) {
+        const bool f = a.force && block_forced(d, j);
+        const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(score[j]);
+        keys[j] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
       }
+      __syncthreads();
+      for (int j0 = 64 * w; j0 < WP * 32; j0 += kRrThreads) {
+        const int j = j0 + lane;
+        bool in = false;
+        if (j < nb) {
+          const unsigned long long kj = keys[j];
+          int rank = 0;
+          for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
+          in = rank < k;
+        }
+        const unsigned long long m = __ballot(in);
+        if (lane == 0) {
+          cur[j0 >> 5] = (uint32_t)m;
+          cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
+        }
+      }
+      __syncthreads();
+      return;
+    }
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      if (count_ge(score, cand) >= k) T = cand;
+    }
+    int need = k - (T == 0xFFFFFFFFu ? 0 : count_ge(score, T + 1u));
+    for (int base = 0; base < nb; base += kRrThreads) {
+      const int j0 = base + 64 * w, j = j0 + lane;
+      const uint32_t hk = j < nb ? hikey(score, j) : 0u;
+      const bool tie = j < nb && hk == T;
+      const unsigned long long tm = __ballot(tie);
+      if (lane == 0) cnt[pass & 1][w] = __popcll(tm);
+      __syncthreads();
+      int before = 0, ties = 0;
+#pragma unroll
+      for (int q = 0; q < kRrThreads / 64; ++q) {
+        const int c = cnt[pass & 1][q];
+        before += q < w ? c : 0;
+        ties += c;
+      }
+      ++pass;
+      const bool in = j < nb && (hk > T || (tie && before + lanes_below(tm) < need));
       const unsigned long long m = __ballot(in);
-      if (lane == 0) {
+      if (lane == 0 && j0 < WP * 32) {
         cur[j0 >> 5] = (uint32_t)m;
         cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
       }
+      need -= min(need, ties);
     }
     __syncthreads();
   };
-  // rv := r, the sum of the dropped contributions; returns ||r||^2 (every thread)
+  // rv := r, the sum of the dropped contributions; returns ||r||^2 (every thread).
+  // When fewer blocks are kept than dropped, r = o - (sum of the kept rows), which
+  // reads the smaller set.
+  const bool via_kept = k < nb - k;
   auto residual = [&]() {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = grp; j < nb; j += kRrThreads / 16)
-      if (!kept(cur, j)) {
+      if (kept(cur, j) == via_kept) {
         const float4 x = row[(size_t)j * 16 + c4];
         acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
       }
@@ -917,6 +996,7 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
       float s = 0.f;
 #pragma unroll
       for (int q = 0; q < kRrThreads / 64; ++q) s += part[q][t];
+      if (via_kept) s = tot[t] - s;
       rv[t] = s;
       s = wave_sum(s * s);
       if (t == 0) red[0] = s;

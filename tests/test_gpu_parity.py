@@ -1331,6 +1331,49 @@ def test_drift_rerank_layer16(dev, rounds, track_best, force):
                f"re-rank 16 frames, {rounds} rounds, track-best {track_best}, force {force}")
 
 
+@pytest.mark.parametrize("force", [False, True])
+def test_drift_rerank_wide_rows_exact_ties(dev, force):
+    """Rows of 528 key blocks (wider than 512, so the top-k comes from the
+    MSB-first priority search) in which the value rows of frames 24 to 47 are
+    zero: 264 blocks contribute exactly nothing and tie at score 0 in every
+    round. Keep is set so that the initial cut falls inside those ties, so the
+    lowest-block rule decides it; the initial set must equal the oracle's
+    exactly, and every round must replay as a valid top-k. With force, keep
+    equals the 48 forced blocks, which all tie at the top priority."""
+    lay = custom_layout(48, 1408, 1374, 128, heads=1)
+    assert lay.nblocks == 528
+    host, vals = random_inputs(lay, 71)
+    tok = np.arange(lay.tokens)
+    zero = (tok // lay.frame_len) >= 24
+    q, k, v = vals
+    v = v.copy()
+    v[:, :, zero] = 0
+    vals = (q, k, v)
+    host = list(host)
+    host[2] = workloads.bf16_bits_from_float(v)
+    nb = lay.nblocks
+    keep = np.array([lay.frames if force else 264 + 40], dtype=np.int32)
+    rounds = 3
+    rows = [(0, i) for i in (0, 5, 263, 264, 300, 527)]
+    label = f"re-rank exact ties, force {force}"
+    rp, ci = run_rerank(dev, lay, host, vals, keep, rounds, True, force, rows, label)
+    # the initial set, taken from the oracle's own run, must match exactly
+    qd, kd, vd = (to_dev(x, dev) for x in host)
+    contrib, _ = bsgm.drift_scores(lay, qd, kd, vd)
+    log = torch.full((nb, rounds + 1, (nb + 31) // 32), -7, dtype=torch.int32, device=dev)
+    bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds, force=force,
+                       swap_log=log, restoration=bsgm.RERANK_TRACK_BEST)
+    torch.cuda.synchronize()
+    lg = log.cpu().numpy()
+    forced = oracle.forced_blocks(lay, force)
+    qbar = oracle.pool(q[:, 0:1], lay)[0, 0]
+    for (_, i) in rows:
+        chat, _, _ = oracle.drift_row(qbar[i], k[0, 0], v[0, 0], lay)
+        _, _, sets, _ = oracle.rerank_row(chat, int(keep[0]), rounds, forced, True)
+        got = parity.mask_words_to_set(lg[i].reshape(rounds + 1, -1)[0], nb)
+        assert got == sorted(sets[0]), (i, len(got))
+
+
 @pytest.mark.parametrize("nb,frames", [(1100, 100), (61, 1)])
 def test_drift_rerank_wide_and_small_rows(dev, nb, frames):
     """Rows of 1100 key blocks (a 100-frame layer's width, beyond what the
