@@ -36,8 +36,8 @@ HBM), each against its algorithmic bytes (real-token inputs read once, outputs
 written once); `workspace_mib` gives the device scratch of each call.
 `detail.drift_100_frames` runs drift selection on the 100-frame layer (1 100
 key blocks per row): contributions materialised, five re-rank rounds with
-track-best, attention; the 16-frame drift layer also times re-rank rounds at
-5 and 10 rounds. `detail.attn_prepare_ms` is the fp16 copy of K alone (it runs beside the
+track-best (and, timed beside it, 3 best-swap rounds), attention; the
+16-frame drift layer also times re-rank rounds at 5 and 10 rounds. `detail.attn_prepare_ms` is the fp16 copy of K alone (it runs beside the
 selection in the step), `attn_with_prepare_frac` the attention's roofline
 fraction with that time charged too, and `attn_rows_bf16_form` the rows the
 fp16-logit form handed to the bf16 form. `cpu_baseline` times the oracle on
@@ -515,8 +515,8 @@ def mib(nbytes: float) -> float:
 def drift_wide_layer(bsgm, workloads, torch, dev, reps: int = 3):
     """Drift selection on the 100-frame layer (1 100 key blocks per row, 16 heads,
     keep 220 = 80 % sparsity): contributions materialised in HBM, then five
-    re-rank rounds with track-best (the best-swap search holds rows of up to 512
-    blocks), then the attention over the kept blocks."""
+    re-rank rounds with track-best, then the attention over the kept blocks;
+    the best-swap rule at 3 rounds is timed beside it."""
     w = workloads.config("vggt_layer_100f_cdf")
     lay = w.layout
     log("generating the 100-frame layer for drift selection")
@@ -543,12 +543,17 @@ def drift_wide_layer(bsgm, workloads, torch, dev, reps: int = 3):
 
     def attend():
         bsgm.sparse_attn_fwd(lay, q, k, v, row_ptr, col_idx, o=o, workspace=aws)
+    def select_best_swap():
+        bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=3,
+                           row_ptr=row_ptr, col_idx=col_idx, want_stat=False)
     sc_ms = gpu_ms(torch, scores, reps)
+    bs_ms = gpu_ms(torch, select_best_swap, reps)
     sel_ms = gpu_ms(torch, select, reps)
     at_ms = gpu_ms(torch, attend, reps)
     executed = int(row_ptr[-1].item())
     out = {"keep_per_query_block": keep[0], "rounds": 5, "restoration": "re-rank, track-best",
            "drift_scores_ms": round(sc_ms, 4), "drift_select_ms": round(sel_ms, 4),
+           "best_swap_3_rounds_select_ms": round(bs_ms, 4),
            "attn_ms": round(at_ms, 4), "ms_per_layer": round(sc_ms + sel_ms + at_ms, 4),
            "executed_block_pairs": executed,
            "scoring_memory_mib": mib(contrib.numel() * 4 + score.numel() * 4 + ws.numel()),

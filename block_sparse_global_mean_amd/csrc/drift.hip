@@ -211,7 +211,7 @@ constexpr int kTa = 3, kTb = 4;  // register tile of dot products: kTa D slots x
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 // float4 registers per thread that hold a whole row of contributions: RR = 8
-// for rows of up to 256 blocks, 16 up to kDriftMaxBlocks
+// for rows of up to 256 blocks, 16 up to kDriftLdsRowBlocks
 // Dynamic LDS a selection workgroup may take (the static arrays need < 4 KB).
 constexpr size_t kDriftSelLdsCap = 160 * 1024 - 6144;
 
@@ -768,6 +768,504 @@ __global__ __launch_bounds__(kSelThreads, 4) void k_select_drift(DriftSelArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Best-swap drift selection for rows wider than the LDS row cache holds
+// (more than 512 blocks). Same rule and swap machinery as k_select_drift; the
+// row of x stays in global memory (L2) and is gathered by block, LDS holds the
+// per-slot records, g, the block priorities and, when it fits, G over D x S.
+// The initial top k comes from an MSB-first search for the k-th largest 32-bit
+// priority (one block-wide count per bit) with ties at it taken lowest block
+// first. Pair products run on the matrix cores as in k_select_drift; without
+// the cached G every round recomputes them and g.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 256;
+constexpr int kWideWaves = kWideThreads / 64;
+
+struct DriftWideLds {
+  size_t slot, gs, hk, slot_of, zb, G, total;
+};
+
+__host__ __device__ inline DriftWideLds drift_wide_lds(int nb, int nslots, size_t gfloats) {
+  DriftWideLds L;
+  size_t o = 0;
+  L.slot = o;    o += (size_t)nslots * 16;       // per slot: |x|^2, weight, block, mass
+  L.gs = o;      o += (size_t)nslots * 4;        // per slot: g = <r, x>
+  L.hk = o;      o += (size_t)nb * 4;            // 32-bit priority of each block
+  L.slot_of = o; o += (size_t)nb * 4;            // slot of each block (-1: forced)
+  L.zb = o;      o += (size_t)nb * 4;            // normalised block mass (renorm)
+  o = (o + 15) & ~(size_t)15;
+  L.G = o;       o += gfloats * 4;               // G[D slot][S slot]
+  L.total = o;
+  return L;
+}
+
+// The swap rows of one selection row, read from global memory by block:
+// x_j = c_j (dropped-sum drift) or z_j o - c_j (renormalised objective, o and
+// z in LDS).
+struct XRow {
+  const float* crow;   // contributions of the row, [nb, 64]
+  const float* zb;     // renorm: z_j
+  const float* ob;     // renorm: o
+  bool renorm;
+
+  __device__ __forceinline__ float4 x4(int j, int c4) const {
+    const float4 v = reinterpret_cast<const float4*>(crow + (size_t)j * 64)[c4];
+    if (!renorm) return v;
+    const float z = zb[j];
+    const float4 o = reinterpret_cast<const float4*>(ob)[c4];
+    return make_float4(z * o.x - v.x, z * o.y - v.y, z * o.z - v.z, z * o.w - v.w);
+  }
+  __device__ __forceinline__ float x1(int j, int c) const {
+    const float v = crow[(size_t)j * 64 + c];
+    return renorm ? zb[j] * ob[c] - v : v;
+  }
+  // <x_j, y> for y in LDS (four 16-byte loads in flight at a time)
+  __device__ __forceinline__ float dot(int j, const float* y) const {
+    const float4* y4 = reinterpret_cast<const float4*>(y);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 1
+    for (int c = 0; c < 16; c += 4) {
+      const float4 a0 = x4(j, c), a1 = x4(j, c + 1), a2 = x4(j, c + 2), a3 = x4(j, c + 3);
+      const float4 b0 = y4[c], b1 = y4[c + 1], b2 = y4[c + 2], b3 = y4[c + 3];
+      s0 = fmaf(a0.x, b0.x, s0); s0 = fmaf(a0.y, b0.y, s0);
+      s0 = fmaf(a0.z, b0.z, s0); s0 = fmaf(a0.w, b0.w, s0);
+      s1 = fmaf(a1.x, b1.x, s1); s1 = fmaf(a1.y, b1.y, s1);
+      s1 = fmaf(a1.z, b1.z, s1); s1 = fmaf(a1.w, b1.w, s1);
+      s0 = fmaf(a2.x, b2.x, s0); s0 = fmaf(a2.y, b2.y, s0);
+      s0 = fmaf(a2.z, b2.z, s0); s0 = fmaf(a2.w, b2.w, s0);
+      s1 = fmaf(a3.x, b3.x, s1); s1 = fmaf(a3.y, b3.y, s1);
+      s1 = fmaf(a3.z, b3.z, s1); s1 = fmaf(a3.w, b3.w, s1);
+    }
+    return s0 + s1;
+  }
+  // Head dims 32 ks + 8 (lane / 16) .. +7 of x_j, split in three bf16 terms:
+  // one operand fragment of v_mfma_f32_16x16x32_bf16 (lane l gives row or
+  // column l % 16); zeros when j < 0.
+  __device__ __forceinline__ void frag(int j, int ks, int lane, bf16x8& h, bf16x8& m,
+                                       bf16x8& l) const {
+    float x[8];
+    if (j >= 0) {
+      const int c4 = 8 * ks + 2 * (lane >> 4);
+      const float4 u = x4(j, c4), v = x4(j, c4 + 1);
+      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+      x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    sel_split3(x, h, m, l);
+  }
+};
+
+template <bool CACHE>
+__global__ __launch_bounds__(kWideThreads, 4) void k_select_drift_wide(DriftSelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
+  const Dims& d = a.d;
+  const int nb = d.nb;
+  const int r = blockIdx.x;
+  const int bh = r / nb, i = r - bh * nb;
+  const int h = bh % d.H, b = bh / d.H;
+  const int k = a.hb.keep[h];
+  const int nd = nb - k, ns = k - (a.force ? d.F : 0), nsl = nd + ns;
+  const DriftWideLds L = drift_wide_lds(nb, nsl, CACHE ? (size_t)nd * ns : 0);
+  SlotRec* slot = reinterpret_cast<SlotRec*>(dsm + L.slot);
+  float* gs = reinterpret_cast<float*>(dsm + L.gs);
+  uint32_t* hk = reinterpret_cast<uint32_t*>(dsm + L.hk);
+  int* slot_of = reinterpret_cast<int*>(dsm + L.slot_of);
+  float* zb = reinterpret_cast<float*>(dsm + L.zb);
+  float* G = reinterpret_cast<float*>(dsm + L.G);
+  const bool renorm = a.renorm != 0;
+  __shared__ __attribute__((aligned(16))) float rv[64];
+  __shared__ __attribute__((aligned(16))) float ob[64];
+  __shared__ __attribute__((aligned(16))) float xa[64];
+  __shared__ __attribute__((aligned(16))) float xb[64];
+  __shared__ __attribute__((aligned(16))) float part[kWideWaves][64];
+  __shared__ float redz[kWideWaves];
+  __shared__ int cnt[2][3][kWideWaves];
+  __shared__ unsigned long long bkey[kWideWaves];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float* crow = a.contrib + ((size_t)bh * nb + i) * (size_t)nb * 64;
+  const XRow X{crow, zb, ob, renorm};
+  int pass = 0;   // alternates the count buffers between barriers
+
+  // Squared norms and priorities: thread t takes chunk t % 16 of blocks
+  // (t + 256 m) / 16 (coalesced); the 16 lanes of a block reduce by exchange.
+  // Renormalised objective: also o = sum_j c_j and the masses z_j.
+  {
+    float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x = t; x < nb * 16; x += kWideThreads) {
+      const float4 v = reinterpret_cast<const float4*>(crow)[x];
+      float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      ss += __shfl_xor(ss, 8, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 1, 64);
+      const int j = x >> 4;
+      if ((x & 15) == 0) {
+        hk[j] = (a.force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(sqrtf(ss));
+        slot_of[j] = __float_as_int(ss);   // the norm, until slots are known
+      }
+      oacc.x += v.x; oacc.y += v.y; oacc.z += v.z; oacc.w += v.w;
+    }
+    if (renorm) {
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        oacc.x += __shfl_xor(oacc.x, o, 64); oacc.y += __shfl_xor(oacc.y, o, 64);
+        oacc.z += __shfl_xor(oacc.z, o, 64); oacc.w += __shfl_xor(oacc.w, o, 64);
+      }
+      if (lane < 16) *reinterpret_cast<float4*>(&part[w][4 * lane]) = oacc;
+      float zt = 0.f;
+      for (int j = t; j < nb; j += kWideThreads) {
+        const float zj = a.zmass[((size_t)bh * nb + i) * nb + j];
+        zb[j] = zj;
+        zt += zj;
+      }
+      zt = wave_sum(zt);
+      if (lane == 0) redz[w] = zt;
+    }
+  }
+  __syncthreads();
+  float ztot = 0.f;
+  if (renorm) {
+    if (t < 64) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int q = 0; q < kWideWaves; ++q) sacc += part[q][t];
+      ob[t] = sacc;
+    }
+#pragma unroll
+    for (int q = 0; q < kWideWaves; ++q) ztot += redz[q];
+  }
+
+  // T: the largest priority with #{hk >= T} >= k
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+    for (int j0 = 64 * w; j0 < nb; j0 += kWideThreads) {
+      const int j = j0 + lane;
+      c += __popcll(__ballot(j < nb && hk[j] >= cand));
+    }
+    if (lane == 0) cnt[pass & 1][0][w] = c;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int q = 0; q < kWideWaves; ++q) total += cnt[pass & 1][0][q];
+    ++pass;
+    if (total >= k) T = cand;
+  }
+  // kept: priority above T, or at T among the lowest blocks; slots: dropped
+  // blocks ascending, then kept non-forced blocks ascending (256 blocks per
+  // step, one barrier each)
+  {
+    int need = k, bd = 0, bs = 0;
+    {
+      int c = 0;
+      for (int j0 = 64 * w; j0 < nb; j0 += kWideThreads) {
+        const int j = j0 + lane;
+        c += __popcll(__ballot(j < nb && hk[j] > T));
+      }
+      if (lane == 0) cnt[pass & 1][0][w] = c;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kWideWaves; ++q) need -= cnt[pass & 1][0][q];
+      ++pass;
+    }
+    for (int base = 0; base < nb; base += kWideThreads) {
+      const int j = base + 64 * w + lane;
+      const bool real = j < nb;
+      const uint32_t pj = real ? hk[j] : 0u;
+      const bool tie = real && pj == T;
+      const unsigned long long tm = __ballot(tie);
+      // ties before this lane, block order: waves below, then lanes below
+      if (lane == 0) cnt[pass & 1][0][w] = __popcll(tm);
+      __syncthreads();
+      int tb = 0, tall = 0;
+#pragma unroll
+      for (int q = 0; q < kWideWaves; ++q) {
+        const int c = cnt[pass & 1][0][q];
+        tb += q < w ? c : 0;
+        tall += c;
+      }
+      ++pass;
+      const bool kept = real && (pj > T || (tie && tb + lanes_below(tm) < need));
+      const bool forced = real && a.force && block_forced(d, j);
+      const bool isd = real && !kept, iss = kept && !forced;
+      const unsigned long long md = __ballot(isd), ms = __ballot(iss);
+      if (lane == 0) {
+        cnt[pass & 1][1][w] = __popcll(md);
+        cnt[pass & 1][2][w] = __popcll(ms);
+      }
+      __syncthreads();
+      int db = 0, sb = 0, dall = 0, sall = 0;
+#pragma unroll
+      for (int q = 0; q < kWideWaves; ++q) {
+        const int cd = cnt[pass & 1][1][q], cs2 = cnt[pass & 1][2][q];
+        db += q < w ? cd : 0;
+        sb += q < w ? cs2 : 0;
+        dall += cd;
+        sall += cs2;
+      }
+      ++pass;
+      if (real) {
+        const int sl = isd ? bd + db + lanes_below(md) : (iss ? nd + bs + sb + lanes_below(ms) : -1);
+        const float cc = __int_as_float(slot_of[j]);
+        slot_of[j] = sl;
+        if (sl >= 0) slot[sl] = SlotRec{cc, 0.f, j, renorm ? zb[j] : 0.f};
+      }
+      need -= min(need, tall);
+      bd += dall;
+      bs += sall;
+    }
+  }
+  __syncthreads();
+
+  float z_s = 0.f;   // renorm: mass of the kept set
+  if (renorm) {
+    // |x_j|^2 of the swap rows, and the dropped mass
+    float zd = 0.f;
+    for (int sl = t; sl < nsl; sl += kWideThreads) {
+      const int j = slot[sl].blk;
+      float c2 = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < 16; ++c) {
+        const float4 x = X.x4(j, c);
+        c2 = fmaf(x.x, x.x, c2); c2 = fmaf(x.y, x.y, c2);
+        c2 = fmaf(x.z, x.z, c2); c2 = fmaf(x.w, x.w, c2);
+      }
+      slot[sl].cc = c2;
+      if (sl < nd) zd += slot[sl].z;
+    }
+    zd = wave_sum(zd);
+    if (lane == 0) redz[w] = zd;
+    __syncthreads();
+    zd = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWideWaves; ++q) zd += redz[q];
+    z_s = ztot - zd;
+  }
+
+  // D x S products on the matrix cores (16 x 16 x 32 tiles, operands split in
+  // three bf16 terms); wave w takes a contiguous run of the (S tile, D tile)
+  // pairs, S tile major, and reloads the S operand only when its tile changes.
+  const int NTD = (nd + 15) >> 4, NTS = (ns + 15) >> 4, npairs = NTD * NTS;
+  auto gram = [&](auto&& consume) {
+    const int p0 = w * npairs / kWideWaves, p1 = (w + 1) * npairs / kWideWaves;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    int cur = -1;
+    bf16x8 bh[2], bm[2], bl[2];
+    for (int p = p0; p < p1; ++p) {
+      const int tb = p / NTD, ta = p - tb * NTD;
+      if (tb != cur) {
+        cur = tb;
+        const int sb = 16 * tb + r16;
+        const int jb = sb < ns ? slot[nd + sb].blk : -1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) X.frag(jb, ks, lane, bh[ks], bm[ks], bl[ks]);
+      }
+      bf16x8 ah[2], am[2], al[2];
+      const int sa = 16 * ta + r16;
+      const int ja = sa < nd ? slot[sa].blk : -1;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) X.frag(ja, ks, lane, ah[ks], am[ks], al[ks]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[ks], bm[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[ks], bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bm[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh[ks], acc, 0, 0, 0);
+      }
+      // lane l holds D rows 4 (l / 16) + x of the tile, S column l % 16
+      const int bi = 16 * tb + r16;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int ai = 16 * ta + 4 * g4 + x;
+        if (ai < nd && bi < ns) consume(ai, bi, acc[x]);
+      }
+    }
+  };
+
+  // r = sum of the dropped rows (wave w sums the D slots w, w + 4, ..., one
+  // head dim per lane), and the cached G
+  {
+    float sacc = 0.f;
+#pragma unroll 4
+    for (int sl = w; sl < nd; sl += kWideWaves) sacc += X.x1(slot[sl].blk, lane);
+    part[w][lane] = sacc;
+  }
+  if (CACHE) gram([&](int ai, int bi, float v) { G[ai * ns + bi] = v; });
+  __syncthreads();
+  if (t < 64) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWideWaves; ++q) sacc += part[q][t];
+    rv[t] = renorm ? fmaf(1.f - ztot, ob[t], sacc) : sacc;
+  }
+  __syncthreads();
+
+  // g = <r, x> and the slot weights |x|^2 - 2 g (D) or |x|^2 + 2 g (S)
+  auto weights = [&]() {
+    for (int sl = t; sl < nsl; sl += kWideThreads) {
+      const float g = X.dot(slot[sl].blk, rv);
+      gs[sl] = g;
+      slot[sl].wgt = sl < nd ? fmaf(-2.f, g, slot[sl].cc) : fmaf(2.f, g, slot[sl].cc);
+    }
+  };
+  weights();
+  __syncthreads();
+
+  float rr = 0.f;
+  for (int round = 0;; ++round) {
+    rr = wave_allsum(rv[lane] * rv[lane]);
+    if (round == a.rounds) break;
+    if (!CACHE && round > 0) {
+      weights();
+      __syncthreads();
+    }
+
+    // candidates ordered by (criterion, a, b) as one 64-bit key
+    unsigned long long best = ~0ull;
+    auto offer = [&](int ai, int bi, float gab) {
+      const SlotRec sa = slot[ai], sb = slot[nd + bi];
+      const float dlt = (sa.wgt + sb.wgt) - 2.f * gab;
+      const float crit = renorm ? renorm_j2(rr, dlt, z_s + sa.z - sb.z) : dlt;
+      const unsigned long long key = ((unsigned long long)orderable(crit) << 32) |
+                                     ((uint32_t)sa.blk << 16) | (uint32_t)sb.blk;
+      best = key < best ? key : best;
+    };
+    if (CACHE) {
+      // thread t takes S slot bi = t % ns and D slots ai = t / ns + m * (256 / ns)
+      const int per = kWideThreads / max(ns, 1);
+      if (ns > 0 && ns <= kWideThreads && t < per * ns) {
+        const int bi = t % ns;
+#pragma unroll 4
+        for (int ai = t / ns; ai < nd; ai += per) offer(ai, bi, G[ai * ns + bi]);
+      } else if (ns > kWideThreads) {
+        for (int x = t; x < nd * ns; x += kWideThreads) offer(x / ns, x % ns, G[x]);
+      }
+    } else {
+      gram(offer);
+    }
+    best = wave_allmin_u64(best);
+    if (lane == 0) bkey[w] = best;
+    __syncthreads();
+    best = bkey[0];
+#pragma unroll
+    for (int q = 1; q < kWideWaves; ++q) best = bkey[q] < best ? bkey[q] : best;
+    const uint32_t hi = (uint32_t)(best >> 32);
+    bool improves;
+    if (renorm) {
+      // criteria are >= 0, whose orderable keys are the float bits with the sign bit set
+      const float jb = __uint_as_float(hi & 0x7FFFFFFFu);
+      improves = best != ~0ull && hi >= 0x80000000u && jb < rr / (z_s * z_s);
+    } else {
+      // delta < 0 (strictly) exactly when its orderable key is below that of -0
+      improves = best != ~0ull && hi < 0x7FFFFFFFu;
+    }
+    const uint32_t bab = (uint32_t)best;
+    const bool do_swap = nd > 0 && ns > 0 && improves;
+    const int ba = (int)(bab >> 16), bb = (int)(bab & 0xFFFFu);
+    if (t == 0 && a.swap_log) {
+      int32_t* lg = a.swap_log + ((size_t)r * a.rounds + round) * 2;
+      lg[0] = do_swap ? ba : -1;
+      lg[1] = do_swap ? bb : -1;
+    }
+    if (!do_swap) {
+      if (a.swap_log)
+        for (int q = round + 1 + t; q < a.rounds; q += kWideThreads) {
+          a.swap_log[((size_t)r * a.rounds + q) * 2] = -1;
+          a.swap_log[((size_t)r * a.rounds + q) * 2 + 1] = -1;
+        }
+      break;   // r and rr describe the final drop set
+    }
+    // Restore ba (D slot pa) and drop bb (S slot sb): wave 0 stages x_a and x_b
+    // in LDS, updates r by -x_a + x_b, and exchanges the two slots' records and
+    // g. No other wave reads slot_of, the records or rv until the barrier
+    // below; after it ba sits in slot sb and bb in slot pa.
+    if (w == 0) {
+      const int pa = slot_of[ba], sb = slot_of[bb];
+      const float va = X.x1(ba, lane), vb = X.x1(bb, lane);
+      xa[lane] = va;
+      xb[lane] = vb;
+      rv[lane] = (rv[lane] - va) + vb;
+      if (lane == 0) {
+        const SlotRec x = slot[pa];
+        slot[pa] = slot[sb];
+        slot[sb] = x;
+        const float gx = gs[pa];
+        gs[pa] = gs[sb];
+        gs[sb] = gx;
+        slot_of[ba] = sb;
+        slot_of[bb] = pa;
+      }
+    }
+    __syncthreads();
+    const int pa = slot_of[bb], sbs = slot_of[ba], pb = sbs - nd;
+    if (renorm) z_s += slot[sbs].z - slot[pa].z;
+    if (CACHE && round + 1 < a.rounds) {
+      // refresh row pa (now x_b) and column pb (now x_a) of G, and every g
+      // (not after the last round, whose products nothing reads)
+      for (int x = t; x < ns + nd; x += kWideThreads) {
+        if (x < ns) {
+          const int sl = nd + x;
+          const float nw = X.dot(slot[sl].blk, xb);   // <x_b, x_s>
+          const float old = G[pa * ns + x];           // <x_a, x_s>
+          G[pa * ns + x] = nw;
+          float g = gs[sl];
+          g = x == pb ? (g - slot[sl].cc) + old : (g - old) + nw;
+          gs[sl] = g;
+          slot[sl].wgt = fmaf(2.f, g, slot[sl].cc);
+        } else {
+          const int y = x - ns;
+          float g = gs[y];
+          if (y == pa) {
+            const float ab = dot64(xb, xa);            // <x_b, x_a>
+            g = (g - ab) + slot[y].cc;
+          } else {
+            const float nw = X.dot(slot[y].blk, xa);   // <x_y, x_a>
+            const float old = G[y * ns + pb];          // <x_y, x_b>
+            G[y * ns + pb] = nw;
+            g = (g - nw) + old;
+          }
+          gs[y] = g;
+          slot[y].wgt = fmaf(-2.f, g, slot[y].cc);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (t == 0 && a.row_stat) a.row_stat[r] = renorm ? sqrtf(rr) / z_s : sqrtf(rr);
+
+  const long long base0 = (long long)b * a.hb.per_batch + a.hb.head_off[h] + (long long)i * k;
+  if (t == 0) {
+    a.row_ptr[r] = (int32_t)base0;
+    if (r == d.rows - 1) a.row_ptr[d.rows] = (int32_t)(base0 + k);
+  }
+  // kept blocks in ascending order: a block is kept iff it sits in an S slot or
+  // is forced; 256 blocks per step
+  int off = 0;
+  for (int base = 0; base < nb; base += kWideThreads) {
+    const int j = base + 64 * w + lane;
+    const bool f = j < nb && (slot_of[j] >= nd || slot_of[j] < 0);
+    const unsigned long long m = __ballot(f);
+    if (lane == 0) cnt[pass & 1][0][w] = __popcll(m);
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int q = 0; q < kWideWaves; ++q) {
+      const int c = cnt[pass & 1][0][q];
+      before += q < w ? c : 0;
+      all += c;
+    }
+    ++pass;
+    if (f) a.col_idx[base0 + off + before + lanes_below(m)] = j;
+    off += all;
+  }
+}
+
 hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, int rounds,
                                int objective, const float* contrib, const float* zmass,
                                int32_t* row_ptr, int32_t* col_idx, float* row_stat,
@@ -780,6 +1278,19 @@ hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, i
   for (int h = 0; h < d.H; ++h) {
     gmax = std::max(gmax, (size_t)(d.nb - hb.keep[h]) * (size_t)(hb.keep[h] - nforced));
     smax = std::max(smax, d.nb - nforced);
+  }
+  if (d.nb > kDriftLdsRowBlocks) {
+    // wide rows: the row stays in L2; G is cached when it fits in 64 KB
+    const size_t lds_cache = drift_wide_lds(d.nb, smax, gmax).total;
+    const bool cache = rounds > 0 && lds_cache <= 64 * 1024;
+    const size_t lds = cache ? lds_cache : drift_wide_lds(d.nb, smax, 0).total;
+    if (lds > kDriftSelLdsCap) return hipErrorInvalidValue;
+    const void* fn = cache ? (const void*)k_select_drift_wide<true> : (const void*)k_select_drift_wide<false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(reinterpret_cast<void (*)(DriftSelArgs)>(const_cast<void*>(fn))),
+                       dim3(d.rows), dim3(kWideThreads), lds, s, a);
+    return hipGetLastError();
   }
   const size_t lds_cache = drift_sel_lds(d.nb, smax, gmax).total;
   const bool cache = rounds > 0 && lds_cache <= kDriftSelLdsCap;

@@ -113,8 +113,10 @@ DenseRowsPlan dense_rows_plan(const Dims& d, int ns);
 hipError_t launch_dense_rows(const Dims& d, int ns, const void* q, const void* k, const void* v,
                              void* o, float* lse, void* ws, hipStream_t s);
 
-// Largest key-block count the drift selection keeps in LDS.
-constexpr int kDriftMaxBlocks = 512;
+// Largest key-block count whose drift selection row the best-swap kernel keeps
+// in LDS; wider rows (up to kDriftMaxBlocks) leave the row in L2.
+constexpr int kDriftLdsRowBlocks = 512;
+constexpr int kDriftMaxBlocks = 4096;
 // Largest block count a pooled selection row handles (16 per thread x 256).
 constexpr int kSelectMaxBlocks = 4096;
 

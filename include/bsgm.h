@@ -175,7 +175,8 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
  *          swap_rounds rounds. A round may raise J; TRACK_BEST returns the set of
  *          least J among the initial set and every round's set (ties: the
  *          earlier; [ReSS] Table S3), RERANK the last one. Rows of any number of
- *          blocks (BEST_SWAP: at most 512).
+ *          blocks (BEST_SWAP: at most 4096; above 512 the row is read from
+ *          global memory in every pass instead of held on chip).
  *   q, k       device [B,H,N,D] (TOPK, CDF; may be NULL for DRIFT)
  *   contrib    device float [B,H,Nb,Nb,D] from bsgm_drift_scores (DRIFT only)
  *   zmass      device float [B,H,Nb,Nb] from bsgm_drift_scores (RENORMALISED only)

@@ -109,8 +109,8 @@ def test_select_argument_errors():
     assert _select(lay, mode=2, contrib=16, objective=1)[0] == -1       # renormalised needs zmass
     assert _select(lay, q=None)[0] == -1
     assert _select(lay, rp=None)[0] == -1
-    big = L(frames=2, frame_len=128 * 300, frame_valid=128 * 300)
-    assert _select(big, mode=2, keep=(5, 5), contrib=16)[0] == -2      # 600 blocks > 512
+    big = L(frames=2, frame_len=128 * 2100, frame_valid=128 * 2100)
+    assert _select(big, mode=2, keep=(5, 5), contrib=16)[0] == -2      # 4200 blocks > 4096
 
 
 def _fused(lay, mode=0, keep=(2, 2), force=False, cap=None, wsb=None, wsp=256, q=16, k=16,

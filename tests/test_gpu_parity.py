@@ -1160,6 +1160,62 @@ def test_drift_wide_rows_cached_search(dev, objective):
     say(f"drift wide rows: sampled rows whose final set differs from the oracle's own run: {differ}")
 
 
+@pytest.mark.parametrize("keep,objective", [(20, oracle.RAW), (264, oracle.RAW),
+                                            (20, oracle.RENORM)])
+def test_drift_best_swap_rows_beyond_512(dev, keep, objective):
+    """Best-swap selection on rows of 528 key blocks, wider than the LDS row
+    cache: the row stays in global memory. Keep 20 caches the D x S products in
+    LDS (508 x 20); keep 264 recomputes them every round (264 x 264)."""
+    lay = custom_layout(48, 1408, 1374, 128, heads=1)
+    assert lay.nblocks == 528
+    host, vals = random_inputs(lay, 73 + keep)
+    nb = lay.nblocks
+    keep_a = np.array([keep], dtype=np.int32)
+    rounds = 3
+    say(f"drift best-swap 528 blocks, keep {keep}, objective {objective}")
+    q, k, v = (to_dev(x, dev) for x in host)
+    zmass = None
+    if objective == oracle.RENORM:
+        zmass = torch.empty((1, 1, nb, nb), dtype=torch.float32, device=dev)
+    contrib, score = bsgm.drift_scores(lay, q, k, v, zmass=zmass)
+    log = torch.full((nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep_a, contrib=contrib, swap_rounds=rounds,
+                                    objective=objective, zmass=zmass, swap_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    assert rpn[-1] == nb * keep
+    rows = [(0, i) for i in (0, 1, 255, 256, 300, 511, 512, 527)]
+    differ = check_drift(lay, vals, keep_a, rounds, False, contrib.cpu().numpy(),
+                         score.cpu().numpy(), rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows,
+                         objective=objective,
+                         zmass_g=None if zmass is None else zmass.cpu().numpy())
+    say(f"drift 528: sampled rows whose final set differs from the oracle's own run: {differ}")
+
+
+def test_drift_best_swap_100_frame_rows(dev):
+    """Best-swap selection on one head of the 100-frame layer (1 100 key blocks
+    per row, keep 220, 3 rounds): pair products recomputed every round."""
+    lay = custom_layout(100, 1408, 1374, 128, heads=1)
+    assert lay.nblocks == 1100
+    host, vals = random_inputs(lay, 79)
+    nb = lay.nblocks
+    keep = np.array([220], dtype=np.int32)
+    rounds = 3
+    q, k, v = (to_dev(x, dev) for x in host)
+    contrib, score = bsgm.drift_scores(lay, q, k, v)
+    log = torch.full((nb, rounds, 2), -7, dtype=torch.int32, device=dev)
+    rp, ci, st = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                    swap_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    rows = [(0, i) for i in (0, 549, 1099)]
+    differ = check_drift(lay, vals, keep, rounds, False, contrib.cpu().numpy(),
+                         score.cpu().numpy(), rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows)
+    say(f"drift 1100: sampled rows whose final set differs from the oracle's own run: {differ}")
+
+
 # renormalised objective: the output shift once dropped blocks are removed
 @pytest.mark.parametrize("dtype,block,force", [("bf16", 64, False), ("bf16", 128, True),
                                                ("f32", 64, True), ("f32", 128, False)])
