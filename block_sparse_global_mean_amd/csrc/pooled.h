@@ -80,9 +80,13 @@ hipError_t launch_select_fused(const Dims& d, const HeadBudget& hb, int dtype, i
                                int32_t* sync, int32_t* row_ptr, int32_t* col_idx,
                                float* row_stat, float* scores_out, hipStream_t s);
 
-// Synchronisation words of the one-launch selection, one per 128-byte line: the
-// ticket, the exit count, the error flag, then one pooled-item count per (b, h).
+// Synchronisation words of the one-launch selection, one per 128-byte line: an
+// unused line, the exit count, the error flag, one pooled-item count per (b, h),
+// then one ticket per XCD work queue (at most kFusedMaxQueues).
 constexpr int kFusedLine = 32;
-inline size_t fused_sync_words(const Dims& d) { return (size_t)kFusedLine * (3 + (size_t)d.B * d.H); }
+constexpr int kFusedMaxQueues = 16;
+inline size_t fused_sync_words(const Dims& d) {
+  return (size_t)kFusedLine * (3 + (size_t)d.B * d.H + kFusedMaxQueues);
+}
 
 }  // namespace bsgm

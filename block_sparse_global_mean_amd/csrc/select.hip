@@ -387,21 +387,30 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
 
 // ---------------------------------------------------------------------------
 // Pooled top-k selection in one launch: the pooling of Q and K and the
-// selection share one grid. Items: first the pooling items, head-major (item x
-// of (b, h) pools query and key blocks 2x and 2x + 1), then the selection
-// items, head-major (four query blocks each, as k_select_pooled). A workgroup
-// takes one item by an atomic ticket, so tickets follow the order in which
-// workgroups start rather than their index. A selection item waits until every
-// pooling item of its (b, h) has published; those items hold lower tickets,
-// so they were taken by workgroups already running, and a pooling item waits
-// on nothing: every wait ends. While one head selects, later heads still pool.
+// selection share one grid, and every (b, h) is pooled and selected on one XCD
+// (its work queue: (b*H + h) mod the XCD count), so that the selection reads
+// the pooled means through that XCD's L2 with no device-wide cache writeback
+// or invalidation. The grid is persistent: a workgroup reads the XCD it runs
+// on (the XCC_ID hardware register) and takes items from that XCD's queue by
+// an atomic ticket until the queue is drained. A queue holds its heads'
+// pooling items (item x of a head pools query and key blocks 2x and 2x + 1),
+// then their selection items (four query blocks each, as k_select_pooled). A
+// selection item waits until every pooling item of its head has published;
+// those hold lower tickets of the same queue, so workgroups already running
+// took them, and a pooling item waits on nothing: every wait ends.
 //
-// Publication: each pooling thread makes its stores visible device-wide (a
-// device-scope release fence, which writes back the XCD's L2) before the item's
-// count goes up; the selecting workgroup acquires at device scope after its
-// wait. Each counter sits on a 128-byte line of its own.
-// The last workgroup to leave resets the ticket, the exit count and the item
-// counts, so every call finds them zero (the caller zeroes them once).
+// Publication inside an XCD: a pooling workgroup waits until its stores are
+// acknowledged by the L2 (vmcnt 0), then raises the head's count; the L1 is
+// write-through and holds no line of that head's means from before (each call
+// starts with clean L1s, and a CU reads a head's means only after they are
+// complete), so the selecting workgroup's loads see them.
+//
+// The last workgroup to leave runs, in order, any queue that no workgroup
+// took (an XCD with no workgroup of this grid), so the result never depends on
+// where the hardware placed the workgroups, and then resets the tickets, the
+// item counts and the exit count, so every call finds them zero (the caller
+// zeroes them once). Its view of the counters needs no fence: each workgroup's
+// last ticket fetch returned before it raised the exit count.
 // ---------------------------------------------------------------------------
 constexpr int kFusedPoolBlocks = 2;        // query and key blocks per pooling item
 constexpr int kFusedSpinLimit = 1 << 22;   // waits of about 64 clocks each
@@ -409,75 +418,94 @@ constexpr int kFusedSpinLimit = 1 << 22;   // waits of about 64 clocks each
 template <typename T, int PW>
 __global__ __launch_bounds__(256) void k_select_fused(SelArgs a, const T* __restrict__ xq,
                                                        const T* __restrict__ xk, float* qbar,
-                                                       float* kbar, int32_t* sync) {
+                                                       float* kbar, int32_t* sync, int nq) {
   constexpr size_t kSelLds = 2 * 64 * kKtStride * sizeof(float);
   constexpr size_t kPoolLds = 2 * kFusedPoolBlocks * PoolGeom<T>::G * 65 * sizeof(float);
   __shared__ __attribute__((aligned(16))) unsigned char lds[kSelLds > kPoolLds ? kSelLds : kPoolLds];
-  __shared__ int s_ticket, s_last;
+  __shared__ int s_item, s_last;
   const Dims& d = a.d;
   const int t = threadIdx.x;
   const int nbh = d.B * d.H;
   const int pool_per_bh = (d.nb + kFusedPoolBlocks - 1) / kFusedPoolBlocks;
   const int sel_per_bh = (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
-  const int npool = nbh * pool_per_bh, total = npool + nbh * sel_per_bh;
-  int32_t* ticket = sync;
   int32_t* exits = sync + kFusedLine;
   int32_t* error = sync + 2 * kFusedLine;
   int32_t* done = sync + 3 * kFusedLine;   // item count of (b, h) = x at done[x * kFusedLine]
+  int32_t* tickets = sync + (3 + nbh) * kFusedLine;   // queue x at tickets[x * kFusedLine]
 
-  if (t == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int item = s_ticket;
-  if (item < npool) {
-    const int bh = item / pool_per_bh, j0 = (item - bh * pool_per_bh) * kFusedPoolBlocks;
-    PoolUnit<T> u[2 * kFusedPoolBlocks];
-#pragma unroll
-    for (int x = 0; x < kFusedPoolBlocks; ++x) {
-      const int j = j0 + x;
-      const bool real = j < d.nb;
-      const size_t tok = ((size_t)bh * d.N + (size_t)(real ? j : 0) * d.blk) * 64;
-      const size_t row = ((size_t)bh * d.nb + j) * 64;
-      const int vlen = real ? block_vlen(d, j) : 0;
-      u[2 * x] = PoolUnit<T>{xq + tok, real ? qbar + row : nullptr, vlen};
-      u[2 * x + 1] = PoolUnit<T>{xk + tok, real ? kbar + row : nullptr, vlen};
-    }
-    pool_units<T, 2 * kFusedPoolBlocks>(
-        u, reinterpret_cast<float(*)[PoolGeom<T>::G][65]>(lds));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
+  // runs item `item` of queue `qu`; false once the queue is drained
+  auto run = [&](int qu) {
+    const int nh = (nbh - qu + nq - 1) / nq;   // heads qu, qu + nq, ...
+    const int npool = nh * pool_per_bh, total = npool + nh * sel_per_bh;
+    __syncthreads();   // the previous item is done with the LDS and s_item
     if (t == 0)
-      __hip_atomic_fetch_add(&done[bh * kFusedLine], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    const int sel = item - npool, bh = sel / sel_per_bh;
-    if (t == 0) {
-      int spins = 0;
-      while (__hip_atomic_load(&done[bh * kFusedLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-             pool_per_bh) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins == kFusedSpinLimit) {
-          __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+      s_item = __hip_atomic_fetch_add(&tickets[qu * kFusedLine], 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= total) return false;
+    if (item < npool) {
+      const int u = item / pool_per_bh, bh = qu + nq * u;
+      const int j0 = (item - u * pool_per_bh) * kFusedPoolBlocks;
+      PoolUnit<T> pu[2 * kFusedPoolBlocks];
+#pragma unroll
+      for (int x = 0; x < kFusedPoolBlocks; ++x) {
+        const int j = j0 + x;
+        const bool real = j < d.nb;
+        const size_t tok = ((size_t)bh * d.N + (size_t)(real ? j : 0) * d.blk) * 64;
+        const size_t row = ((size_t)bh * d.nb + j) * 64;
+        const int vlen = real ? block_vlen(d, j) : 0;
+        pu[2 * x] = PoolUnit<T>{xq + tok, real ? qbar + row : nullptr, vlen};
+        pu[2 * x + 1] = PoolUnit<T>{xk + tok, real ? kbar + row : nullptr, vlen};
+      }
+      pool_units<T, 2 * kFusedPoolBlocks>(
+          pu, reinterpret_cast<float(*)[PoolGeom<T>::G][65]>(lds));
+      // every store of this workgroup acknowledged by the L2 before the count
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+      __syncthreads();
+      if (t == 0)
+        __hip_atomic_fetch_add(&done[bh * kFusedLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int sel = item - npool, u = sel / sel_per_bh, bh = qu + nq * u;
+      if (t == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(&done[bh * kFusedLine], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) < pool_per_bh) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins == kFusedSpinLimit) {
+            __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
         }
       }
+      __syncthreads();
+      select_rows<PW, false>(a, bh, sel - u * sel_per_bh,
+                             reinterpret_cast<float(*)[64 * kKtStride]>(lds));
     }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    select_rows<PW, false>(a, bh, sel - bh * sel_per_bh,
-                           reinterpret_cast<float(*)[64 * kKtStride]>(lds));
-  }
+    return true;
+  };
+
+  // XCC_ID (hardware register 20, bits 3:0): the XCD this workgroup runs on
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u);
+  if (xcc < nq)
+    while (run(xcc)) {
+    }
   __syncthreads();
   if (t == 0)
-    s_last = __hip_atomic_fetch_add(exits, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+    s_last = __hip_atomic_fetch_add(exits, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (int)gridDim.x - 1;
   __syncthreads();
   if (s_last) {
-    // every other workgroup's release on the exit count precedes this acquire
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int qu = 0; qu < nq; ++qu)
+      while (run(qu)) {
+      }
+    __syncthreads();
     for (int x = t; x < nbh; x += 256)
       __hip_atomic_store(&done[x * kFusedLine], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == 0) {
-      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(exits, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int x = t; x < kFusedMaxQueues; x += 256)
+      __hip_atomic_store(&tickets[x * kFusedLine], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0) __hip_atomic_store(exits, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -487,22 +515,27 @@ hipError_t launch_select_fused(const Dims& d, const HeadBudget& hb, int dtype, i
                                float* row_stat, float* scores_out, hipStream_t s) {
   SelArgs a{d, hb, 0, 0.f, force, qbar, kbar, row_ptr, col_idx, row_stat, scores_out,
             nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
-  const int nbh = d.B * d.H;
-  const long long items =
-      (long long)nbh * ((d.nb + kFusedPoolBlocks - 1) / kFusedPoolBlocks +
-                        (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg);
-  if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)items), block(256);
+  // one queue per XCD; resident workgroups: four per CU
+  int dev = 0, nxcc = 1, ncu = 256;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nxcc < 1)
+    nxcc = 1;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      ncu < 1)
+    ncu = 256;
+  const int nq = nxcc < kFusedMaxQueues ? nxcc : kFusedMaxQueues;
+  const dim3 grid((unsigned)(4 * ncu)), block(256);
   auto go = [&](auto pw) {
     constexpr int PW = decltype(pw)::value;
     if (dtype == 1)
       hipLaunchKernelGGL((k_select_fused<__bf16, PW>), grid, block, 0, s, a,
                          static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), qbar, kbar,
-                         sync);
+                         sync, nq);
     else
       hipLaunchKernelGGL((k_select_fused<float, PW>), grid, block, 0, s, a,
                          static_cast<const float*>(q), static_cast<const float*>(k), qbar, kbar,
-                         sync);
+                         sync, nq);
   };
   const int per = (d.nb + 63) / 64;
   if (per <= 1) go(std::integral_constant<int, 1>{});

@@ -226,8 +226,9 @@ int bsgm_select_blocks_pooled(const bsgm_layout* layout, const bsgm_select_param
  * ([ReSS] Table 1: selection overhead with and without a fused kernel). The
  * result is bitwise that of bsgm_select_blocks in TOPK mode (same pooling and
  * selection arithmetic); the pooled means stay in the workspace. Inside the
- * launch the selection of a (batch, head) starts once that head's pooling is
- * done, while later heads still pool.
+ * launch each (batch, head) is pooled and then selected on one XCD of the GPU,
+ * its selection starting once that head's pooling is done, while other heads
+ * still pool.
  *   params     mode must be BSGM_SEL_TOPK (BSGM_E_UNSUPPORTED otherwise);
  *              keep_per_head and force_frame_first_block as bsgm_select_blocks
  *   q, k, row_ptr, col_idx, col_capacity, row_stat, scores_out
@@ -250,7 +251,7 @@ int bsgm_select_blocks_fused(const bsgm_layout* layout, const bsgm_select_params
                              int64_t col_capacity, float* row_stat, float* scores_out, void* ws,
                              size_t ws_bytes, void* stream);
 
-/* Device workspace bytes of bsgm_select_blocks_fused: 128 * (3 + batch * heads)
+/* Device workspace bytes of bsgm_select_blocks_fused: 128 * (19 + batch * heads)
  * bytes of synchronisation words and the pooled Q and K (4 * B * H * Nb * D
  * bytes each), each part rounded up to 256 bytes; 0 for an invalid layout (see
  * bsgm_last_error). */

@@ -129,7 +129,7 @@ def _fused(lay, mode=0, keep=(2, 2), force=False, cap=None, wsb=None, wsp=256, q
 def test_fused_select_workspace_and_errors():
     lay = L(batch=3)                      # 3 x 2 (b, h), 8 blocks each, 48 rows
     al = lambda x: (x + 255) // 256 * 256
-    assert bsgm.fused_workspace_bytes(lay) == al(128 * (3 + 6)) + 2 * al(48 * 64 * 4)
+    assert bsgm.fused_workspace_bytes(lay) == al(128 * (3 + 6 + 16)) + 2 * al(48 * 64 * 4)
     with pytest.raises(bsgm.BsgmError):
         bsgm.fused_workspace_bytes(L(head_dim=32))
     assert _fused(lay, mode=bsgm.CDF) == -2

@@ -259,9 +259,10 @@ def test_select_from_pooled_means(dev, mode, case):
 # pooled top-k selection in one launch
 # --------------------------------------------------------------------------
 def sync_words(lay, ws):
-    """The fused workspace's synchronisation area: ticket, exit count, error flag and
-    one count per (b, h), each on a 128-byte line (the rest of every line unused)."""
-    n = 32 * (3 + lay.batch * lay.heads)
+    """The fused workspace's synchronisation area: an unused line, the exit count,
+    the error flag, one count per (b, h) and 16 queue tickets, each on a 128-byte
+    line (the rest of every line unused)."""
+    n = 32 * (3 + lay.batch * lay.heads + 16)
     return ws[:4 * n].view(torch.int32).cpu().numpy()
 
 
