@@ -153,7 +153,9 @@ struct WaveItem {
 
 __device__ __forceinline__ bool wave_item(const Dims& d, int rtpw, WaveItem& it) {
   const int nrt = (d.nb + 31) / 32, nsplit = (nrt + rtpw - 1) / rtpw;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform (the compiler cannot tell from threadIdx), so that every
+  // index and address derived from it lives in scalar registers
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (gw >= d.B * d.H * d.nb * nsplit) return false;
   const int s = gw % nsplit, bj = gw / nsplit;
   it.bh = bj / d.nb;
@@ -315,37 +317,40 @@ __device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveI
   }
 
   // contrib rows: lanes 0-31 write 128 contiguous bytes of one query row,
-  // lanes 32-63 those of the row 4 below. The (b, h, j) base is wave-uniform
-  // and one (b, h)'s rows span nb^2 * 64 floats (< 2^30 for nb < 4096), so
-  // lanes address with 32-bit offsets from it.
-  const uint32_t rs = (uint32_t)d.nb * 64u;
-  float* base = a.contrib + ((size_t)bh * d.nb * d.nb + j) * 64;
-  const uint32_t off0 = (uint32_t)(32 * rt + 4 * hh) * rs + (uint32_t)n;
+  // lanes 32-63 those of the row 4 below. Raw buffer stores off a wave-uniform
+  // resource at (b, h, row tile, j): the lane's byte offset in a VGPR, the
+  // row's (a multiple of the row pitch) in an SGPR, so no store needs address
+  // arithmetic. The tile spans under 32 * nb * 256 bytes.
+  const uint32_t rsb = (uint32_t)d.nb * 256u;   // bytes between query rows
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      a.contrib + (((size_t)bh * d.nb + 32 * rt) * d.nb + j) * 64, 0, (int)(32u * rsb), 0x00020000);
+  const uint32_t off0 = (uint32_t)(4 * hh) * rsb + (uint32_t)n * 4u;
   if (32 * rt + 32 <= d.nb) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const uint32_t o = off0 + (uint32_t)(8 * (x >> 2) + (x & 3)) * rs;
-      base[o] = c[0][x];
-      base[o + 32u] = c[1][x];
+      const int so = (8 * (x >> 2) + (x & 3)) * (int)rsb;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0][x]), rs, (int)off0, so, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[1][x]), rs, (int)off0 + 128, so, 0);
     }
   } else {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int r = 8 * (x >> 2) + (x & 3);
-      if (32 * rt + 4 * hh + r < d.nb) {
-        const uint32_t o = off0 + (uint32_t)r * rs;
-        base[o] = c[0][x];
-        base[o + 32u] = c[1][x];
+      const int rr = 8 * (x >> 2) + (x & 3);
+      if (32 * rt + 4 * hh + rr < d.nb) {
+        const int so = rr * (int)rsb;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0][x]), rs, (int)off0, so, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[1][x]), rs, (int)off0 + 128, so, 0);
       }
     }
   }
 
   // score: sum of squares over the 64 head dims (32 lanes x 2 tiles) of each
-  // of the 16 rows a lane holds. Halving exchanges leave lane n with the
+  // of the 16 rows a lane holds, with one fixed contraction so that the
+  // rounding does not depend on instruction scheduling. Halving exchanges leave lane n with the
   // total of row x = 8 b4 + 4 b3 + 2 b2 + b1 (b_k = bit k of n).
   float v[16];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) v[x] = c[0][x] * c[0][x] + c[1][x] * c[1][x];
+  for (int x = 0; x < 16; ++x) v[x] = fmaf(c[0][x], c[0][x], c[1][x] * c[1][x]);
 #pragma unroll
   for (int step = 0; step < 4; ++step) {
     const int msk = 16 >> step, half = 8 >> step;
