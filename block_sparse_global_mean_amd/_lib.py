@@ -31,7 +31,8 @@ EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
            "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes", "bsgm_attn_prepare",
            "bsgm_sparse_attn_fwd_prepared", "bsgm_select_blocks_fused", "bsgm_fused_workspace_bytes",
-           "bsgm_select_blocks_pooled", "bsgm_select_blocks_noalloc")
+           "bsgm_select_blocks_pooled", "bsgm_select_blocks_noalloc", "bsgm_select_drift_streamed",
+           "bsgm_drift_streamed_workspace_bytes")
 
 
 class BsgmError(RuntimeError):
@@ -95,10 +96,14 @@ def library() -> ctypes.CDLL:
         lib.bsgm_special_rows_dense_fwd.argtypes = [lp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
         lib.bsgm_vasc_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
                                                 vp, vp, sz, vp]
+        lib.bsgm_select_drift_streamed.argtypes = [lp, pp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
+                                                   vp, vp, sz, vp]
+        lib.bsgm_drift_streamed_workspace_bytes.argtypes = [lp]
+        lib.bsgm_drift_streamed_workspace_bytes.restype = sz
         for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
                      "bsgm_sparse_attn_fwd", "bsgm_special_rows_dense_fwd",
                      "bsgm_vasc_select_blocks", "bsgm_select_blocks_fused", "bsgm_select_blocks_pooled",
-                     "bsgm_select_blocks_noalloc",
+                     "bsgm_select_blocks_noalloc", "bsgm_select_drift_streamed",
                      "bsgm_attn_prepare",
                      "bsgm_sparse_attn_fwd_prepared"):
             getattr(lib, name).restype = ctypes.c_int
@@ -291,6 +296,56 @@ def select_blocks(layout, mode: int, keep: Sequence[int], q=None, k=None, contri
         ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(contrib), _ptr(zmass), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), _ptr(row_stat), _ptr(scores_out), _ptr(swap_log),
         *_ws(workspace), _stream(stream)))
+    return row_ptr, col_idx, row_stat
+
+
+def drift_streamed_workspace_bytes(layout) -> int:
+    L = c_layout(layout)
+    n = library().bsgm_drift_streamed_workspace_bytes(ctypes.byref(L))
+    if n == 0:
+        raise BsgmError(1, library().bsgm_last_error().decode())
+    return n
+
+
+def select_drift_streamed(layout, keep: Sequence[int], q, k, v, swap_rounds: int = 5,
+                          track_best: bool = True, force: bool = False, row_ptr=None,
+                          col_idx=None, row_stat=None, set_log=None, workspace=None,
+                          want_stat: bool = True, stream=None):
+    """Drift selection by re-rank rounds straight from Q, K and V, without the
+    [B,H,Nb,Nb,D] contributions (dropped-sum objective, bf16). set_log, when
+    given, receives [rows, swap_rounds + 1, ceil(nb / 32)] kept bitmasks."""
+    n, nb, rows = _dims(layout)
+    shape = (layout.batch, layout.heads, n, layout.head_dim)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, _tdtype(layout), shape)
+    dev = q.device
+    _opt(row_ptr, "row_ptr", torch.int32, (rows + 1,))
+    if col_idx is not None:
+        _expect_1d(col_idx, "col_idx", torch.int32)
+    _opt(row_stat, "row_stat", torch.float32, (rows,))
+    if set_log is not None:
+        per_row = (swap_rounds + 1) * ((nb + 31) // 32)
+        if not isinstance(set_log, torch.Tensor) or not set_log.is_cuda or \
+                set_log.dtype != torch.int32 or not set_log.is_contiguous() or \
+                set_log.numel() < rows * per_row:
+            raise ValueError(f"set_log must be a contiguous int32 device tensor of at least "
+                             f"{rows} x {per_row} elements")
+    cap = col_capacity(layout, DRIFT, keep, force)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_stat is None and want_stat:
+        row_stat = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(drift_streamed_workspace_bytes(layout), dtype=torch.uint8,
+                                device=dev)
+    L = c_layout(layout)
+    P, _keep = c_params(DRIFT, keep, 0.9, force, swap_rounds, DROPPED_SUM,
+                        RERANK_TRACK_BEST if track_best else RERANK)
+    _check(library().bsgm_select_drift_streamed(
+        ctypes.byref(L), ctypes.byref(P), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
+        col_idx.numel(), _ptr(row_stat), _ptr(set_log), *_ws(workspace), _stream(stream)))
     return row_ptr, col_idx, row_stat
 
 

@@ -143,6 +143,37 @@ WsLayout ws_layout(const bsgm::Dims& d, int mode) {
   return w;
 }
 
+// Workspace of the streamed (expanded-form) re-rank drift selection. The
+// squared scores and the per-round dot products reuse the statistics' bytes,
+// which are dead once (M_i, Z_i) are formed.
+struct StreamWs {
+  size_t qbar, qsplit, stats, mz, part, rsplit, jsq, jbest, m0, m1, best, total;
+};
+
+StreamWs stream_ws_layout(const bsgm::Dims& d) {
+  StreamWs w{};
+  const size_t rows = (size_t)d.rows, words = (size_t)((d.nb + 31) / 32);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  w.qbar = take(rows * 64 * sizeof(float));
+  w.qsplit = take(rows * 3 * 64 * 2);
+  w.stats = take(rows * d.nb * 2 * sizeof(float));   // later: ||c||^2, then <r, c>
+  w.mz = take(rows * 2 * sizeof(float));
+  w.part = take(rows * bsgm::drift_round_groups(d) * 64 * sizeof(float));
+  w.rsplit = take(rows * 3 * 64 * 2);
+  w.jsq = take(rows * sizeof(float));
+  w.jbest = take(rows * sizeof(float));
+  w.m0 = take(rows * words * 4);
+  w.m1 = take(rows * words * 4);
+  w.best = take(rows * words * 4);
+  w.total = off;
+  return w;
+}
+
 // Checks the per-head budgets and fills the closed-form CSR offsets.
 int check_budget(const bsgm::Dims& d, const bsgm_select_params* P, bsgm::HeadBudget* hb) {
   if (!P) return fail(BSGM_E_ARG, "params is NULL");
@@ -262,6 +293,91 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
     e = bsgm::launch_drift_contrib(d, layout->dtype, qbar, k, v, contrib, score, zmass, s);
   }
   if (e != hipSuccess) return hip_fail(e, "drift launch");
+  return ok();
+}
+
+size_t bsgm_drift_streamed_workspace_bytes(const bsgm_layout* layout) {
+  bsgm::Dims d;
+  if (check_layout(layout, &d) != BSGM_OK) return 0;
+  ok();
+  return stream_ws_layout(d).total;
+}
+
+int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_params* params,
+                               const void* q, const void* k, const void* v, int32_t* row_ptr,
+                               int32_t* col_idx, int64_t col_capacity, float* row_stat,
+                               int32_t* set_log, void* ws, size_t ws_bytes, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  bsgm::HeadBudget hb;
+  st = check_budget(d, params, &hb);
+  if (st != BSGM_OK) return st;
+  if (params->mode != BSGM_SEL_DRIFT)
+    return fail(BSGM_E_ARG, "streamed drift selection takes mode BSGM_SEL_DRIFT (got %d)",
+                params->mode);
+  if (params->restoration != BSGM_RESTORE_RERANK &&
+      params->restoration != BSGM_RESTORE_RERANK_TRACK_BEST)
+    return fail(BSGM_E_UNSUPPORTED, "streamed drift selection takes the re-rank restoration rules");
+  if (params->drift_objective != BSGM_DRIFT_DROPPED_SUM)
+    return fail(BSGM_E_UNSUPPORTED, "streamed drift selection takes the dropped-sum objective");
+  if (params->swap_rounds < 0) return fail(BSGM_E_ARG, "swap_rounds must be >= 0");
+  if (layout->dtype != BSGM_BF16)
+    return fail(BSGM_E_UNSUPPORTED, "streamed drift selection: dtype must be BSGM_BF16");
+  if (!q || !k || !v || !row_ptr || !col_idx || !ws)
+    return fail(BSGM_E_ARG, "q, k, v, row_ptr, col_idx and ws must be non-NULL");
+  const long long need = (long long)d.B * hb.per_batch;
+  if (need > 0x7FFFFFFFLL)
+    return fail(BSGM_E_UNSUPPORTED, "worst-case nnz %lld does not fit int32 CSR", need);
+  if (col_capacity < need)
+    return fail(BSGM_E_CAPACITY, "col_capacity %lld below worst-case nnz %lld",
+                (long long)col_capacity, need);
+  const StreamWs w = stream_ws_layout(d);
+  if (ws_bytes < w.total)
+    return fail(BSGM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  char* base = static_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(base + w.qbar);
+  float2* mz = reinterpret_cast<float2*>(base + w.mz);
+  float* sqnorm = reinterpret_cast<float*>(base + w.stats);
+  float* dot = sqnorm + (size_t)d.rows * d.nb;
+  float* part = reinterpret_cast<float*>(base + w.part);
+  float* jsq = reinterpret_cast<float*>(base + w.jsq);
+  float* jbest = reinterpret_cast<float*>(base + w.jbest);
+  uint32_t* masks[2] = {reinterpret_cast<uint32_t*>(base + w.m0),
+                        reinterpret_cast<uint32_t*>(base + w.m1)};
+  const bool tb = params->restoration == BSGM_RESTORE_RERANK_TRACK_BEST;
+  uint32_t* best = tb ? reinterpret_cast<uint32_t*>(base + w.best) : nullptr;
+  const int force = params->force_frame_first_block ? 1 : 0, R = params->swap_rounds;
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  e = bsgm::launch_drift_sqnorms_bf16(d, qbar, base + w.qsplit, k, v,
+                                      reinterpret_cast<float2*>(base + w.stats), mz, sqnorm, s);
+  if (e != hipSuccess) return hip_fail(e, "drift score launch");
+  e = bsgm::launch_drift_stream_step(d, hb, force, R, 0, sqnorm, nullptr, nullptr, masks[0],
+                                     set_log, s);
+  if (e != hipSuccess) return hip_fail(e, "drift step launch");
+  int c = 0;
+  for (int round = 1; round <= R; ++round, c ^= 1) {
+    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], part,
+                                         base + w.rsplit, jsq, best, jbest, round - 1, s);
+    if (e != hipSuccess) return hip_fail(e, "drift residual launch");
+    e = bsgm::launch_drift_dot_bf16(d, base + w.qsplit, base + w.rsplit, k, v, mz, dot, s);
+    if (e != hipSuccess) return hip_fail(e, "drift dot launch");
+    e = bsgm::launch_drift_stream_step(d, hb, force, R, round, sqnorm, dot, masks[c],
+                                       masks[c ^ 1], set_log, s);
+    if (e != hipSuccess) return hip_fail(e, "drift step launch");
+  }
+  // J of the last set: the track-best comparison and row_stat need it
+  if (tb || row_stat) {
+    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], part,
+                                         base + w.rsplit, jsq, best, jbest, R, s);
+    if (e != hipSuccess) return hip_fail(e, "drift residual launch");
+  }
+  e = bsgm::launch_drift_stream_emit(d, hb, tb ? best : masks[c], tb ? jbest : jsq, row_ptr,
+                                     col_idx, row_stat, s);
+  if (e != hipSuccess) return hip_fail(e, "drift emit launch");
   return ok();
 }
 

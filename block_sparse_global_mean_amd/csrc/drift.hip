@@ -1348,14 +1348,131 @@ __host__ __device__ inline size_t rerank_lds_bytes(int nb) {
   return align_up16((size_t)nb * 4) * 2 + (size_t)nb * 8 + 2 * words * 4;
 }
 
+// cur := the forced blocks plus the top k of score (ties: lower block), for one
+// row per workgroup of kRrThreads threads (all of them call it; it ends with a
+// barrier). Rows of up to 512 blocks count each block's rank against every
+// key (keys: nb entries of LDS); wider rows find the k-th largest 32-bit
+// priority T by an MSB-first search (one block-wide count per bit), then keep
+// every block above T and the lowest blocks at T. cur: whole 64-block ballots
+// of LDS; cnt: LDS scratch of the block-wide counts.
+__device__ void rr_select(const Dims& d, int force, int k, const float* score,
+                          unsigned long long* keys, uint32_t* cur, int (*cnt)[kRrThreads / 64]) {
+  const int nb = d.nb, WP = (nb + 63) / 64 * 2;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  auto hikey = [&](int j) -> uint32_t {
+    return (force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(score[j]);
+  };
+  int pass = 0;
+  // number of blocks whose priority is at least cand (every thread; one barrier)
+  auto count_ge = [&](uint32_t cand) {
+    int c = 0;
+    for (int j0 = 64 * w; j0 < nb; j0 += kRrThreads) {
+      const int j = j0 + lane;
+      c += __popcll(__ballot(j < nb && hikey(j) >= cand));
+    }
+    if (lane == 0) cnt[pass & 1][w] = c;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int q = 0; q < kRrThreads / 64; ++q) total += cnt[pass & 1][q];
+    ++pass;
+    return total;
+  };
+  if (nb <= 512) {
+    for (int j = t; j < nb; j += kRrThreads) {
+      const bool f = force && block_forced(d, j);
+      const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(score[j]);
+      keys[j] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
+    }
+    __syncthreads();
+    for (int j0 = 64 * w; j0 < WP * 32; j0 += kRrThreads) {
+      const int j = j0 + lane;
+      bool in = false;
+      if (j < nb) {
+        const unsigned long long kj = keys[j];
+        int rank = 0;
+        for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
+        in = rank < k;
+      }
+      const unsigned long long m = __ballot(in);
+      if (lane == 0) {
+        cur[j0 >> 5] = (uint32_t)m;
+        cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (count_ge(cand) >= k) T = cand;
+  }
+  int need = k - (T == 0xFFFFFFFFu ? 0 : count_ge(T + 1u));
+  for (int base = 0; base < nb; base += kRrThreads) {
+    const int j0 = base + 64 * w, j = j0 + lane;
+    const uint32_t hk = j < nb ? hikey(j) : 0u;
+    const bool tie = j < nb && hk == T;
+    const unsigned long long tm = __ballot(tie);
+    if (lane == 0) cnt[pass & 1][w] = __popcll(tm);
+    __syncthreads();
+    int before = 0, ties = 0;
+#pragma unroll
+    for (int q = 0; q < kRrThreads / 64; ++q) {
+      const int c = cnt[pass & 1][q];
+      before += q < w ? c : 0;
+      ties += c;
+    }
+    ++pass;
+    const bool in = j < nb && (hk > T || (tie && before + lanes_below(tm) < need));
+    const unsigned long long m = __ballot(in);
+    if (lane == 0 && j0 < WP * 32) {
+      cur[j0 >> 5] = (uint32_t)m;
+      cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
+    }
+    need -= min(need, ties);
+  }
+  __syncthreads();
+}
+
+// Row r's CSR entry (closed form: every row of head h keeps keep[h] blocks)
+// and its kept blocks in ascending order, from the kept flags `out`; one wave
+// walks the words 64 at a time.
+__device__ void rr_emit(const Dims& d, const HeadBudget& hb, int r, const uint32_t* out,
+                        int32_t* row_ptr, int32_t* col_idx, int lane) {
+  const int nb = d.nb, W = (nb + 31) >> 5;
+  const int bh = r / nb, i = r - bh * nb;
+  const int h = bh % d.H, b = bh / d.H;
+  const int k = hb.keep[h];
+  const long long base = (long long)b * hb.per_batch + hb.head_off[h] + (long long)i * k;
+  if (lane == 0) {
+    row_ptr[r] = (int32_t)base;
+    if (r == d.rows - 1) row_ptr[d.rows] = (int32_t)(base + k);
+  }
+  int off = 0;
+  for (int x0 = 0; x0 < W; x0 += 64) {
+    const int x = x0 + lane;
+    const uint32_t m = x < W ? out[x] : 0u;
+    const int n = __popc(m);
+    int incl = n;   // inclusive scan of the counts over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int pos = off + incl - n;
+    for (uint32_t mm = m; mm; mm &= mm - 1) col_idx[base + pos++] = 32 * x + __ffs(mm) - 1;
+    off += __shfl(incl, 63, 64);
+  }
+}
+
 __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char rsm[];
   const Dims& d = a.d;
   const int nb = d.nb, W = (nb + 31) >> 5, WP = (nb + 63) / 64 * 2;
   const int r = blockIdx.x;
   const int bh = r / nb, i = r - bh * nb;
-  const int h = bh % d.H, b = bh / d.H;
-  const int k = a.hb.keep[h];
+  const int k = a.hb.keep[bh % d.H];
   float* cc = reinterpret_cast<float*>(rsm);                                   // ||c_j||^2
   float* g = reinterpret_cast<float*>(rsm + align_up16((size_t)nb * 4));      // scores
   unsigned long long* keys =
@@ -1404,87 +1521,6 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
   }
   __syncthreads();
 
-  // cur := the forced blocks plus the top k of score (ties: lower block).
-  // Rows of up to 512 blocks count each block's rank against every key; wider
-  // rows find the k-th largest 32-bit priority T by an MSB-first search (one
-  // block-wide count per bit), then keep every block above T and the lowest
-  // blocks at T.
-  auto hikey = [&](const float* score, int j) -> uint32_t {
-    return (a.force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(score[j]);
-  };
-  int pass = 0;
-  // number of blocks whose priority is at least cand (every thread; one barrier)
-  auto count_ge = [&](const float* score, uint32_t cand) {
-    int c = 0;
-    for (int j0 = 64 * w; j0 < nb; j0 += kRrThreads) {
-      const int j = j0 + lane;
-      c += __popcll(__ballot(j < nb && hikey(score, j) >= cand));
-    }
-    if (lane == 0) cnt[pass & 1][w] = c;
-    __syncthreads();
-    int total = 0;
-#pragma unroll
-    for (int q = 0; q < kRrThreads / 64; ++q) total += cnt[pass & 1][q];
-    ++pass;
-    return total;
-  };
-  auto select = [&](const float* score) {
-    if (nb <= 512) {
-      for (int j = t; j < nb; j += kRrThreads) {
-        const bool f = a.force && block_forced(d, j);
-        const unsigned long long hi = f ? 0xFFFFFFFFull : (unsigned long long)orderable(score[j]);
-        keys[j] = (hi << 32) | (unsigned long long)(~(uint32_t)j);
-      }
-      __syncthreads();
-      for (int j0 = 64 * w; j0 < WP * 32; j0 += kRrThreads) {
-        const int j = j0 + lane;
-        bool in = false;
-        if (j < nb) {
-          const unsigned long long kj = keys[j];
-          int rank = 0;
-          for (int q = 0; q < nb; ++q) rank += keys[q] > kj ? 1 : 0;
-          in = rank < k;
-        }
-        const unsigned long long m = __ballot(in);
-        if (lane == 0) {
-          cur[j0 >> 5] = (uint32_t)m;
-          cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
-        }
-      }
-      __syncthreads();
-      return;
-    }
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      if (count_ge(score, cand) >= k) T = cand;
-    }
-    int need = k - (T == 0xFFFFFFFFu ? 0 : count_ge(score, T + 1u));
-    for (int base = 0; base < nb; base += kRrThreads) {
-      const int j0 = base + 64 * w, j = j0 + lane;
-      const uint32_t hk = j < nb ? hikey(score, j) : 0u;
-      const bool tie = j < nb && hk == T;
-      const unsigned long long tm = __ballot(tie);
-      if (lane == 0) cnt[pass & 1][w] = __popcll(tm);
-      __syncthreads();
-      int before = 0, ties = 0;
-#pragma unroll
-      for (int q = 0; q < kRrThreads / 64; ++q) {
-        const int c = cnt[pass & 1][q];
-        before += q < w ? c : 0;
-        ties += c;
-      }
-      ++pass;
-      const bool in = j < nb && (hk > T || (tie && before + lanes_below(tm) < need));
-      const unsigned long long m = __ballot(in);
-      if (lane == 0 && j0 < WP * 32) {
-        cur[j0 >> 5] = (uint32_t)m;
-        cur[(j0 >> 5) + 1] = (uint32_t)(m >> 32);
-      }
-      need -= min(need, ties);
-    }
-    __syncthreads();
-  };
   // rv := r, the sum of the dropped contributions; returns ||r||^2 (every thread).
   // When fewer blocks are kept than dropped, r = o - (sum of the kept rows), which
   // reads the smaller set.
@@ -1521,7 +1557,7 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
         a.set_log[((size_t)r * (a.rounds + 1) + round) * W + x] = (int32_t)cur[x];
   };
 
-  select(cc);
+  rr_select(d, a.force, k, cc, keys, cur, cnt);
   float rr = residual();
   log_set(0);
   float best_rr = rr;
@@ -1534,7 +1570,7 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
       if (c4 == 0) g[j] = 2.f * s + (kept(cur, j) ? cc[j] : -cc[j]);
     }
     __syncthreads();
-    select(g);
+    rr_select(d, a.force, k, g, keys, cur, cnt);
     rr = residual();
     log_set(round);
     if (rr < best_rr) {   // uniform: every thread holds the same rr and best_rr
@@ -1545,29 +1581,7 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
   __syncthreads();
   const uint32_t* out = a.track_best ? best : cur;
   if (t == 0 && a.row_stat) a.row_stat[r] = sqrtf(a.track_best ? best_rr : rr);
-  const long long base = (long long)b * a.hb.per_batch + a.hb.head_off[h] + (long long)i * k;
-  if (t == 0) {
-    a.row_ptr[r] = (int32_t)base;
-    if (r == d.rows - 1) a.row_ptr[d.rows] = (int32_t)(base + k);
-  }
-  // kept blocks in ascending order: wave 0 walks the words 64 at a time
-  if (w == 0) {
-    int off = 0;
-    for (int x0 = 0; x0 < W; x0 += 64) {
-      const int x = x0 + lane;
-      const uint32_t m = x < W ? out[x] : 0u;
-      const int n = __popc(m);
-      int incl = n;   // inclusive scan of the counts over the wave
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      int pos = off + incl - n;
-      for (uint32_t mm = m; mm; mm &= mm - 1) a.col_idx[base + pos++] = 32 * x + __ffs(mm) - 1;
-      off += __shfl(incl, 63, 64);
-    }
-  }
+  if (w == 0) rr_emit(d, a.hb, r, out, a.row_ptr, a.col_idx, lane);
 }
 
 hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int force, int rounds,
@@ -1581,6 +1595,97 @@ hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int f
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_select_drift_rerank, dim3(d.rows), dim3(kRrThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Re-rank rounds in the expanded form (no contributions kept): the same rule
+// as k_select_drift_rerank, with the scores assembled from per-(row, block)
+// scalars that the round kernels recompute, g_j = 2 <r, c_j> -/+ ||c_j||^2.
+// One workgroup per row selects the round's set into a global bitmask.
+// ---------------------------------------------------------------------------
+struct DriftStepArgs {
+  Dims d;
+  HeadBudget hb;
+  int force;
+  int rounds;
+  const float* sqnorm;    // [rows, nb]: ||c_ij||^2
+  const float* dot;       // [rows, nb]: <r_i, c_ij> for the previous set (round > 0)
+  const uint32_t* prev;   // [rows, W]: the previous set (round > 0)
+  uint32_t* next;         // [rows, W]: this round's set
+  int32_t* set_log;       // [rows, rounds + 1, W] or null
+};
+
+__host__ __device__ inline size_t step_lds_bytes(int nb) {
+  return align_up16((size_t)nb * 4) + (size_t)nb * 8 + (size_t)(nb + 63) / 64 * 2 * 4;
+}
+
+__global__ __launch_bounds__(kRrThreads) void k_drift_stream_step(DriftStepArgs a, int round) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char ssm[];
+  const Dims& d = a.d;
+  const int nb = d.nb, W = (nb + 31) >> 5;
+  const int r = blockIdx.x, t = threadIdx.x;
+  const int k = a.hb.keep[(r / nb) % d.H];
+  float* g = reinterpret_cast<float*>(ssm);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(ssm + align_up16((size_t)nb * 4));
+  uint32_t* cur = reinterpret_cast<uint32_t*>(keys + nb);
+  __shared__ int cnt[2][kRrThreads / 64];
+  const float* nr = a.sqnorm + (size_t)r * nb;
+  if (round == 0) {
+    for (int j = t; j < nb; j += kRrThreads) g[j] = nr[j];
+  } else {
+    const float* dt = a.dot + (size_t)r * nb;
+    const uint32_t* pv = a.prev + (size_t)r * W;
+    for (int j = t; j < nb; j += kRrThreads) {
+      const bool in = ((pv[j >> 5] >> (j & 31)) & 1u) != 0;
+      g[j] = 2.f * dt[j] + (in ? nr[j] : -nr[j]);
+    }
+  }
+  __syncthreads();
+  rr_select(d, a.force, k, g, keys, cur, cnt);
+  for (int x = t; x < W; x += kRrThreads) {
+    a.next[(size_t)r * W + x] = cur[x];
+    if (a.set_log) a.set_log[((size_t)r * (a.rounds + 1) + round) * W + x] = (int32_t)cur[x];
+  }
+}
+
+// The CSR of the final sets (one wave per row) and, when asked, J = sqrt(jsq).
+struct DriftEmitArgs {
+  Dims d;
+  HeadBudget hb;
+  const uint32_t* kept;   // [rows, W]
+  const float* jsq;       // [rows]: J^2 of the kept set
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  float* row_stat;
+};
+
+__global__ __launch_bounds__(256) void k_drift_stream_emit(DriftEmitArgs a) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= a.d.rows) return;
+  const int W = (a.d.nb + 31) >> 5;
+  if (lane == 0 && a.row_stat) a.row_stat[r] = sqrtf(a.jsq[r]);
+  rr_emit(a.d, a.hb, r, a.kept + (size_t)r * W, a.row_ptr, a.col_idx, lane);
+}
+
+hipError_t launch_drift_stream_step(const Dims& d, const HeadBudget& hb, int force, int rounds,
+                                    int round, const float* sqnorm, const float* dot,
+                                    const uint32_t* prev, uint32_t* next, int32_t* set_log,
+                                    hipStream_t s) {
+  DriftStepArgs a{d, hb, force, rounds, sqnorm, dot, prev, next, set_log};
+  const size_t lds = step_lds_bytes(d.nb);
+  hipError_t e = hipFuncSetAttribute((const void*)k_drift_stream_step,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_drift_stream_step, dim3(d.rows), dim3(kRrThreads), lds, s, a, round);
+  return hipGetLastError();
+}
+
+hipError_t launch_drift_stream_emit(const Dims& d, const HeadBudget& hb, const uint32_t* kept,
+                                    const float* jsq, int32_t* row_ptr, int32_t* col_idx,
+                                    float* row_stat, hipStream_t s) {
+  DriftEmitArgs a{d, hb, kept, jsq, row_ptr, col_idx, row_stat};
+  hipLaunchKernelGGL(k_drift_stream_emit, dim3((d.rows + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -82,18 +82,21 @@ __global__ __launch_bounds__(256) void k_qbar_split(DriftMfmaArgs a) {
   o[16] = l;
 }
 
-// K fragments of key block j, straight from global memory into registers: for
-// sub-tile t and head-dim step ks, lane l holds the 8 head dims 16 ks + 8 (l / 32)
-// .. +7 of key row 32 t + key_perm(l % 32) (the A operand of S^T = K Qbar^T,
-// the layout k_frag reads from an LDS tile).
+// Row fragments of sub-tile t of a block of 64-wide bf16 rows (K, or V as the
+// A operand of V R^T), straight from global memory into registers: for
+// head-dim step ks, lane l holds the 8 head dims 16 ks + 8 (l / 32) .. +7 of
+// row 32 t + key_perm(l % 32) (the A operand of S^T = K Qbar^T, the layout
+// k_frag reads from an LDS tile).
+__device__ __forceinline__ void load_row_frags(const __bf16* blk, int t, int lane, bf16x8 (&f)[4]) {
+  const __bf16* rowp = blk + (size_t)(32 * t + key_perm(lane & 31)) * 64 + 8 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) f[ks] = *reinterpret_cast<const bf16x8*>(rowp + 16 * ks);
+}
+
 template <int KT>
 __device__ __forceinline__ void load_k_frags(const __bf16* kblk, int lane, bf16x8 (&kf)[KT][4]) {
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const __bf16* rowp = kblk + (size_t)(32 * t + key_perm(lane & 31)) * 64 + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[t][ks] = *reinterpret_cast<const bf16x8*>(rowp + 16 * ks);
-  }
+  for (int t = 0; t < KT; ++t) load_row_frags(kblk, t, lane, kf[t]);
 }
 
 // B operand of S^T = K Qbar^T for the query tile starting at row i0: lane l holds
@@ -259,32 +262,19 @@ __global__ __launch_bounds__(256) void k_drift_norm(DriftMfmaArgs a) {
   if (lane == 0) a.mz[r] = make_float2(m * kLog2e, 1.f / z);
 }
 
-// contrib, score (and zmass when ZM) of one 32-row query tile against the
-// wave's key block, whose V tile sits in LDS at vb. FULL: the block has no
-// padding keys, and the score products of the next sub-tile are issued before
-// this sub-tile's weights, as in stats_tile. Otherwise sub-tiles that hold only
+// c += W V over the wave's key block (V tile in LDS at vb) for one 32-row
+// query tile, with weights W_iu = exp2(s_iu c2 - mzx) * wsc (lane l's query is
+// l % 32; wsc = 0 leaves its row unchanged). c[mt]: rows = queries
+// 8 (x / 4) + 4 (l / 32) + x % 4 of the tile, column = head dim 32 mt + l % 32.
+// ZM: wsum collects the lane's weights. FULL: the block has no padding keys,
+// and the score products of the next sub-tile are issued before this
+// sub-tile's weights, as in stats_tile. Otherwise sub-tiles that hold only
 // padding keys (weights all zero) are skipped.
 template <int KT, bool ZM, bool FULL>
-__device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveItem& it, int rt,
-                                             int vlen, int lane, const bf16x8 (&kf)[KT][4],
-                                             const unsigned char* vb) {
-  const Dims& d = a.d;
-  const int n = lane & 31, hh = lane >> 5;
-  const int i = 32 * rt + n;
-  const int j = it.j, bh = it.bh;
-  bf16x8 qh[4], qm[4], ql[4];
-  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
-  const float2 mz = i < d.nb ? a.mz[(size_t)bh * d.nb + i] : make_float2(0.f, 0.f);
-  const float c2 = d.scale * kLog2e;
-
-  // c[mt]: rows = queries 8 (x / 4) + 4 (l / 32) + x % 4 of the tile, column =
-  // head dim 32 mt + l % 32.
-  f32x16 c[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
-  float wsum = 0.f;
+__device__ __forceinline__ void weigh_values(const bf16x8 (&kf)[KT][4], const unsigned char* vb,
+                                             const bf16x8 (&qh)[4], const bf16x8 (&qm)[4],
+                                             const bf16x8 (&ql)[4], float mzx, float wsc, float c2,
+                                             int vlen, int lane, f32x16 (&c)[2], float& wsum) {
   f32x16 s = qk_tile(kf[0], qh, qm, ql);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
@@ -300,7 +290,7 @@ __device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveI
       float p[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        p[x] = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mz.x)) * mz.y;
+        p[x] = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mzx)) * wsc;
         if (ZM) wsum += p[x];
       }
       bf16x8 ph, pm, pl;
@@ -315,39 +305,67 @@ __device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveI
     }
     if (FULL && t + 1 < KT) s = sn;
   }
+}
+
+// contrib, score (and zmass when ZM) of one 32-row query tile against the
+// wave's key block, whose V tile sits in LDS at vb. NC: no contributions are
+// written, and score receives the squared norm ||contrib_ij||^2 instead.
+template <int KT, bool ZM, bool FULL, bool NC>
+__device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveItem& it, int rt,
+                                             int vlen, int lane, const bf16x8 (&kf)[KT][4],
+                                             const unsigned char* vb) {
+  const Dims& d = a.d;
+  const int n = lane & 31, hh = lane >> 5;
+  const int i = 32 * rt + n;
+  const int j = it.j, bh = it.bh;
+  bf16x8 qh[4], qm[4], ql[4];
+  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  const float2 mz = i < d.nb ? a.mz[(size_t)bh * d.nb + i] : make_float2(0.f, 0.f);
+  const float c2 = d.scale * kLog2e;
+
+  f32x16 c[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
+  float wsum = 0.f;
+  weigh_values<KT, ZM, FULL>(kf, vb, qh, qm, ql, mz.x, mz.y, c2, vlen, lane, c, wsum);
 
   // contrib rows: lanes 0-31 write 128 contiguous bytes of one query row,
   // lanes 32-63 those of the row 4 below. Raw buffer stores off a wave-uniform
   // resource at (b, h, row tile, j): the lane's byte offset in a VGPR, the
   // row's (a multiple of the row pitch) in an SGPR, so no store needs address
   // arithmetic. The tile spans under 32 * nb * 256 bytes.
-  const uint32_t rsb = (uint32_t)d.nb * 256u;   // bytes between query rows
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      a.contrib + (((size_t)bh * d.nb + 32 * rt) * d.nb + j) * 64, 0, (int)(32u * rsb), 0x00020000);
-  const uint32_t off0 = (uint32_t)(4 * hh) * rsb + (uint32_t)n * 4u;
-  if (32 * rt + 32 <= d.nb) {
+  if (!NC) {
+    const uint32_t rsb = (uint32_t)d.nb * 256u;   // bytes between query rows
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.contrib + (((size_t)bh * d.nb + 32 * rt) * d.nb + j) * 64, 0, (int)(32u * rsb), 0x00020000);
+    const uint32_t off0 = (uint32_t)(4 * hh) * rsb + (uint32_t)n * 4u;
+    if (32 * rt + 32 <= d.nb) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int so = (8 * (x >> 2) + (x & 3)) * (int)rsb;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0][x]), rs, (int)off0, so, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[1][x]), rs, (int)off0 + 128, so, 0);
-    }
-  } else {
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int rr = 8 * (x >> 2) + (x & 3);
-      if (32 * rt + 4 * hh + rr < d.nb) {
-        const int so = rr * (int)rsb;
+      for (int x = 0; x < 16; ++x) {
+        const int so = (8 * (x >> 2) + (x & 3)) * (int)rsb;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0][x]), rs, (int)off0, so, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[1][x]), rs, (int)off0 + 128, so, 0);
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int rr = 8 * (x >> 2) + (x & 3);
+        if (32 * rt + 4 * hh + rr < d.nb) {
+          const int so = rr * (int)rsb;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0][x]), rs, (int)off0, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[1][x]), rs, (int)off0 + 128, so, 0);
+        }
       }
     }
   }
 
   // score: sum of squares over the 64 head dims (32 lanes x 2 tiles) of each
   // of the 16 rows a lane holds, with one fixed contraction so that the
-  // rounding does not depend on instruction scheduling. Halving exchanges leave lane n with the
-  // total of row x = 8 b4 + 4 b3 + 2 b2 + b1 (b_k = bit k of n).
+  // rounding does not depend on instruction scheduling. Halving exchanges
+  // leave lane n with the total of row x = 8 b4 + 4 b3 + 2 b2 + b1 (b_k = bit
+  // k of n).
   float v[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) v[x] = fmaf(c[0][x], c[0][x], c[1][x] * c[1][x]);
@@ -367,7 +385,7 @@ __device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveI
                  ((n >> 1) & 1);
   const int qi = 32 * rt + 8 * (xr >> 2) + 4 * hh + (xr & 3);
   if ((n & 1) == 0 && qi < d.nb)
-    a.score[((size_t)bh * d.nb + qi) * d.nb + j] = sqrtf(v[0]);
+    a.score[((size_t)bh * d.nb + qi) * d.nb + j] = NC ? v[0] : sqrtf(v[0]);
   if (ZM) {
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsum), __float_as_uint(wsum),
                                                      false, false);
@@ -379,7 +397,17 @@ __device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveI
 // Each wave transposes its block's V through a private LDS tile (swizzled
 // 128-byte rows, read back with the transposing LDS reads of v_frag) and keeps
 // its K fragments in registers.
-template <int BLK, bool ZM>
+template <int BLK>
+__device__ __forceinline__ void stage_v(const __bf16* src, int lane, unsigned char* vb) {
+#pragma unroll
+  for (int m = 0; m < BLK / 8; ++m) {
+    const int q = lane + 64 * m, row = q >> 3, pc = q & 7;
+    *reinterpret_cast<uint4*>(vb + row * 128 + ((pc ^ swz(row)) << 4)) =
+        *reinterpret_cast<const uint4*>(src + (size_t)row * 64 + pc * 8);
+  }
+}
+
+template <int BLK, bool ZM, bool NC>
 __global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a, int rtpw) {
   constexpr int KT = BLK / 32, TB = BLK * 128;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
@@ -389,23 +417,173 @@ __global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a, 
   const int lane = threadIdx.x & 63;
   unsigned char* vb = smem + (threadIdx.x >> 6) * TB;
   const size_t tok0 = (size_t)it.bh * d.N + (size_t)it.j * BLK;
-  {
-    const __bf16* src = a.v + tok0 * 64;
-#pragma unroll
-    for (int m = 0; m < BLK / 8; ++m) {
-      const int q = lane + 64 * m, row = q >> 3, pc = q & 7;
-      *reinterpret_cast<uint4*>(vb + row * 128 + ((pc ^ swz(row)) << 4)) =
-          *reinterpret_cast<const uint4*>(src + (size_t)row * 64 + pc * 8);
-    }
-  }
+  stage_v<BLK>(a.v + tok0 * 64, lane, vb);
   bf16x8 kf[KT][4];
   load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
   const int vlen = block_vlen(d, it.j);
   // (the pipelined form needs 16 more registers than the zmass variant has)
   if (vlen == BLK && !ZM)
-    for (int rt = it.rt0; rt < it.rt1; ++rt) contrib_tile<KT, ZM, true>(a, it, rt, vlen, lane, kf, vb);
+    for (int rt = it.rt0; rt < it.rt1; ++rt)
+      contrib_tile<KT, ZM, true, NC>(a, it, rt, vlen, lane, kf, vb);
   else
-    for (int rt = it.rt0; rt < it.rt1; ++rt) contrib_tile<KT, ZM, false>(a, it, rt, vlen, lane, kf, vb);
+    for (int rt = it.rt0; rt < it.rt1; ++rt)
+      contrib_tile<KT, ZM, false, NC>(a, it, rt, vlen, lane, kf, vb);
+}
+
+// ---------------------------------------------------------------------------
+// Re-rank rounds in the expanded form, without the contributions. With
+// r_i = sum_{j in D_i} contrib_ij the residual of row i's drop set D_i, a
+// round scores block j by 2 <r_i, contrib_ij> -/+ ||contrib_ij||^2, and
+//   <r_i, contrib_ij> = sum_{u in j} w_iu <v_u, r_i>,   w_iu = exp(l_iu - M_i) / Z_i,
+// so each round needs r_i (a weighted value sum over the dropped blocks) and
+// then one scalar per (i, j), both recomputed from qbar, K, V and (M_i, Z_i).
+// Nothing of size rows x nb x 64 is kept.
+// ---------------------------------------------------------------------------
+struct DriftRoundArgs {
+  const uint32_t* kept;   // [rows, W]: the round's kept set (bit j % 32 of word j / 32)
+  float* part;            // [rows, ngroups, 64]: per group of key blocks, the dropped sum
+  int ngroups;
+  __bf16* rsplit;         // [rows, 3, 64]: r as hi, mid, lo bf16 terms
+  float* dot;             // [rows, nb]: <r_i, contrib_ij>
+};
+
+// Residual partial sums: one wave per (b, h, 32-row query tile, run of
+// consecutive key blocks). For each block of its run the wave stages V and K
+// as the contribution kernel does and adds W V, the weights of rows that keep
+// the block set to zero; a block that every row of the tile keeps is skipped.
+template <int BLK>
+__global__ __launch_bounds__(256, 2) void k_drift_dropsum(DriftMfmaArgs a, DriftRoundArgs r) {
+  constexpr int KT = BLK / 32, TB = BLK * 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+  const Dims& d = a.d;
+  const int nrt = (d.nb + 31) / 32, G = r.ngroups, W = (d.nb + 31) >> 5;
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (gw >= d.B * d.H * nrt * G) return;
+  const int g = gw % G, rt = (gw / G) % nrt, bh = gw / (G * nrt);
+  const int j0 = (int)((long long)g * d.nb / G), j1 = (int)((long long)(g + 1) * d.nb / G);
+  const int lane = threadIdx.x & 63, n = lane & 31, hh = lane >> 5;
+  const int i = 32 * rt + n;
+  unsigned char* vb = smem + (threadIdx.x >> 6) * TB;
+  bf16x8 qh[4], qm[4], ql[4];
+  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  const float2 mz = i < d.nb ? a.mz[(size_t)bh * d.nb + i] : make_float2(0.f, 0.f);
+  const float c2 = d.scale * kLog2e;
+  const uint32_t* krow = r.kept + ((size_t)bh * d.nb + min(i, d.nb - 1)) * W;
+  f32x16 c[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
+  float wsum = 0.f;   // (unused)
+  uint32_t word = 0;
+  int wi = -1;
+  for (int j = j0; j < j1; ++j) {
+    if ((j >> 5) != wi) {
+      wi = j >> 5;
+      word = krow[wi];
+    }
+    const bool drop = i < d.nb && ((word >> (j & 31)) & 1u) == 0;
+    if (__ballot(drop) == 0ull) continue;   // uniform
+    const size_t tok0 = (size_t)bh * d.N + (size_t)j * BLK;
+    stage_v<BLK>(a.v + tok0 * 64, lane, vb);
+    bf16x8 kf[KT][4];
+    load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
+    const int vlen = block_vlen(d, j);
+    // (the pipelined form of full blocks does not fit the registers left here)
+    weigh_values<KT, false, false>(kf, vb, qh, qm, ql, mz.x, drop ? mz.y : 0.f, c2, vlen, lane,
+                                   c, wsum);
+  }
+  // row q of the tile: [row, g, 64]; lanes 0-31 write 128 contiguous bytes
+  float* prow = r.part + (((size_t)bh * d.nb + 32 * rt) * G + g) * 64;
+  const size_t rs = (size_t)G * 64;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int q = 8 * (x >> 2) + 4 * hh + (x & 3);
+    if (32 * rt + q < d.nb) {
+      prow[q * rs + n] = c[0][x];
+      prow[q * rs + 32 + n] = c[1][x];
+    }
+  }
+}
+
+// Per row (one wave): r = the sum of the group partials in group order, its
+// three bf16 terms for the dot products, and J^2 = ||r||^2. With best, also
+// keeps the kept set of least J so far (round 0 starts it; ties keep the
+// earlier set).
+__global__ __launch_bounds__(256) void k_drift_resid(DriftRoundArgs r, int rows, int W, int round,
+                                                     float* jsq, uint32_t* best, float* jbest) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* p = r.part + (size_t)row * r.ngroups * 64 + lane;
+  float x = 0.f;
+  for (int g = 0; g < r.ngroups; ++g) x += p[(size_t)g * 64];
+  const __bf16 h = (__bf16)x;
+  const float r1 = x - (float)h;
+  const __bf16 m = (__bf16)r1;
+  const __bf16 l = (__bf16)(r1 - (float)m);
+  __bf16* o = r.rsplit + (size_t)row * 192 + lane;
+  o[0] = h;
+  o[64] = m;
+  o[128] = l;
+  const float j2 = wave_sum(x * x);   // bitwise the same in every lane
+  if (lane == 0) jsq[row] = j2;
+  if (best) {
+    const bool take = round == 0 || j2 < jbest[row];
+    if (take) {
+      if (lane == 0) jbest[row] = j2;
+      for (int w = lane; w < W; w += 64) best[(size_t)row * W + w] = r.kept[(size_t)row * W + w];
+    }
+  }
+}
+
+// <r_i, contrib_ij> of one 32-row query tile against the wave's key block:
+// X = V R^T on the matrix cores (V rows as the A operand, as K in the scores;
+// r as three bf16 terms, so the products are exact), then the weighted sum
+// sum_u w_iu X_ui over the block's real keys. X has the layout of S^T.
+template <int KT>
+__device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoundArgs& r,
+                                         const WaveItem& it, int rt, int vlen, int lane,
+                                         const bf16x8 (&kf)[KT][4], const __bf16* vblk) {
+  const Dims& d = a.d;
+  const int i = 32 * rt + (lane & 31);
+  bf16x8 qh[4], qm[4], ql[4], rh[4], rm[4], rl[4];
+  load_qsplit(a.qsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  load_qsplit(r.rsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, rh, rm, rl);
+  const float2 mz = i < d.nb ? a.mz[(size_t)it.bh * d.nb + i] : make_float2(0.f, 0.f);
+  const float c2 = d.scale * kLog2e;
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
+    f32x16 s = qk_tile(kf[t], qh, qm, ql);
+    mask_padding(s, t, vlen, lane);   // weight 0 for padding keys
+    bf16x8 vf[4];
+    load_row_frags(vblk, t, lane, vf);
+    const f32x16 xv = qk_tile(vf, rh, rm, rl);
+#pragma unroll
+    for (int x = 0; x < 16; ++x)
+      acc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[x], c2, -mz.x)) * mz.y, xv[x], acc);
+  }
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
+                                                   false, false);
+  const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  if (lane < 32 && i < d.nb) r.dot[((size_t)it.bh * d.nb + i) * d.nb + it.j] = tot;
+}
+
+// Same work split as the statistics: one wave per (b, h, key block, run of
+// query tiles), K fragments in registers, V fragments loaded per sub-tile.
+template <int BLK>
+__global__ __launch_bounds__(256, 2) void k_drift_dot(DriftMfmaArgs a, DriftRoundArgs r, int rtpw) {
+  constexpr int KT = BLK / 32;
+  const Dims& d = a.d;
+  WaveItem it;
+  if (!wave_item(d, rtpw, it)) return;
+  const int lane = threadIdx.x & 63;
+  const size_t tok0 = (size_t)it.bh * d.N + (size_t)it.j * BLK;
+  bf16x8 kf[KT][4];
+  load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
+  const int vlen = block_vlen(d, it.j);
+  for (int rt = it.rt0; rt < it.rt1; ++rt) dot_tile<KT>(a, r, it, rt, vlen, lane, kf, a.v + tok0 * 64);
 }
 
 // Query tiles per wave for `slots` resident waves on the chip: among the
@@ -441,20 +619,17 @@ static int compute_units() {
   return cu;
 }
 
-hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
-                                     const void* v, float2* stats, float2* mz, float* contrib,
-                                     float* score, float* zmass, hipStream_t s) {
-  DriftMfmaArgs a{d, qbar, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, stats, mz, contrib,
-                  score, zmass};
+// qbar's split terms, the per-(i, j) statistics and the per-row (M_i, Z_i).
+static hipError_t launch_drift_stats(const DriftMfmaArgs& a, hipStream_t s) {
+  const Dims& d = a.d;
   const int nrt = (d.nb + 31) / 32;
-  const int cu = compute_units();
   const long long bjs = (long long)d.B * d.H * d.nb;
   hipLaunchKernelGGL(k_qbar_split, dim3((d.rows * 8 + 255) / 256), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     // stats: 3 waves per SIMD
-    const int r = tiles_per_wave(d, cu * 12);
+    const int r = tiles_per_wave(d, compute_units() * 12);
     const long long waves = bjs * ((nrt + r - 1) / r);
     const dim3 grid((unsigned)((waves + 3) / 4));
     if (d.blk == 128)
@@ -465,22 +640,94 @@ hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, void* qsp
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_drift_norm, dim3((d.rows + 3) / 4), dim3(256), 0, s, a);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+// Grid of a per-(b, h, key block, run of query tiles) kernel at `slots`
+// resident waves; r receives the run length.
+static dim3 wave_grid(const Dims& d, int slots, int& r) {
+  const int nrt = (d.nb + 31) / 32;
+  r = tiles_per_wave(d, slots);
+  const long long waves = (long long)d.B * d.H * d.nb * ((nrt + r - 1) / r);
+  return dim3((unsigned)((waves + 3) / 4));
+}
+
+template <bool ZM, bool NC>
+static void launch_contrib(const DriftMfmaArgs& a, hipStream_t s) {
+  // contributions: 2 waves per SIMD
+  int r = 0;
+  const dim3 grid = wave_grid(a.d, compute_units() * 8, r);
+  if (a.d.blk == 128)
+    hipLaunchKernelGGL((k_drift_contrib_mfma<128, ZM, NC>), grid, dim3(256), 0, s, a, r);
+  else
+    hipLaunchKernelGGL((k_drift_contrib_mfma<64, ZM, NC>), grid, dim3(256), 0, s, a, r);
+}
+
+hipError_t launch_drift_contrib_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
+                                     const void* v, float2* stats, float2* mz, float* contrib,
+                                     float* score, float* zmass, hipStream_t s) {
+  DriftMfmaArgs a{d, qbar, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, stats, mz, contrib,
+                  score, zmass};
+  hipError_t e = launch_drift_stats(a, s);
   if (e != hipSuccess) return e;
-  {
-    // contributions: 2 waves per SIMD
-    const int r = tiles_per_wave(d, cu * 8);
-    const long long waves = bjs * ((nrt + r - 1) / r);
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    const bool zm = zmass != nullptr;
-    if (d.blk == 128) {
-      if (zm) hipLaunchKernelGGL((k_drift_contrib_mfma<128, true>), grid, dim3(256), 0, s, a, r);
-      else hipLaunchKernelGGL((k_drift_contrib_mfma<128, false>), grid, dim3(256), 0, s, a, r);
-    } else {
-      if (zm) hipLaunchKernelGGL((k_drift_contrib_mfma<64, true>), grid, dim3(256), 0, s, a, r);
-      else hipLaunchKernelGGL((k_drift_contrib_mfma<64, false>), grid, dim3(256), 0, s, a, r);
-    }
-  }
+  if (zmass) launch_contrib<true, false>(a, s);
+  else launch_contrib<false, false>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_drift_sqnorms_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
+                                     const void* v, float2* stats, float2* mz, float* sqnorm,
+                                     hipStream_t s) {
+  DriftMfmaArgs a{d, qbar, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, stats, mz, nullptr,
+                  sqnorm, nullptr};
+  hipError_t e = launch_drift_stats(a, s);
+  if (e != hipSuccess) return e;
+  launch_contrib<false, true>(a, s);
+  return hipGetLastError();
+}
+
+int drift_round_groups(const Dims& d) {
+  // about 2048 waves (two workgroups of 4 per CU on 256 CUs), at most 16 groups
+  const long long tiles = (long long)d.B * d.H * ((d.nb + 31) / 32);
+  long long g = (2048 + tiles - 1) / tiles;
+  if (g > 16) g = 16;
+  if (g > d.nb) g = d.nb;
+  return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const void* k,
+                                      const void* v, const float2* mz, const uint32_t* kept,
+                                      float* part, void* rsplit, float* jsq, uint32_t* best,
+                                      float* jbest, int round, hipStream_t s) {
+  DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
+                  const_cast<float2*>(mz), nullptr, nullptr, nullptr};
+  const int G = drift_round_groups(d);
+  DriftRoundArgs r{kept, part, G, (__bf16*)rsplit, nullptr};
+  const long long waves = (long long)d.B * d.H * ((d.nb + 31) / 32) * G;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (d.blk == 128)
+    hipLaunchKernelGGL(k_drift_dropsum<128>, grid, dim3(256), 0, s, a, r);
+  else
+    hipLaunchKernelGGL(k_drift_dropsum<64>, grid, dim3(256), 0, s, a, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_drift_resid, dim3((d.rows + 3) / 4), dim3(256), 0, s, r, d.rows,
+                     (d.nb + 31) >> 5, round, jsq, best, jbest);
+  return hipGetLastError();
+}
+
+hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* rsplit,
+                                 const void* k, const void* v, const float2* mz, float* dot,
+                                 hipStream_t s) {
+  DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
+                  const_cast<float2*>(mz), nullptr, nullptr, nullptr};
+  DriftRoundArgs r{nullptr, nullptr, 0, (__bf16*)rsplit, dot};
+  int rt = 0;
+  const dim3 grid = wave_grid(d, compute_units() * 8, rt);
+  if (d.blk == 128)
+    hipLaunchKernelGGL(k_drift_dot<128>, grid, dim3(256), 0, s, a, r, rt);
+  else
+    hipLaunchKernelGGL(k_drift_dot<64>, grid, dim3(256), 0, s, a, r, rt);
   return hipGetLastError();
 }
 

@@ -88,6 +88,35 @@ hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int f
                                       int32_t* col_idx, float* row_stat, int32_t* set_log,
                                       hipStream_t s);
 
+// Re-rank rounds in the expanded form, without the contributions (bf16 K and
+// V). sqnorm: the squared drift scores ||c_ij||^2 [rows, nb], after qbar's
+// split terms, the statistics and (M_i, Z_i) as launch_drift_contrib_bf16.
+hipError_t launch_drift_sqnorms_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
+                                     const void* v, float2* stats, float2* mz, float* sqnorm,
+                                     hipStream_t s);
+// Groups of key blocks of the residual pass (part holds [rows, groups, 64]).
+int drift_round_groups(const Dims& d);
+// The residual r_i of the drop set of `kept` ([rows, ceil(nb / 32)] bitmasks),
+// as three bf16 terms in rsplit [rows, 3, 64], and J^2 = ||r_i||^2 in jsq; with
+// best non-null, best/jbest keep the set of least J (round 0 starts them).
+hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const void* k,
+                                      const void* v, const float2* mz, const uint32_t* kept,
+                                      float* part, void* rsplit, float* jsq, uint32_t* best,
+                                      float* jbest, int round, hipStream_t s);
+// dot[i, j] = <r_i, c_ij> for every block, recomputed from qbar, K and V.
+hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* rsplit,
+                                 const void* k, const void* v, const float2* mz, float* dot,
+                                 hipStream_t s);
+// One round's selection from sqnorm and dot (round 0: sqnorm alone), into next.
+hipError_t launch_drift_stream_step(const Dims& d, const HeadBudget& hb, int force, int rounds,
+                                    int round, const float* sqnorm, const float* dot,
+                                    const uint32_t* prev, uint32_t* next, int32_t* set_log,
+                                    hipStream_t s);
+// The CSR of the kept sets, and row_stat = sqrt(jsq) when row_stat is non-null.
+hipError_t launch_drift_stream_emit(const Dims& d, const HeadBudget& hb, const uint32_t* kept,
+                                    const float* jsq, int32_t* row_ptr, int32_t* col_idx,
+                                    float* row_stat, hipStream_t s);
+
 // Block-sparse attention forward. ws: attn_workspace_bytes(d) bytes of device
 // scratch (enables the fp16 logits: an fp16 copy of K, a range flag per
 // (b, h, key block) and a fallback flag per row), or null (bf16 logits only).

@@ -199,6 +199,43 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
                        float* row_stat, float* scores_out, int32_t* swap_log,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Drift selection by re-rank rounds without the contributions ([ReSS]
+ * Table 1: drift scoring with and without expansion, and its scoring memory).
+ * The same selection as bsgm_select_blocks with mode DRIFT, objective
+ * DROPPED_SUM and restoration RERANK or RERANK_TRACK_BEST, computed from Q,
+ * K and V directly. A round's score expands as
+ *   g_j = 2 <r, contrib_j> + ||contrib_j||^2   (j kept; minus for j dropped),
+ *   <r, contrib_ij> = sum_{u in block j} e_u <v_u, r> / sum_u e_u,
+ * so each round recomputes the residual r of its drop set (a weighted value
+ * sum over the dropped blocks) and then one scalar per (row, block) from the
+ * keys and values; the row statistics (max and sum of exp) are computed once.
+ * Scoring memory is per (row, block) scalars, not [B,H,Nb,Nb,D] floats; the
+ * cost is two passes over K and V per round.
+ *   params     mode BSGM_SEL_DRIFT, keep_per_head, force_frame_first_block,
+ *              swap_rounds (>= 0), drift_objective DROPPED_SUM, restoration
+ *              RERANK or RERANK_TRACK_BEST
+ *   q, k, v    device [B,H,N,D] bf16
+ *   row_ptr, col_idx, col_capacity  as bsgm_select_blocks
+ *   row_stat   device float [B*H*Nb] or NULL: the drift J of the returned set
+ *   set_log    device int32 [B*H*Nb, swap_rounds + 1, ceil(Nb / 32)] or NULL:
+ *              the kept set of the initial selection and of each round, as
+ *              bsgm_select_blocks' swap_log in the re-rank modes
+ *   ws         device, >= bsgm_drift_streamed_workspace_bytes(layout) bytes
+ * Errors: BSGM_E_ARG for a NULL q, k, v, row_ptr, col_idx or ws, another mode,
+ * or negative swap_rounds; BSGM_E_UNSUPPORTED for fp32 layouts, the best-swap
+ * rule or the renormalised objective; BSGM_E_CAPACITY, BSGM_E_WORKSPACE as
+ * bsgm_select_blocks. Rows of any number of blocks.
+ */
+int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_params* params,
+                               const void* q, const void* k, const void* v, int32_t* row_ptr,
+                               int32_t* col_idx, int64_t col_capacity, float* row_stat,
+                               int32_t* set_log, void* ws, size_t ws_bytes, void* stream);
+
+/* Device workspace of bsgm_select_drift_streamed: about
+ * B*H*Nb * (8*Nb + 1040 + 12*ceil(Nb/32)) bytes plus a partial residual of at
+ * most 16 x 64 floats per row; 0 if the layout is invalid. */
+size_t bsgm_drift_streamed_workspace_bytes(const bsgm_layout* layout);
+
 /* TOPK or CDF selection from pooled means the caller already holds (from
  * bsgm_pool_blocks of Q and of K): the second half of bsgm_select_blocks, with
  * the same results bit for bit when given the same means. A caller can thus

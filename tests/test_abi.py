@@ -113,6 +113,47 @@ def test_select_argument_errors():
     assert _select(big, mode=2, keep=(5, 5), contrib=16)[0] == -2      # 4200 blocks > 4096
 
 
+def _streamed(lay, mode=2, keep=(3, 5), force=False, rounds=2, objective=0,
+              restoration=bsgm.RERANK_TRACK_BEST, cap=None, wsb=None, q=16, k=16, v=16, rp=16,
+              ci=16, wsp=256):
+    lib = bsgm.library()
+    c = _lib.c_layout(lay)
+    P, arr = _lib.c_params(mode, keep, 0.9, force, rounds, objective, restoration)
+    need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
+    cap = need if cap is None else cap
+    wsb = lib.bsgm_drift_streamed_workspace_bytes(ctypes.byref(c)) if wsb is None else wsb
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.bsgm_select_drift_streamed(ctypes.byref(c), ctypes.byref(P), p(q), p(k), p(v),
+                                          p(rp), p(ci), cap, None, None, p(wsp), wsb, None)
+
+
+def test_streamed_drift_workspace_and_errors():
+    lay = L()                             # 2 heads x 8 blocks: 16 rows
+    rows, nb, words = 16, 8, 1
+    al = lambda x: (x + 255) // 256 * 256
+    groups = 8                            # min(16, nb, ceil(2048 / (2 heads x 1 query tile)))
+    # pooled q and its bf16 terms; per (row, block) two floats (statistics, then
+    # the squared scores and the round's dot products); M and 1/Z; the group
+    # partials of the residual and its bf16 terms; J^2 and the best J^2; three
+    # kept-set bitmasks
+    expect = (al(rows * 64 * 4) + al(rows * 192 * 2) + al(rows * nb * 8) + al(rows * 8)
+              + al(rows * groups * 64 * 4) + al(rows * 192 * 2) + 2 * al(rows * 4)
+              + 3 * al(rows * words * 4))
+    c = _lib.c_layout(lay)
+    assert bsgm.library().bsgm_drift_streamed_workspace_bytes(ctypes.byref(c)) == expect
+    assert bsgm.drift_streamed_workspace_bytes(lay) == expect
+    assert _streamed(lay, keep=(0, 2)) == -1
+    assert _streamed(lay, mode=0) == -1
+    assert _streamed(lay, restoration=bsgm.BEST_SWAP) == -2
+    assert _streamed(lay, objective=1) == -2
+    assert _streamed(lay, rounds=-1) == -1
+    assert _streamed(L(dtype="f32")) == -2
+    for name in ("q", "k", "v", "rp", "ci", "wsp"):
+        assert _streamed(lay, **{name: None}) == -1, name
+    assert _streamed(lay, cap=8 * 3 + 8 * 5 - 1) == -3
+    assert _streamed(lay, wsb=expect - 1) == -4
+
+
 def _fused(lay, mode=0, keep=(2, 2), force=False, cap=None, wsb=None, wsp=256, q=16, k=16,
            rp=16, ci=16):
     lib = bsgm.library()

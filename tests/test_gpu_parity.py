@@ -1335,17 +1335,18 @@ def check_rerank(lay, vals, keep, rounds, track_best, force, contrib_g, rpn, cin
     words = (nb + 31) // 32
     qbar_cache = {}
     differ = 0
-    for (h, i) in rows_to_check:
-        if h not in qbar_cache:
-            qbar_cache[h] = oracle.pool(q[:, h:h + 1], lay)[0, 0]
-        chat, _, _ = oracle.drift_row(qbar_cache[h][i], k[0, h], v[0, h], lay)
-        r = h * nb + i
+    for row in rows_to_check:
+        b, h, i = row if len(row) == 3 else (0,) + tuple(row)
+        if (b, h) not in qbar_cache:
+            qbar_cache[(b, h)] = oracle.pool(q[b:b + 1, h:h + 1], lay)[0, 0]
+        chat, _, _ = oracle.drift_row(qbar_cache[(b, h)][i], k[b, h], v[b, h], lay)
+        r = (b * lay.heads + h) * nb + i
         lg = log_g[r].reshape(rounds + 1, words)
         sets = [parity.mask_words_to_set(lg[x], nb) for x in range(rounds + 1)]
         ok, why = parity.rerank_valid(sets, rows[r], chat, int(keep[h]), forced, track_best)
-        assert ok, f"row {(h, i)}: {why}"
+        assert ok, f"row {(b, h, i)}: {why}"
         jref = oracle.drift_j(chat, rows[r])
-        assert abs(stat_g[r] - jref) <= 1e-4 * max(jref, 1e-30), (h, i, stat_g[r], jref)
+        assert abs(stat_g[r] - jref) <= 1e-4 * max(jref, 1e-30), (b, h, i, stat_g[r], jref)
         kept_ref, _, _, _ = oracle.rerank_row(chat, int(keep[h]), rounds, forced, track_best)
         differ += kept_ref != rows[r]
     return differ
@@ -1444,6 +1445,141 @@ def test_drift_rerank_wide_and_small_rows(dev, nb, frames):
     keep = np.array([max(4, nb // 5)], dtype=np.int32)
     rows = [(0, i) for i in spread_rows(nb, 24)]
     run_rerank(dev, lay, host, vals, keep, 5, True, False, rows, f"re-rank rows of {nb} blocks")
+
+
+# --------------------------------------------------------------------------
+# re-rank rounds in the expanded form (no contributions kept)
+def run_streamed(dev, lay, host, vals, keep, rounds, track_best, force, rows_to_check, label,
+                 min_same=0.9):
+    """The streamed selection on every checked row against the oracle (the same
+    rule as the materialised re-rank: logged sets replay as top-k choices, the
+    returned set, its J), then the logged sets of every row against the
+    materialised form's: the two round the same sums differently, so only
+    near-ties may differ, and at least min_same of the rows must match."""
+    q, k, v = (to_dev(x, dev) for x in host)
+    nb = lay.nblocks
+    rows = lay.batch * lay.heads * nb
+    words = (nb + 31) // 32
+    log = torch.full((rows, rounds + 1, words), -7, dtype=torch.int32, device=dev)
+    say(f"{label}: streamed selection")
+    rp, ci, st = bsgm.select_drift_streamed(lay, keep, q, k, v, swap_rounds=rounds,
+                                            track_best=track_best, force=force, set_log=log)
+    torch.cuda.synchronize()
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    parity.check_csr_wellformed(rpn, cin, nb)
+    assert rpn[-1] == lay.batch * nb * int(np.sum(keep))
+    differ = check_rerank(lay, vals, keep, rounds, track_best, force, None, rpn, cin,
+                          st.cpu().numpy(), log.cpu().numpy(), rows_to_check)
+    say(f"{label}: {len(rows_to_check)} rows checked, {differ} with sets other than the oracle's")
+    contrib, _ = bsgm.drift_scores(lay, q, k, v)
+    log_m = torch.full_like(log, -7)
+    rule = bsgm.RERANK_TRACK_BEST if track_best else bsgm.RERANK
+    rp_m, ci_m, _ = bsgm.select_blocks(lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds,
+                                       force=force, swap_log=log_m, restoration=rule)
+    torch.cuda.synchronize()
+    del contrib
+    same = int((log == log_m).all(dim=2).all(dim=1).sum().item())
+    say(f"{label}: {rows - same} of {rows} rows log other sets than the materialised form")
+    assert same >= min_same * rows, (same, rows)
+    return rp, ci, st, log
+
+
+@pytest.mark.parametrize("rounds,track_best,force", [(5, True, False), (10, False, True),
+                                                     (0, True, False)])
+def test_drift_streamed_layer16(dev, rounds, track_best, force):
+    """16 frames, 2 heads (176 key blocks, keep 35): the expanded-form re-rank
+    at 0, 5 and 10 rounds; every row of head 0 and the XCD boundary rows of
+    head 1 against the oracle; a second call gives bitwise the same result."""
+    w, data = preset(4, heads=2)
+    lay = w.layout
+    host = [data[n + "_bits"] for n in ("q", "k", "v")]
+    vals = (data["q"], data["k"], data["v"])
+    keep = data["keep"]
+    if force:
+        keep = np.maximum(keep, lay.frames + 3).astype(np.int32)
+    rows = [(0, i) for i in range(lay.nblocks)] + [(1, i) for i in xcd_boundary_rows(lay.nblocks)]
+    label = f"streamed re-rank 16 frames, {rounds} rounds, track-best {track_best}, force {force}"
+    rp, ci, st, log = run_streamed(dev, lay, host, vals, keep, rounds, track_best, force, rows,
+                                   label)
+    q, k, v = (to_dev(x, dev) for x in host)
+    log2 = torch.full_like(log, -7)
+    rp2, ci2, st2 = bsgm.select_drift_streamed(lay, keep, q, k, v, swap_rounds=rounds,
+                                               track_best=track_best, force=force, set_log=log2)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp2) and torch.equal(ci, ci2) and torch.equal(log, log2)
+    assert torch.equal(st.view(torch.int32), st2.view(torch.int32))
+
+
+@pytest.mark.parametrize("force", [False, True])
+def test_drift_streamed_exact_ties(dev, force):
+    """Rows of 528 key blocks whose value rows of frames 24 to 47 are zero: 264
+    blocks score exactly 0 in every round (their weighted value dot products
+    are exact zeros too), and keep cuts inside those ties, so the lowest-block
+    rule decides; the initial set must equal the oracle's exactly."""
+    lay = custom_layout(48, 1408, 1374, 128, heads=1)
+    host, vals = random_inputs(lay, 71)
+    tok = np.arange(lay.tokens)
+    zero = (tok // lay.frame_len) >= 24
+    q, k, v = vals
+    v = v.copy()
+    v[:, :, zero] = 0
+    vals = (q, k, v)
+    host = list(host)
+    host[2] = workloads.bf16_bits_from_float(v)
+    nb = lay.nblocks
+    keep = np.array([lay.frames if force else 264 + 40], dtype=np.int32)
+    rounds = 3
+    rows = [(0, i) for i in (0, 5, 263, 264, 300, 527)]
+    _, _, _, log = run_streamed(dev, lay, host, vals, keep, rounds, True, force, rows,
+                                f"streamed re-rank exact ties, force {force}")
+    lg = log.cpu().numpy()
+    forced = oracle.forced_blocks(lay, force)
+    qbar = oracle.pool(q[:, 0:1], lay)[0, 0]
+    for (_, i) in rows:
+        chat, _, _ = oracle.drift_row(qbar[i], k[0, 0], v[0, 0], lay)
+        _, _, sets, _ = oracle.rerank_row(chat, int(keep[0]), rounds, forced, True)
+        got = parity.mask_words_to_set(lg[i].reshape(rounds + 1, -1)[0], nb)
+        assert got == sorted(sets[0]), (i, len(got))
+
+
+@pytest.mark.parametrize("nb,frames,block", [(1100, 100, 128), (61, 1, 64)])
+def test_drift_streamed_wide_and_small_rows(dev, nb, frames, block):
+    """Rows of 1100 key blocks (a 100-frame layer's width) and a single ragged
+    frame of 61 blocks of 64."""
+    if nb == 1100:
+        lay = custom_layout(frames, 1408, 1374, block, heads=1)
+    else:
+        lay = custom_layout(1, 61 * 64, 61 * 64 - 40, block, heads=1)
+    assert lay.nblocks == nb
+    host, vals = random_inputs(lay, 55 + nb)
+    keep = np.array([max(4, nb // 5)], dtype=np.int32)
+    rows = [(0, i) for i in spread_rows(nb, 24)]
+    run_streamed(dev, lay, host, vals, keep, 5, True, False, rows,
+                 f"streamed re-rank rows of {nb} blocks")
+
+
+def test_drift_streamed_batch2_ragged(dev):
+    """Two batch entries, two heads with different budgets, ragged frames of
+    blocks of 64: every row of both batch entries of head 1."""
+    lay = custom_layout(3, 1408, 1374, 64, heads=2, batch=2)
+    host, vals = random_inputs(lay, 91)
+    keep = np.array([9, 23], dtype=np.int32)
+    nb = lay.nblocks
+    rows = [(b, 1, i) for b in range(2) for i in range(nb)] + [(1, 0, i) for i in spread_rows(nb, 8)]
+    run_streamed(dev, lay, host, vals, keep, 4, True, True, rows, "streamed re-rank batch 2")
+
+
+def test_drift_streamed_layer16_full_size(dev):
+    """The 16-frame drift layer at full size (16 heads, 5 rounds, track-best):
+    the XCD boundary rows and evenly spaced rows of heads 0, 7 and 15 against
+    the oracle; every row against the materialised form."""
+    w, data = preset(4)
+    lay = w.layout
+    host = [data[n + "_bits"] for n in ("q", "k", "v")]
+    vals = (data["q"], data["k"], data["v"])
+    rows = [(h, i) for h in (0, 7, 15) for i in spread_rows(lay.nblocks, 24)]
+    run_streamed(dev, lay, host, vals, data["keep"], 5, True, False, rows,
+                 "streamed re-rank 16 frames full size")
 
 
 # --------------------------------------------------------------------------

@@ -290,3 +290,32 @@ def test_rerank_fixed_point_stays():
     chat = np.array([[5.0, 0.0], [0.0, 4.0], [0.1, 0.0], [0.0, -0.1]])
     kept, j, sets, js = oracle.rerank_row(chat, 2, 4)
     assert all(sx == [0, 1] for sx in sets) and len(set(js)) == 1
+
+
+def test_expanded_round_score_needs_no_contributions():
+    """The identity the expanded re-rank rests on: for any residual r,
+    <r, c_ij> = sum_{u in block j} w_iu <v_u, r> with w_iu the pooled query's
+    softmax weights over the real keys, so a round's scores can be formed from
+    Q, K and V without the contributions."""
+    lay = layout(frames=3, frame_len=32, frame_valid=27, block=8, D=16, scale=0.25)
+    rng = np.random.default_rng(5)
+    ntok = lay.frames * lay.frame_len
+    q, k, v = (rng.standard_normal((1, 1, ntok, 16)) for _ in range(3))
+    pad = (np.arange(ntok) % lay.frame_len) >= lay.frame_valid
+    for a in (q, k, v):
+        a[:, :, pad] = 0
+    qbar = oracle.pool(q, lay)[0, 0]
+    nb = ntok // lay.block
+    real = np.flatnonzero(~pad)
+    for i in (0, 5, nb - 1):
+        chat, _, _ = oracle.drift_row(qbar[i], k[0, 0], v[0, 0], lay)
+        logits = lay.scale * (k[0, 0, real] @ qbar[i])
+        w = np.exp(logits - logits.max())
+        w /= w.sum()
+        r = rng.standard_normal(16)
+        vr = v[0, 0, real] @ r
+        blk = real // lay.block
+        for j in range(nb):
+            lhs = float(r @ chat[j])
+            rhs = float(np.sum(w[blk == j] * vr[blk == j]))
+            assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (i, j, lhs, rhs)
