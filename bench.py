@@ -551,15 +551,28 @@ def drift_wide_layer(bsgm, workloads, torch, dev, reps: int = 3):
     sel_ms = gpu_ms(torch, select, reps)
     at_ms = gpu_ms(torch, attend, reps)
     executed = int(row_ptr[-1].item())
+    scoring_mib = mib(contrib.numel() * 4 + score.numel() * 4 + ws.numel())
+    del contrib, score, ws
+    torch.cuda.empty_cache()
+    # the same selection in the expanded form, with no contributions allocated
+    sws = torch.empty(bsgm.drift_streamed_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+
+    def select_streamed():
+        bsgm.select_drift_streamed(lay, keep, q, k, v, swap_rounds=5, track_best=True,
+                                   row_ptr=row_ptr, col_idx=col_idx, workspace=sws,
+                                   want_stat=False)
+    st_ms = gpu_ms(torch, select_streamed, reps)
     out = {"keep_per_query_block": keep[0], "rounds": 5, "restoration": "re-rank, track-best",
            "drift_scores_ms": round(sc_ms, 4), "drift_select_ms": round(sel_ms, 4),
            "best_swap_3_rounds_select_ms": round(bs_ms, 4),
            "attn_ms": round(at_ms, 4), "ms_per_layer": round(sc_ms + sel_ms + at_ms, 4),
            "executed_block_pairs": executed,
-           "scoring_memory_mib": mib(contrib.numel() * 4 + score.numel() * 4 + ws.numel()),
+           "scoring_memory_mib": scoring_mib,
+           "streamed_scores_and_select_ms": round(st_ms, 4),
+           "streamed_scoring_memory_mib": mib(sws.numel()),
            "attn_effective_tflops": round(executed * 4.0 * 128 * 128 * 64 / (at_ms * 1e-3) / 1e12,
                                           2)}
-    del contrib, score, q, k, v, o
+    del sws, q, k, v, o
     torch.cuda.empty_cache()
     return out
 
@@ -643,6 +656,18 @@ def side_config(bsgm, workloads, torch, dev, name: str, reps: int = 5, flush=Non
                                    restoration=bsgm.RERANK_TRACK_BEST)
             out[f"rerank_track_best_{rr_rounds}_rounds_select_ms"] = round(
                 gpu_ms(torch, select_rr, reps), 4)
+        # the 5-round re-rank in the expanded form (scores and selection from
+        # Q, K and V, no contributions)
+        sws = torch.empty(bsgm.drift_streamed_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+
+        def select_streamed():
+            bsgm.select_drift_streamed(lay, keep, q, k, v, swap_rounds=5, track_best=True,
+                                       force=w.force_frame_first_block, row_ptr=row_ptr,
+                                       col_idx=col_idx, workspace=sws, want_stat=False)
+        out["streamed_rerank_track_best_5_rounds_ms"] = round(gpu_ms(torch, select_streamed, reps),
+                                                              4)
+        out["streamed_workspace_mib"] = mib(sws.numel())
+        del sws
         sel = out["drift_scores_ms"] + out["drift_select_ms"]
         out["workspace_mib"] = {"drift_scores": mib(ws_bytes),
                                 "contributions_and_scores": mib(chat_bytes + 2 * rows * nb * 4)}

@@ -163,7 +163,7 @@ StreamWs stream_ws_layout(const bsgm::Dims& d) {
   w.qsplit = take(rows * 3 * 64 * 2);
   w.stats = take(rows * d.nb * 2 * sizeof(float));   // later: ||c||^2, then <r, c>
   w.mz = take(rows * 2 * sizeof(float));
-  w.part = take(rows * bsgm::drift_round_groups(d) * 64 * sizeof(float));
+  w.part = take(rows * bsgm::drift_round_groups_max(d) * 64 * sizeof(float));
   w.rsplit = take(rows * 3 * 64 * 2);
   w.jsq = take(rows * sizeof(float));
   w.jbest = take(rows * sizeof(float));

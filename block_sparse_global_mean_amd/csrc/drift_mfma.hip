@@ -537,13 +537,14 @@ __global__ __launch_bounds__(256) void k_drift_resid(DriftRoundArgs r, int rows,
 }
 
 // <r_i, contrib_ij> of one 32-row query tile against the wave's key block:
-// X = V R^T on the matrix cores (V rows as the A operand, as K in the scores;
-// r as three bf16 terms, so the products are exact), then the weighted sum
-// sum_u w_iu X_ui over the block's real keys. X has the layout of S^T.
+// X = V R^T on the matrix cores (V rows as the A operand, read from the
+// wave's LDS tile as K fragments are; r as three bf16 terms, so the products
+// are exact), then the weighted sum sum_u w_iu X_ui over the block's real
+// keys. X has the layout of S^T.
 template <int KT>
 __device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoundArgs& r,
                                          const WaveItem& it, int rt, int vlen, int lane,
-                                         const bf16x8 (&kf)[KT][4], const __bf16* vblk) {
+                                         const bf16x8 (&kf)[KT][4], const unsigned char* vb) {
   const Dims& d = a.d;
   const int i = 32 * rt + (lane & 31);
   bf16x8 qh[4], qm[4], ql[4], rh[4], rm[4], rl[4];
@@ -558,7 +559,8 @@ __device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoun
     f32x16 s = qk_tile(kf[t], qh, qm, ql);
     mask_padding(s, t, vlen, lane);   // weight 0 for padding keys
     bf16x8 vf[4];
-    load_row_frags(vblk, t, lane, vf);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vf[ks] = k_frag(vb, t, ks, lane);
     const f32x16 xv = qk_tile(vf, rh, rm, rl);
 #pragma unroll
     for (int x = 0; x < 16; ++x)
@@ -570,20 +572,23 @@ __device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoun
   if (lane < 32 && i < d.nb) r.dot[((size_t)it.bh * d.nb + i) * d.nb + it.j] = tot;
 }
 
-// Same work split as the statistics: one wave per (b, h, key block, run of
-// query tiles), K fragments in registers, V fragments loaded per sub-tile.
+// Same work split as the contributions: one wave per (b, h, key block, run of
+// query tiles), K fragments in registers, V in the wave's LDS tile.
 template <int BLK>
 __global__ __launch_bounds__(256, 2) void k_drift_dot(DriftMfmaArgs a, DriftRoundArgs r, int rtpw) {
-  constexpr int KT = BLK / 32;
+  constexpr int KT = BLK / 32, TB = BLK * 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
   const Dims& d = a.d;
   WaveItem it;
   if (!wave_item(d, rtpw, it)) return;
   const int lane = threadIdx.x & 63;
+  unsigned char* vb = smem + (threadIdx.x >> 6) * TB;
   const size_t tok0 = (size_t)it.bh * d.N + (size_t)it.j * BLK;
+  stage_v<BLK>(a.v + tok0 * 64, lane, vb);
   bf16x8 kf[KT][4];
   load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
   const int vlen = block_vlen(d, it.j);
-  for (int rt = it.rt0; rt < it.rt1; ++rt) dot_tile<KT>(a, r, it, rt, vlen, lane, kf, a.v + tok0 * 64);
+  for (int rt = it.rt0; rt < it.rt1; ++rt) dot_tile<KT>(a, r, it, rt, vlen, lane, kf, vb);
 }
 
 // Query tiles per wave for `slots` resident waves on the chip: among the
@@ -686,13 +691,23 @@ hipError_t launch_drift_sqnorms_bf16(const Dims& d, const float* qbar, void* qsp
   return hipGetLastError();
 }
 
-int drift_round_groups(const Dims& d) {
-  // about 2048 waves (two workgroups of 4 per CU on 256 CUs), at most 16 groups
+int drift_round_groups_max(const Dims& d) { return d.nb < 16 ? d.nb : 16; }
+
+// Groups of key blocks per query tile in the residual pass: the count of least
+// makespan at `slots` resident waves (whole rounds of waves times the blocks
+// a wave walks), the larger count among equals.
+static int drift_round_groups(const Dims& d, int slots) {
   const long long tiles = (long long)d.B * d.H * ((d.nb + 31) / 32);
-  long long g = (2048 + tiles - 1) / tiles;
-  if (g > 16) g = 16;
-  if (g > d.nb) g = d.nb;
-  return (int)(g < 1 ? 1 : g);
+  int best = 1;
+  long long best_span = -1;
+  for (int g = 1; g <= drift_round_groups_max(d); ++g) {
+    const long long span = ((tiles * g + slots - 1) / slots) * ((d.nb + g - 1) / g);
+    if (best_span < 0 || span <= best_span) {
+      best_span = span;
+      best = g;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const void* k,
@@ -701,7 +716,7 @@ hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const v
                                       float* jbest, int round, hipStream_t s) {
   DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
                   const_cast<float2*>(mz), nullptr, nullptr, nullptr};
-  const int G = drift_round_groups(d);
+  const int G = drift_round_groups(d, compute_units() * 8);
   DriftRoundArgs r{kept, part, G, (__bf16*)rsplit, nullptr};
   const long long waves = (long long)d.B * d.H * ((d.nb + 31) / 32) * G;
   const dim3 grid((unsigned)((waves + 3) / 4));

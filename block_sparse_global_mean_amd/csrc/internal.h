@@ -94,8 +94,8 @@ hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int f
 hipError_t launch_drift_sqnorms_bf16(const Dims& d, const float* qbar, void* qsplit, const void* k,
                                      const void* v, float2* stats, float2* mz, float* sqnorm,
                                      hipStream_t s);
-// Groups of key blocks of the residual pass (part holds [rows, groups, 64]).
-int drift_round_groups(const Dims& d);
+// Most groups of key blocks of the residual pass (part holds [rows, groups, 64]).
+int drift_round_groups_max(const Dims& d);
 // The residual r_i of the drop set of `kept` ([rows, ceil(nb / 32)] bitmasks),
 // as three bf16 terms in rsplit [rows, 3, 64], and J^2 = ||r_i||^2 in jsq; with
 // best non-null, best/jbest keep the set of least J (round 0 starts them).

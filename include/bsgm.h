@@ -232,8 +232,8 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
                                int32_t* set_log, void* ws, size_t ws_bytes, void* stream);
 
 /* Device workspace of bsgm_select_drift_streamed: about
- * B*H*Nb * (8*Nb + 1040 + 12*ceil(Nb/32)) bytes plus a partial residual of at
- * most 16 x 64 floats per row; 0 if the layout is invalid. */
+ * B*H*Nb * (8*Nb + 1040 + 12*ceil(Nb/32)) bytes, plus min(16, Nb) x 64 floats
+ * per row of partial residual sums; 0 if the layout is invalid. */
 size_t bsgm_drift_streamed_workspace_bytes(const bsgm_layout* layout);
 
 /* TOPK or CDF selection from pooled means the caller already holds (from

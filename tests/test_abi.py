@@ -131,7 +131,7 @@ def test_streamed_drift_workspace_and_errors():
     lay = L()                             # 2 heads x 8 blocks: 16 rows
     rows, nb, words = 16, 8, 1
     al = lambda x: (x + 255) // 256 * 256
-    groups = 8                            # min(16, nb, ceil(2048 / (2 heads x 1 query tile)))
+    groups = 8                            # min(16, nb): the most groups the residual pass uses
     # pooled q and its bf16 terms; per (row, block) two floats (statistics, then
     # the squared scores and the round's dot products); M and 1/Z; the group
     # partials of the residual and its bf16 terms; J^2 and the best J^2; three
