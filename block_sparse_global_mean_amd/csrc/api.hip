@@ -147,7 +147,7 @@ WsLayout ws_layout(const bsgm::Dims& d, int mode) {
 // squared scores and the per-round dot products reuse the statistics' bytes,
 // which are dead once (M_i, Z_i) are formed.
 struct StreamWs {
-  size_t qbar, qsplit, stats, mz, part, rsplit, jsq, jbest, m0, m1, best, total;
+  size_t qbar, qsplit, stats, mz, obar, part, rsplit, jsq, jbest, m0, m1, best, total;
 };
 
 StreamWs stream_ws_layout(const bsgm::Dims& d) {
@@ -163,6 +163,7 @@ StreamWs stream_ws_layout(const bsgm::Dims& d) {
   w.qsplit = take(rows * 3 * 64 * 2);
   w.stats = take(rows * d.nb * 2 * sizeof(float));   // later: ||c||^2, then <r, c>
   w.mz = take(rows * 2 * sizeof(float));
+  w.obar = take(rows * 64 * sizeof(float));
   w.part = take(rows * bsgm::drift_round_groups_max(d) * 64 * sizeof(float));
   w.rsplit = take(rows * 3 * 64 * 2);
   w.jsq = take(rows * sizeof(float));
@@ -358,9 +359,20 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   e = bsgm::launch_drift_stream_step(d, hb, force, R, 0, sqnorm, nullptr, nullptr, masks[0],
                                      set_log, s);
   if (e != hipSuccess) return hip_fail(e, "drift step launch");
+  // with fewer blocks kept than dropped in every head, r = o - (sum of the kept
+  // blocks): the rounds then weigh the smaller set, after one pass for o
+  bool via_kept = true;
+  for (int h = 0; h < d.H; ++h) via_kept = via_kept && hb.keep[h] < d.nb - hb.keep[h];
+  float* obar = reinterpret_cast<float*>(base + w.obar);
+  if (via_kept && (R > 0 || tb || row_stat)) {
+    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, nullptr, 0, obar, part,
+                                         base + w.rsplit, jsq, nullptr, jbest, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "drift total launch");
+  }
+  const int vk = via_kept ? 1 : 0;
   int c = 0;
   for (int round = 1; round <= R; ++round, c ^= 1) {
-    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], part,
+    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], vk, obar, part,
                                          base + w.rsplit, jsq, best, jbest, round - 1, s);
     if (e != hipSuccess) return hip_fail(e, "drift residual launch");
     e = bsgm::launch_drift_dot_bf16(d, base + w.qsplit, base + w.rsplit, k, v, mz, dot, s);
@@ -371,7 +383,7 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   }
   // J of the last set: the track-best comparison and row_stat need it
   if (tb || row_stat) {
-    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], part,
+    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], vk, obar, part,
                                          base + w.rsplit, jsq, best, jbest, R, s);
     if (e != hipSuccess) return hip_fail(e, "drift residual launch");
   }

@@ -440,8 +440,11 @@ __global__ __launch_bounds__(256, 2) void k_drift_contrib_mfma(DriftMfmaArgs a, 
 // Nothing of size rows x nb x 64 is kept.
 // ---------------------------------------------------------------------------
 struct DriftRoundArgs {
-  const uint32_t* kept;   // [rows, W]: the round's kept set (bit j % 32 of word j / 32)
-  float* part;            // [rows, ngroups, 64]: per group of key blocks, the dropped sum
+  const uint32_t* kept;   // [rows, W]: the round's kept set (bit j % 32 of word j / 32),
+                          // or null: every block counts (the total o_i = sum_j contrib_ij)
+  int via_kept;           // sum the kept blocks and take r = o - that sum
+  float* obar;            // [rows, 64]: o_i
+  float* part;            // [rows, ngroups, 64]: per group of key blocks, the partial sum
   int ngroups;
   __bf16* rsplit;         // [rows, 3, 64]: r as hi, mid, lo bf16 terms
   float* dot;             // [rows, nb]: <r_i, contrib_ij>
@@ -449,8 +452,11 @@ struct DriftRoundArgs {
 
 // Residual partial sums: one wave per (b, h, 32-row query tile, run of
 // consecutive key blocks). For each block of its run the wave stages V and K
-// as the contribution kernel does and adds W V, the weights of rows that keep
-// the block set to zero; a block that every row of the tile keeps is skipped.
+// as the contribution kernel does and adds W V, with the weights of the rows
+// for which the block does not count set to zero; a block no row of the tile
+// counts is skipped. A block counts where it is dropped, or with via_kept
+// where it is kept (the smaller set when fewer blocks are kept than dropped:
+// the kept sets of a tile's rows overlap, so most blocks are skipped).
 template <int BLK>
 __global__ __launch_bounds__(256, 2) void k_drift_dropsum(DriftMfmaArgs a, DriftRoundArgs r) {
   constexpr int KT = BLK / 32, TB = BLK * 128;
@@ -475,14 +481,17 @@ __global__ __launch_bounds__(256, 2) void k_drift_dropsum(DriftMfmaArgs a, Drift
 #pragma unroll
     for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
   float wsum = 0.f;   // (unused)
+  // a block counts where its kept bit differs from `flip`; every block counts
+  // for the total (no kept sets)
+  const uint32_t flip = r.via_kept ? 1u : 0u;
   uint32_t word = 0;
   int wi = -1;
   for (int j = j0; j < j1; ++j) {
-    if ((j >> 5) != wi) {
+    if (r.kept && (j >> 5) != wi) {
       wi = j >> 5;
-      word = krow[wi];
+      word = krow[wi] ^ (flip ? 0u : 0xFFFFFFFFu);
     }
-    const bool drop = i < d.nb && ((word >> (j & 31)) & 1u) == 0;
+    const bool drop = i < d.nb && (!r.kept || ((word >> (j & 31)) & 1u) != 0);
     if (__ballot(drop) == 0ull) continue;   // uniform
     const size_t tok0 = (size_t)bh * d.N + (size_t)j * BLK;
     stage_v<BLK>(a.v + tok0 * 64, lane, vb);
@@ -506,10 +515,11 @@ __global__ __launch_bounds__(256, 2) void k_drift_dropsum(DriftMfmaArgs a, Drift
   }
 }
 
-// Per row (one wave): r = the sum of the group partials in group order, its
-// three bf16 terms for the dot products, and J^2 = ||r||^2. With best, also
-// keeps the kept set of least J so far (round 0 starts it; ties keep the
-// earlier set).
+// Per row (one wave): the sum of the group partials in group order. Without
+// kept sets that is o_i, stored as such. Otherwise r (o_i minus the sum with
+// via_kept), its three bf16 terms for the dot products, and J^2 = ||r||^2;
+// with best, also the kept set of least J so far (round 0 starts it; ties
+// keep the earlier set).
 __global__ __launch_bounds__(256) void k_drift_resid(DriftRoundArgs r, int rows, int W, int round,
                                                      float* jsq, uint32_t* best, float* jbest) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -517,6 +527,11 @@ __global__ __launch_bounds__(256) void k_drift_resid(DriftRoundArgs r, int rows,
   const float* p = r.part + (size_t)row * r.ngroups * 64 + lane;
   float x = 0.f;
   for (int g = 0; g < r.ngroups; ++g) x += p[(size_t)g * 64];
+  if (!r.kept) {
+    r.obar[(size_t)row * 64 + lane] = x;
+    return;
+  }
+  if (r.via_kept) x = r.obar[(size_t)row * 64 + lane] - x;
   const __bf16 h = (__bf16)x;
   const float r1 = x - (float)h;
   const __bf16 m = (__bf16)r1;
@@ -712,12 +727,13 @@ static int drift_round_groups(const Dims& d, int slots) {
 
 hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const void* k,
                                       const void* v, const float2* mz, const uint32_t* kept,
-                                      float* part, void* rsplit, float* jsq, uint32_t* best,
-                                      float* jbest, int round, hipStream_t s) {
+                                      int via_kept, float* obar, float* part, void* rsplit,
+                                      float* jsq, uint32_t* best, float* jbest, int round,
+                                      hipStream_t s) {
   DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
                   const_cast<float2*>(mz), nullptr, nullptr, nullptr};
   const int G = drift_round_groups(d, compute_units() * 8);
-  DriftRoundArgs r{kept, part, G, (__bf16*)rsplit, nullptr};
+  DriftRoundArgs r{kept, via_kept, obar, part, G, (__bf16*)rsplit, nullptr};
   const long long waves = (long long)d.B * d.H * ((d.nb + 31) / 32) * G;
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (d.blk == 128)
@@ -736,7 +752,7 @@ hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* 
                                  hipStream_t s) {
   DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
                   const_cast<float2*>(mz), nullptr, nullptr, nullptr};
-  DriftRoundArgs r{nullptr, nullptr, 0, (__bf16*)rsplit, dot};
+  DriftRoundArgs r{nullptr, 0, nullptr, nullptr, 0, (__bf16*)rsplit, dot};
   int rt = 0;
   const dim3 grid = wave_grid(d, compute_units() * 8, rt);
   if (d.blk == 128)

@@ -99,10 +99,13 @@ int drift_round_groups_max(const Dims& d);
 // The residual r_i of the drop set of `kept` ([rows, ceil(nb / 32)] bitmasks),
 // as three bf16 terms in rsplit [rows, 3, 64], and J^2 = ||r_i||^2 in jsq; with
 // best non-null, best/jbest keep the set of least J (round 0 starts them).
+// via_kept: r_i = obar_i minus the sum over the kept blocks. kept null: obar_i =
+// sum_j contrib_ij into obar [rows, 64] (nothing else written).
 hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const void* k,
                                       const void* v, const float2* mz, const uint32_t* kept,
-                                      float* part, void* rsplit, float* jsq, uint32_t* best,
-                                      float* jbest, int round, hipStream_t s);
+                                      int via_kept, float* obar, float* part, void* rsplit,
+                                      float* jsq, uint32_t* best, float* jbest, int round,
+                                      hipStream_t s);
 // dot[i, j] = <r_i, c_ij> for every block, recomputed from qbar, K and V.
 hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* rsplit,
                                  const void* k, const void* v, const float2* mz, float* dot,

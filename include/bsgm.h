@@ -207,8 +207,10 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
  *   g_j = 2 <r, contrib_j> + ||contrib_j||^2   (j kept; minus for j dropped),
  *   <r, contrib_ij> = sum_{u in block j} e_u <v_u, r> / sum_u e_u,
  * so each round recomputes the residual r of its drop set (a weighted value
- * sum over the dropped blocks) and then one scalar per (row, block) from the
- * keys and values; the row statistics (max and sum of exp) are computed once.
+ * sum over the dropped blocks or, when every head keeps fewer blocks than it
+ * drops, the total sum_j contrib_ij minus that over the kept blocks) and then
+ * one scalar per (row, block) from the keys and values; the row statistics
+ * (max and sum of exp) and the total are computed once.
  * Scoring memory is per (row, block) scalars, not [B,H,Nb,Nb,D] floats; the
  * cost is two passes over K and V per round.
  *   params     mode BSGM_SEL_DRIFT, keep_per_head, force_frame_first_block,
@@ -232,7 +234,7 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
                                int32_t* set_log, void* ws, size_t ws_bytes, void* stream);
 
 /* Device workspace of bsgm_select_drift_streamed: about
- * B*H*Nb * (8*Nb + 1040 + 12*ceil(Nb/32)) bytes, plus min(16, Nb) x 64 floats
+ * B*H*Nb * (8*Nb + 1296 + 12*ceil(Nb/32)) bytes, plus min(16, Nb) x 64 floats
  * per row of partial residual sums; 0 if the layout is invalid. */
 size_t bsgm_drift_streamed_workspace_bytes(const bsgm_layout* layout);
 

@@ -133,11 +133,11 @@ def test_streamed_drift_workspace_and_errors():
     al = lambda x: (x + 255) // 256 * 256
     groups = 8                            # min(16, nb): the most groups the residual pass uses
     # pooled q and its bf16 terms; per (row, block) two floats (statistics, then
-    # the squared scores and the round's dot products); M and 1/Z; the group
-    # partials of the residual and its bf16 terms; J^2 and the best J^2; three
+    # the squared scores and the round's dot products); M and 1/Z; the total
+    # o = sum_j c_j; the group partials of the residual and its bf16 terms; J^2 and the best J^2; three
     # kept-set bitmasks
     expect = (al(rows * 64 * 4) + al(rows * 192 * 2) + al(rows * nb * 8) + al(rows * 8)
-              + al(rows * groups * 64 * 4) + al(rows * 192 * 2) + 2 * al(rows * 4)
+              + al(rows * 64 * 4) + al(rows * groups * 64 * 4) + al(rows * 192 * 2) + 2 * al(rows * 4)
               + 3 * al(rows * words * 4))
     c = _lib.c_layout(lay)
     assert bsgm.library().bsgm_drift_streamed_workspace_bytes(ctypes.byref(c)) == expect

@@ -1510,6 +1510,20 @@ def test_drift_streamed_layer16(dev, rounds, track_best, force):
     assert torch.equal(st.view(torch.int32), st2.view(torch.int32))
 
 
+def test_drift_streamed_more_kept_than_dropped(dev):
+    """Keep 120 of 176 blocks (more kept than dropped, so the rounds sum the
+    dropped blocks directly rather than the total minus the kept ones), with a
+    second head at keep 40 (mixed budgets take the dropped sums as well)."""
+    w, data = preset(4, heads=2)
+    lay = w.layout
+    host = [data[n + "_bits"] for n in ("q", "k", "v")]
+    vals = (data["q"], data["k"], data["v"])
+    keep = np.array([120, 40], dtype=np.int32)
+    rows = [(h, i) for h in (0, 1) for i in spread_rows(lay.nblocks, 24)]
+    run_streamed(dev, lay, host, vals, keep, 4, True, False, rows,
+                 "streamed re-rank, more kept than dropped")
+
+
 @pytest.mark.parametrize("force", [False, True])
 def test_drift_streamed_exact_ties(dev, force):
     """Rows of 528 key blocks whose value rows of frames 24 to 47 are zero: 264
