@@ -312,8 +312,8 @@ def select_drift_streamed(layout, keep: Sequence[int], q, k, v, swap_rounds: int
                           col_idx=None, row_stat=None, set_log=None, workspace=None,
                           want_stat: bool = True, stream=None):
     """Drift selection by re-rank rounds straight from Q, K and V, without the
-    [B,H,Nb,Nb,D] contributions (dropped-sum objective, bf16). set_log, when
-    given, receives [rows, swap_rounds + 1, ceil(nb / 32)] kept bitmasks."""
+    [B,H,Nb,Nb,D] contributions (dropped-sum objective). set_log, when given,
+    receives [rows, swap_rounds + 1, ceil(nb / 32)] kept bitmasks."""
     n, nb, rows = _dims(layout)
     shape = (layout.batch, layout.heads, n, layout.head_dim)
     for t, name in ((q, "q"), (k, "k"), (v, "v")):

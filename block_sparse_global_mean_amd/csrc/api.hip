@@ -323,8 +323,6 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   if (params->drift_objective != BSGM_DRIFT_DROPPED_SUM)
     return fail(BSGM_E_UNSUPPORTED, "streamed drift selection takes the dropped-sum objective");
   if (params->swap_rounds < 0) return fail(BSGM_E_ARG, "swap_rounds must be >= 0");
-  if (layout->dtype != BSGM_BF16)
-    return fail(BSGM_E_UNSUPPORTED, "streamed drift selection: dtype must be BSGM_BF16");
   if (!q || !k || !v || !row_ptr || !col_idx || !ws)
     return fail(BSGM_E_ARG, "q, k, v, row_ptr, col_idx and ws must be non-NULL");
   const long long need = (long long)d.B * hb.per_batch;
@@ -342,6 +340,7 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   float* sqnorm = reinterpret_cast<float*>(base + w.stats);
   float* dot = sqnorm + (size_t)d.rows * d.nb;
   float* part = reinterpret_cast<float*>(base + w.part);
+  float* obar = reinterpret_cast<float*>(base + w.obar);
   float* jsq = reinterpret_cast<float*>(base + w.jsq);
   float* jbest = reinterpret_cast<float*>(base + w.jbest);
   uint32_t* masks[2] = {reinterpret_cast<uint32_t*>(base + w.m0),
@@ -351,10 +350,26 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   const int force = params->force_frame_first_block ? 1 : 0, R = params->swap_rounds;
   hipStream_t s = (hipStream_t)stream;
 
+  // bf16 K and V take the matrix-core passes, fp32 the vector-ALU ones
+  const bool f32 = layout->dtype == BSGM_F32;
+  void* rsplit = base + w.rsplit;
+  auto residual = [&](const uint32_t* kept, int vk, int round, uint32_t* bst) {
+    return f32 ? bsgm::launch_drift_residual_f32(d, qbar, k, v, kept, vk, obar, part, rsplit, jsq,
+                                                 bst, jbest, round, s)
+               : bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, kept, vk, obar,
+                                                  part, rsplit, jsq, bst, jbest, round, s);
+  };
+  auto dots = [&]() {
+    return f32 ? bsgm::launch_drift_dot_f32(d, qbar, rsplit, k, v, dot, s)
+               : bsgm::launch_drift_dot_bf16(d, base + w.qsplit, rsplit, k, v, mz, dot, s);
+  };
+
   hipError_t e = bsgm::launch_pool(d, layout->dtype, q, qbar, s);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
-  e = bsgm::launch_drift_sqnorms_bf16(d, qbar, base + w.qsplit, k, v,
-                                      reinterpret_cast<float2*>(base + w.stats), mz, sqnorm, s);
+  e = f32 ? bsgm::launch_drift_sqnorms_f32(d, qbar, k, v, sqnorm, s)
+          : bsgm::launch_drift_sqnorms_bf16(d, qbar, base + w.qsplit, k, v,
+                                            reinterpret_cast<float2*>(base + w.stats), mz, sqnorm,
+                                            s);
   if (e != hipSuccess) return hip_fail(e, "drift score launch");
   e = bsgm::launch_drift_stream_step(d, hb, force, R, 0, sqnorm, nullptr, nullptr, masks[0],
                                      set_log, s);
@@ -363,19 +378,16 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   // blocks): the rounds then weigh the smaller set, after one pass for o
   bool via_kept = true;
   for (int h = 0; h < d.H; ++h) via_kept = via_kept && hb.keep[h] < d.nb - hb.keep[h];
-  float* obar = reinterpret_cast<float*>(base + w.obar);
   if (via_kept && (R > 0 || tb || row_stat)) {
-    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, nullptr, 0, obar, part,
-                                         base + w.rsplit, jsq, nullptr, jbest, 0, s);
+    e = residual(nullptr, 0, 0, nullptr);
     if (e != hipSuccess) return hip_fail(e, "drift total launch");
   }
   const int vk = via_kept ? 1 : 0;
   int c = 0;
   for (int round = 1; round <= R; ++round, c ^= 1) {
-    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], vk, obar, part,
-                                         base + w.rsplit, jsq, best, jbest, round - 1, s);
+    e = residual(masks[c], vk, round - 1, best);
     if (e != hipSuccess) return hip_fail(e, "drift residual launch");
-    e = bsgm::launch_drift_dot_bf16(d, base + w.qsplit, base + w.rsplit, k, v, mz, dot, s);
+    e = dots();
     if (e != hipSuccess) return hip_fail(e, "drift dot launch");
     e = bsgm::launch_drift_stream_step(d, hb, force, R, round, sqnorm, dot, masks[c],
                                        masks[c ^ 1], set_log, s);
@@ -383,8 +395,7 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   }
   // J of the last set: the track-best comparison and row_stat need it
   if (tb || row_stat) {
-    e = bsgm::launch_drift_residual_bf16(d, base + w.qsplit, k, v, mz, masks[c], vk, obar, part,
-                                         base + w.rsplit, jsq, best, jbest, R, s);
+    e = residual(masks[c], vk, R, best);
     if (e != hipSuccess) return hip_fail(e, "drift residual launch");
   }
   e = bsgm::launch_drift_stream_emit(d, hb, tb ? best : masks[c], tb ? jbest : jsq, row_ptr,

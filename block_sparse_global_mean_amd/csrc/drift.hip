@@ -7,7 +7,10 @@
 //   contrib_ij = sum_{u in j} e_u v_u / Z_i,  Z_i = sum_u e_u,  score_ij = ||contrib_ij||,
 //   zmass_ij = sum_{u in j} e_u / Z_i (optional).
 // Pass 1 finds (M_i, Z_i) with an online log-sum-exp; pass 2 walks the key
-// blocks and writes contrib and score. All arithmetic is fp32.
+// blocks and writes contrib and score. All arithmetic is fp32. The same
+// kernel serves the re-rank rounds without the contributions (the expanded
+// score): squared scores only, the residual r_i of a drop set, and the dot
+// products <r_i, contrib_ij>, each from the contributions it forms and drops.
 #include <algorithm>
 
 #include "device_util.h"
@@ -15,6 +18,22 @@
 namespace bsgm {
 
 constexpr int kDriftRows = 8;   // pooled query rows per workgroup
+
+// What pass 2 of k_drift_contrib produces.
+enum DriftF32Mode {
+  kF32Contrib = 0,   // contrib, score (and zmass)
+  kF32SqNorm = 1,    // score = ||contrib_ij||^2 only
+  kF32Resid = 2,     // part[row] = sum of the contributions of the counted blocks
+  kF32Dot = 3        // dot[row, j] = <r_row, contrib_ij>
+};
+
+struct DriftF32Round {
+  const uint32_t* kept;   // [rows, W] kept sets, or null: every block counts
+  int via_kept;           // count the kept blocks, else the dropped ones
+  float* part;            // [rows, 64]
+  const __bf16* rsplit;   // [rows, 3, 64]: r as three bf16 terms (exact sum)
+  float* dot;             // [rows, nb]
+};
 
 template <typename T>
 __device__ __forceinline__ void load_row64(const T* p, float (&x)[64]) {
@@ -28,13 +47,14 @@ __device__ __forceinline__ void load_row64(const T* p, float (&x)[64]) {
   }
 }
 
-template <typename T>
+template <typename T, int MODE>
 __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__ qbar,
                                                        const T* __restrict__ K,
                                                        const T* __restrict__ V,
                                                        float* __restrict__ contrib,
                                                        float* __restrict__ score,
-                                                       float* __restrict__ zmass, Dims d) {
+                                                       float* __restrict__ zmass, Dims d,
+                                                       DriftF32Round rd) {
   __shared__ float qs[kDriftRows][64];
   __shared__ float E[kDriftRows][128];
   __shared__ float Vs[128][65];
@@ -101,6 +121,15 @@ __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__
   // Pass 2: per key block, weights e_u / Z into LDS, then contrib = E V.
   const int ri = t >> 5;            // output row of this thread
   const int dp = (t & 31) * 2;      // output column pair
+  const int irow = min(i0 + ri, d.nb - 1);
+  const size_t grow = (size_t)bh * d.nb + irow;
+  const int W = (d.nb + 31) >> 5;
+  float rs0 = 0.f, rs1 = 0.f;       // kF32Resid: the running sum; kF32Dot: r
+  if (MODE == kF32Dot) {
+    const __bf16* rp = rd.rsplit + grow * 192 + dp;
+    rs0 = ((float)rp[0] + (float)rp[64]) + (float)rp[128];
+    rs1 = ((float)rp[1] + (float)rp[65]) + (float)rp[129];
+  }
   for (int j = 0; j < d.nb; ++j) {
     const int vlen = block_vlen(d, j);
     const size_t tok0 = (size_t)j * d.blk;
@@ -140,17 +169,38 @@ __global__ __launch_bounds__(256) void k_drift_contrib(const float* __restrict__
       zs += e;
     }
     const int ii = i0 + ri;
-    float sq = a0 * a0 + a1 * a1;
+    if (MODE == kF32Resid) {
+      const bool in = rd.kept == nullptr ||
+                      ((((rd.kept[grow * W + (j >> 5)] >> (j & 31)) & 1u) != 0) ==
+                       (rd.via_kept != 0));
+      if (in) {
+        rs0 += a0;
+        rs1 += a1;
+      }
+    } else if (MODE == kF32Dot) {
+      float dt = fmaf(a1, rs1, a0 * rs0);
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
-    if (ii < d.nb) {
-      float2* dst = reinterpret_cast<float2*>(contrib + (((size_t)bh * d.nb + ii) * d.nb + j) * 64 + dp);
-      *dst = make_float2(a0, a1);
-      if ((t & 31) == 0) score[((size_t)bh * d.nb + ii) * d.nb + j] = sqrtf(sq);
-      if ((t & 31) == 0 && zmass) zmass[((size_t)bh * d.nb + ii) * d.nb + j] = zs;
+      for (int o = 16; o >= 1; o >>= 1) dt += __shfl_xor(dt, o, 64);
+      if (ii < d.nb && (t & 31) == 0) rd.dot[((size_t)bh * d.nb + ii) * d.nb + j] = dt;
+    } else {
+      float sq = a0 * a0 + a1 * a1;
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      if (ii < d.nb) {
+        if (MODE == kF32Contrib) {
+          float2* dst = reinterpret_cast<float2*>(
+              contrib + (((size_t)bh * d.nb + ii) * d.nb + j) * 64 + dp);
+          *dst = make_float2(a0, a1);
+        }
+        if ((t & 31) == 0)
+          score[((size_t)bh * d.nb + ii) * d.nb + j] = MODE == kF32SqNorm ? sq : sqrtf(sq);
+        if ((t & 31) == 0 && zmass) zmass[((size_t)bh * d.nb + ii) * d.nb + j] = zs;
+      }
     }
     __syncthreads();
   }
+  if (MODE == kF32Resid && i0 + ri < d.nb)
+    *reinterpret_cast<float2*>(rd.part + grow * 64 + dp) = make_float2(rs0, rs1);
 }
 
 hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, const void* k,
@@ -158,8 +208,39 @@ hipError_t launch_drift_contrib(const Dims& d, int dtype, const float* qbar, con
                                 hipStream_t s) {
   if (dtype != 0) return hipErrorInvalidValue;   // bf16 takes launch_drift_contrib_bf16
   dim3 grid((d.nb + kDriftRows - 1) / kDriftRows, d.B * d.H);
-  hipLaunchKernelGGL(k_drift_contrib<float>, grid, dim3(256), 0, s, qbar, (const float*)k,
-                     (const float*)v, contrib, score, zmass, d);
+  hipLaunchKernelGGL((k_drift_contrib<float, kF32Contrib>), grid, dim3(256), 0, s, qbar,
+                     (const float*)k, (const float*)v, contrib, score, zmass, d, DriftF32Round{});
+  return hipGetLastError();
+}
+
+hipError_t launch_drift_sqnorms_f32(const Dims& d, const float* qbar, const void* k, const void* v,
+                                    float* sqnorm, hipStream_t s) {
+  dim3 grid((d.nb + kDriftRows - 1) / kDriftRows, d.B * d.H);
+  hipLaunchKernelGGL((k_drift_contrib<float, kF32SqNorm>), grid, dim3(256), 0, s, qbar,
+                     (const float*)k, (const float*)v, nullptr, sqnorm, nullptr, d,
+                     DriftF32Round{});
+  return hipGetLastError();
+}
+
+hipError_t launch_drift_residual_f32(const Dims& d, const float* qbar, const void* k,
+                                     const void* v, const uint32_t* kept, int via_kept,
+                                     float* obar, float* part, void* rsplit, float* jsq,
+                                     uint32_t* best, float* jbest, int round, hipStream_t s) {
+  dim3 grid((d.nb + kDriftRows - 1) / kDriftRows, d.B * d.H);
+  DriftF32Round rd{kept, via_kept, part, nullptr, nullptr};
+  hipLaunchKernelGGL((k_drift_contrib<float, kF32Resid>), grid, dim3(256), 0, s, qbar,
+                     (const float*)k, (const float*)v, nullptr, nullptr, nullptr, d, rd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_drift_resid(d, kept, via_kept, obar, part, 1, rsplit, jsq, best, jbest, round, s);
+}
+
+hipError_t launch_drift_dot_f32(const Dims& d, const float* qbar, const void* rsplit,
+                                const void* k, const void* v, float* dot, hipStream_t s) {
+  dim3 grid((d.nb + kDriftRows - 1) / kDriftRows, d.B * d.H);
+  DriftF32Round rd{nullptr, 0, nullptr, (const __bf16*)rsplit, dot};
+  hipLaunchKernelGGL((k_drift_contrib<float, kF32Dot>), grid, dim3(256), 0, s, qbar,
+                     (const float*)k, (const float*)v, nullptr, nullptr, nullptr, d, rd);
   return hipGetLastError();
 }
 

@@ -747,6 +747,15 @@ hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const v
   return hipGetLastError();
 }
 
+hipError_t launch_drift_resid(const Dims& d, const uint32_t* kept, int via_kept, float* obar,
+                              float* part, int ngroups, void* rsplit, float* jsq, uint32_t* best,
+                              float* jbest, int round, hipStream_t s) {
+  DriftRoundArgs r{kept, via_kept, obar, part, ngroups, (__bf16*)rsplit, nullptr};
+  hipLaunchKernelGGL(k_drift_resid, dim3((d.rows + 3) / 4), dim3(256), 0, s, r, d.rows,
+                     (d.nb + 31) >> 5, round, jsq, best, jbest);
+  return hipGetLastError();
+}
+
 hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* rsplit,
                                  const void* k, const void* v, const float2* mz, float* dot,
                                  hipStream_t s) {

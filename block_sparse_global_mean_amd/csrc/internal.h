@@ -106,6 +106,20 @@ hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const v
                                       int via_kept, float* obar, float* part, void* rsplit,
                                       float* jsq, uint32_t* best, float* jbest, int round,
                                       hipStream_t s);
+// The per-row step after the residual partials: part [rows, ngroups, 64] summed
+// in group order into r (or into obar when kept is null), as above.
+hipError_t launch_drift_resid(const Dims& d, const uint32_t* kept, int via_kept, float* obar,
+                              float* part, int ngroups, void* rsplit, float* jsq, uint32_t* best,
+                              float* jbest, int round, hipStream_t s);
+// The same three passes for fp32 K and V on the vector ALU (part: one group).
+hipError_t launch_drift_sqnorms_f32(const Dims& d, const float* qbar, const void* k, const void* v,
+                                    float* sqnorm, hipStream_t s);
+hipError_t launch_drift_residual_f32(const Dims& d, const float* qbar, const void* k,
+                                     const void* v, const uint32_t* kept, int via_kept,
+                                     float* obar, float* part, void* rsplit, float* jsq,
+                                     uint32_t* best, float* jbest, int round, hipStream_t s);
+hipError_t launch_drift_dot_f32(const Dims& d, const float* qbar, const void* rsplit,
+                                const void* k, const void* v, float* dot, hipStream_t s);
 // dot[i, j] = <r_i, c_ij> for every block, recomputed from qbar, K and V.
 hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* rsplit,
                                  const void* k, const void* v, const float2* mz, float* dot,

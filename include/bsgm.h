@@ -216,7 +216,8 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
  *   params     mode BSGM_SEL_DRIFT, keep_per_head, force_frame_first_block,
  *              swap_rounds (>= 0), drift_objective DROPPED_SUM, restoration
  *              RERANK or RERANK_TRACK_BEST
- *   q, k, v    device [B,H,N,D] bf16
+ *   q, k, v    device [B,H,N,D] of layout->dtype (bf16: the passes run on the
+ *              matrix cores with fp32-accurate split operands; fp32: vector ALU)
  *   row_ptr, col_idx, col_capacity  as bsgm_select_blocks
  *   row_stat   device float [B*H*Nb] or NULL: the drift J of the returned set
  *   set_log    device int32 [B*H*Nb, swap_rounds + 1, ceil(Nb / 32)] or NULL:
@@ -224,8 +225,8 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
  *              bsgm_select_blocks' swap_log in the re-rank modes
  *   ws         device, >= bsgm_drift_streamed_workspace_bytes(layout) bytes
  * Errors: BSGM_E_ARG for a NULL q, k, v, row_ptr, col_idx or ws, another mode,
- * or negative swap_rounds; BSGM_E_UNSUPPORTED for fp32 layouts, the best-swap
- * rule or the renormalised objective; BSGM_E_CAPACITY, BSGM_E_WORKSPACE as
+ * or negative swap_rounds; BSGM_E_UNSUPPORTED for the best-swap rule or the
+ * renormalised objective; BSGM_E_CAPACITY, BSGM_E_WORKSPACE as
  * bsgm_select_blocks. Rows of any number of blocks.
  */
 int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_params* params,
@@ -431,7 +432,8 @@ int bsgm_vasc_select_blocks(const bsgm_layout* layout, const bsgm_select_params*
  * Only those rows of o and lse are written; run it after bsgm_sparse_attn_fwd
  * to replace their sparse result. bf16 only (BSGM_E_UNSUPPORTED otherwise).
  *   n_special  1..frame_valid special tokens per frame (VGGT: camera + 4 registers = 5)
- *   q, k, v    device [B,H,N,D] bf16
+ *   q, k, v    device [B,H,N,D] of layout->dtype (bf16: the passes run on the
+ *              matrix cores with fp32-accurate split operands; fp32: vector ALU)
  *   o          device [B,H,N,D] bf16, rows f*frame_len + p (p < n_special) written
  *   lse        device float [B,H,N] or NULL, the same rows written
  *   ws         device, >= bsgm_special_rows_workspace_bytes(layout, n_special) bytes

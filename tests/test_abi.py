@@ -147,7 +147,6 @@ def test_streamed_drift_workspace_and_errors():
     assert _streamed(lay, restoration=bsgm.BEST_SWAP) == -2
     assert _streamed(lay, objective=1) == -2
     assert _streamed(lay, rounds=-1) == -1
-    assert _streamed(L(dtype="f32")) == -2
     for name in ("q", "k", "v", "rp", "ci", "wsp"):
         assert _streamed(lay, **{name: None}) == -1, name
     assert _streamed(lay, cap=8 * 3 + 8 * 5 - 1) == -3

@@ -1556,17 +1556,21 @@ def test_drift_streamed_exact_ties(dev, force):
         assert got == sorted(sets[0]), (i, len(got))
 
 
-@pytest.mark.parametrize("nb,frames,block", [(1100, 100, 128), (61, 1, 64)])
-def test_drift_streamed_wide_and_small_rows(dev, nb, frames, block):
-    """Rows of 1100 key blocks (a 100-frame layer's width) and a single ragged
-    frame of 61 blocks of 64."""
+@pytest.mark.parametrize("nb,frames,block,dtype", [(1100, 100, 128, "bf16"), (61, 1, 64, "bf16"),
+                                                   (61, 1, 64, "f32"), (24, 3, 128, "f32")])
+def test_drift_streamed_wide_and_small_rows(dev, nb, frames, block, dtype):
+    """Rows of 1100 key blocks (a 100-frame layer's width), a single ragged
+    frame of 61 blocks of 64 in bf16 and fp32 (the vector-ALU passes), and
+    three fp32 frames of 8 blocks of 128."""
     if nb == 1100:
         lay = custom_layout(frames, 1408, 1374, block, heads=1)
+    elif nb == 61:
+        lay = custom_layout(1, 61 * 64, 61 * 64 - 40, block, heads=1, dtype=dtype)
     else:
-        lay = custom_layout(1, 61 * 64, 61 * 64 - 40, block, heads=1)
+        lay = custom_layout(frames, 8 * 128, 8 * 128 - 100, block, heads=2, dtype=dtype)
     assert lay.nblocks == nb
     host, vals = random_inputs(lay, 55 + nb)
-    keep = np.array([max(4, nb // 5)], dtype=np.int32)
+    keep = np.full(lay.heads, max(4, nb // 5), dtype=np.int32)
     rows = [(0, i) for i in spread_rows(nb, 24)]
     run_streamed(dev, lay, host, vals, keep, 5, True, False, rows,
                  f"streamed re-rank rows of {nb} blocks")
