@@ -24,16 +24,17 @@ struct PoolUnit {
   int vlen;
 };
 
-// Means of U <= 4 blocks by a workgroup of 256 threads; part holds U x G x 65 floats
-// of LDS. Every row of every unit is loaded before any is summed, so that the
-// loads are in flight together. Per unit the sum runs over rows in order
-// within a thread and over row groups in order across threads.
+// Means of U <= 4 blocks by a workgroup of 256 threads (t: the thread's index);
+// part holds U x G x 65 floats of LDS. Every row of every unit is loaded before
+// any is summed, so that the loads are in flight together. Per unit the sum
+// runs over rows in order within a thread and over row groups in order across
+// threads.
 template <typename T, int U>
 __device__ __forceinline__ void pool_units(const PoolUnit<T> (&u)[U],
-                                           float (*part)[PoolGeom<T>::G][65]) {
+                                           float (*part)[PoolGeom<T>::G][65],
+                                           int t = threadIdx.x) {
   static_assert(U >= 1 && U <= 4, "one unit per wave of the 256-thread workgroup");
   using PG = PoolGeom<T>;
-  const int t = threadIdx.x;
   const int c = t % PG::C, g = t / PG::C;
   uint4 raw[U][PG::RMAX];
 #pragma unroll

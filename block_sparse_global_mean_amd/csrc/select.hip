@@ -46,13 +46,14 @@ constexpr int kSelRowsPerWg = 4;
 constexpr int kKtStride = 68;   // LDS row stride (floats) of the pooled-K tile
 
 // The rows of workgroup `wg` of (b, h) = bh: query blocks 4 wg .. 4 wg + 3, one
-// per wave. `kt` is 2 x 64 x kKtStride floats of LDS. No barrier follows the
-// point where a wave without a row returns.
+// per wave. `kt` is 2 x 64 x kKtStride floats of LDS; t is the thread's index
+// in the workgroup. No barrier follows the point where a wave without a row
+// returns.
 template <int PW, bool VASC>   // key blocks per lane: nb <= 64 * PW; VASC: mode 3
 __device__ __forceinline__ void select_rows(const SelArgs& a, int bh, int wg,
-                                            float (*kt)[64 * kKtStride]) {
+                                            float (*kt)[64 * kKtStride], int t = threadIdx.x) {
   const Dims& d = a.d;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lane = t & 63, w = t >> 6;
   const int i = wg * kSelRowsPerWg + w;
   const bool live = i < d.nb;
   const int h = bh % d.H, b = bh / d.H;
@@ -393,11 +394,14 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
 // or invalidation. The grid is persistent: a workgroup reads the XCD it runs
 // on (the XCC_ID hardware register) and takes items from that XCD's queue by
 // an atomic ticket until the queue is drained. A queue holds its heads'
-// pooling items (item x of a head pools query and key blocks 2x and 2x + 1),
-// then their selection items (four query blocks each, as k_select_pooled). A
-// selection item waits until every pooling item of its head has published;
-// those hold lower tickets of the same queue, so workgroups already running
-// took them, and a pooling item waits on nothing: every wait ends.
+// pooling items (item x of a head pools key blocks 4x .. 4x + 3), then their
+// selection items (item x pools query blocks 4x .. 4x + 3 and selects those
+// rows, as k_select_pooled), so that the query loads of one item overlap the
+// selection work of others. A selection item waits until every pooling item of
+// its head has published; those hold lower tickets of the same queue, so
+// workgroups already running took them, and a pooling item waits on nothing:
+// every wait ends. A selection item reads back the pooled queries it wrote
+// itself, after its own stores are acknowledged and a barrier.
 //
 // Publication inside an XCD: a pooling workgroup waits until its stores are
 // acknowledged by the L2 (vmcnt 0), then raises the head's count; the L1 is
@@ -412,22 +416,34 @@ hipError_t launch_select_pooled(const Dims& d, const HeadBudget& hb, int mode, f
 // zeroes them once). Its view of the counters needs no fence: each workgroup's
 // last ticket fetch returned before it raised the exit count.
 // ---------------------------------------------------------------------------
-constexpr int kFusedPoolBlocks = 2;        // query and key blocks per pooling item
 constexpr int kFusedSpinLimit = 1 << 22;   // waits of about 64 clocks each
 
+// The thread index, opaque to the compiler: the items of the persistent loop
+// take it afresh, so that the lane-dependent offsets of the pooling and
+// selection code are not hoisted out of the loop and held in registers across
+// all items (which took the kernel from about 120 to 226 registers, and from
+// four workgroups per CU to two).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Four workgroups per CU (128 registers): the grid assumes them.
 template <typename T, int PW>
-__global__ __launch_bounds__(256) void k_select_fused(SelArgs a, const T* __restrict__ xq,
+__global__ __launch_bounds__(256, 4) void k_select_fused(SelArgs a, const T* __restrict__ xq,
                                                        const T* __restrict__ xk, float* qbar,
                                                        float* kbar, int32_t* sync, int nq) {
   constexpr size_t kSelLds = 2 * 64 * kKtStride * sizeof(float);
-  constexpr size_t kPoolLds = 2 * kFusedPoolBlocks * PoolGeom<T>::G * 65 * sizeof(float);
+  constexpr size_t kPoolLds = kSelRowsPerWg * PoolGeom<T>::G * 65 * sizeof(float);
   __shared__ __attribute__((aligned(16))) unsigned char lds[kSelLds > kPoolLds ? kSelLds : kPoolLds];
   __shared__ int s_item, s_last;
   const Dims& d = a.d;
   const int t = threadIdx.x;
   const int nbh = d.B * d.H;
-  const int pool_per_bh = (d.nb + kFusedPoolBlocks - 1) / kFusedPoolBlocks;
-  const int sel_per_bh = (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
+  // per (b, h): pooling items of 4 key blocks, then selection items of 4 rows
+  const int kpool_per_bh = (d.nb + kSelRowsPerWg - 1) / kSelRowsPerWg;
+  const int sel_per_bh = kpool_per_bh;
   int32_t* exits = sync + kFusedLine;
   int32_t* error = sync + 2 * kFusedLine;
   int32_t* done = sync + 3 * kFusedLine;   // item count of (b, h) = x at done[x * kFusedLine]
@@ -436,52 +452,57 @@ __global__ __launch_bounds__(256) void k_select_fused(SelArgs a, const T* __rest
   // runs item `item` of queue `qu`; false once the queue is drained
   auto run = [&](int qu) {
     const int nh = (nbh - qu + nq - 1) / nq;   // heads qu, qu + nq, ...
-    const int npool = nh * pool_per_bh, total = npool + nh * sel_per_bh;
+    const int npool = nh * kpool_per_bh, total = npool + nh * sel_per_bh;
     __syncthreads();   // the previous item is done with the LDS and s_item
     if (t == 0)
       s_item = __hip_atomic_fetch_add(&tickets[qu * kFusedLine], 1, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int item = s_item;
+    // uniform, but read from LDS: say so, so that the item's indices and
+    // addresses stay in scalar registers
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= total) return false;
-    if (item < npool) {
-      const int u = item / pool_per_bh, bh = qu + nq * u;
-      const int j0 = (item - u * pool_per_bh) * kFusedPoolBlocks;
-      PoolUnit<T> pu[2 * kFusedPoolBlocks];
+    const bool kpool = item < npool;
+    const int u = kpool ? item / kpool_per_bh : (item - npool) / sel_per_bh;
+    const int x = kpool ? item - u * kpool_per_bh : item - npool - u * sel_per_bh;
+    const int bh = qu + nq * u;
+    // blocks 4x .. 4x + 3: of K for a pooling item, of Q (the rows it then
+    // selects) for a selection item
+    PoolUnit<T> pu[kSelRowsPerWg];
 #pragma unroll
-      for (int x = 0; x < kFusedPoolBlocks; ++x) {
-        const int j = j0 + x;
-        const bool real = j < d.nb;
-        const size_t tok = ((size_t)bh * d.N + (size_t)(real ? j : 0) * d.blk) * 64;
-        const size_t row = ((size_t)bh * d.nb + j) * 64;
-        const int vlen = real ? block_vlen(d, j) : 0;
-        pu[2 * x] = PoolUnit<T>{xq + tok, real ? qbar + row : nullptr, vlen};
-        pu[2 * x + 1] = PoolUnit<T>{xk + tok, real ? kbar + row : nullptr, vlen};
+    for (int y = 0; y < kSelRowsPerWg; ++y) {
+      const int j = kSelRowsPerWg * x + y;
+      const bool real = j < d.nb;
+      const size_t tok = ((size_t)bh * d.N + (size_t)(real ? j : 0) * d.blk) * 64;
+      const size_t row = ((size_t)bh * d.nb + j) * 64;
+      pu[y] = PoolUnit<T>{(kpool ? xk : xq) + tok, real ? (kpool ? kbar : qbar) + row : nullptr,
+                          real ? block_vlen(d, j) : 0};
+    }
+    pool_units<T, kSelRowsPerWg>(pu, reinterpret_cast<float(*)[PoolGeom<T>::G][65]>(lds),
+                                 opaque_tid());
+    // every store of this workgroup acknowledged by the L2 before the count,
+    // or before the selection reads its pooled queries back
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    if (!kpool && t == 0) {
+      // the selection needs all of its head's pooled keys
+      int spins = 0;
+      while (__hip_atomic_load(&done[bh * kFusedLine], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) < kpool_per_bh) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kFusedSpinLimit) {
+          __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
       }
-      pool_units<T, 2 * kFusedPoolBlocks>(
-          pu, reinterpret_cast<float(*)[PoolGeom<T>::G][65]>(lds));
-      // every store of this workgroup acknowledged by the L2 before the count
-      __builtin_amdgcn_s_waitcnt(0);
-      asm volatile("" ::: "memory");
-      __syncthreads();
+    }
+    __syncthreads();
+    if (kpool) {
       if (t == 0)
         __hip_atomic_fetch_add(&done[bh * kFusedLine], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      const int sel = item - npool, u = sel / sel_per_bh, bh = qu + nq * u;
-      if (t == 0) {
-        int spins = 0;
-        while (__hip_atomic_load(&done[bh * kFusedLine], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT) < pool_per_bh) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins == kFusedSpinLimit) {
-            __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      select_rows<PW, false>(a, bh, sel - u * sel_per_bh,
-                             reinterpret_cast<float(*)[64 * kKtStride]>(lds));
+      select_rows<PW, false>(a, bh, x, reinterpret_cast<float(*)[64 * kKtStride]>(lds),
+                             opaque_tid());
     }
     return true;
   };
