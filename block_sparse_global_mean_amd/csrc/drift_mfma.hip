@@ -33,7 +33,8 @@ struct DriftMfmaArgs {
   const __bf16* k;       // [B, H, N, 64]
   const __bf16* v;
   float2* stats;         // [B*H*nb, nb]: (m_ij, z_ij)
-  float2* mz;            // [B*H*nb]: (M_i * log2(e), 1 / Z_i)
+  float2* mz;            // [B*H*nb]: (M_i log2(e) + log2(Z_i), 1 / Z_i): the weights are
+                         // exp2(l_iu log2(e) - mz.x)
   float* contrib;        // [B*H*nb, nb, 64]
   float* score;          // [B*H*nb, nb]
   float* zmass;          // [B*H*nb, nb] or null: sum over the block of exp(l - M) / Z
@@ -259,12 +260,14 @@ __global__ __launch_bounds__(256) void k_drift_norm(DriftMfmaArgs a) {
     z += e.y * expf(e.x - m);
   }
   z = wave_sum(z);
-  if (lane == 0) a.mz[r] = make_float2(m * kLog2e, 1.f / z);
+  // 1/Z folded into the exponent: a rounding of log2(Z) scales every weight of
+  // the row by the same factor (2^-24 relative per unit of log2(Z))
+  if (lane == 0) a.mz[r] = make_float2(fmaf(m, kLog2e, log2f(z)), 1.f / z);
 }
 
 // c += W V over the wave's key block (V tile in LDS at vb) for one 32-row
-// query tile, with weights W_iu = exp2(s_iu c2 - mzx) * wsc (lane l's query is
-// l % 32; wsc = 0 leaves its row unchanged). c[mt]: rows = queries
+// query tile, with weights W_iu = exp2(s_iu c2 - mzx) (lane l's query is l % 32;
+// mzx = +inf leaves its row unchanged). c[mt]: rows = queries
 // 8 (x / 4) + 4 (l / 32) + x % 4 of the tile, column = head dim 32 mt + l % 32.
 // ZM: wsum collects the lane's weights. FULL: the block has no padding keys,
 // and the score products of the next sub-tile are issued before this
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(256) void k_drift_norm(DriftMfmaArgs a) {
 template <int KT, bool ZM, bool FULL>
 __device__ __forceinline__ void weigh_values(const bf16x8 (&kf)[KT][4], const unsigned char* vb,
                                              const bf16x8 (&qh)[4], const bf16x8 (&qm)[4],
-                                             const bf16x8 (&ql)[4], float mzx, float wsc, float c2,
+                                             const bf16x8 (&ql)[4], float mzx, float c2,
                                              int vlen, int lane, f32x16 (&c)[2], float& wsum) {
   f32x16 s = qk_tile(kf[0], qh, qm, ql);
 #pragma unroll
@@ -290,7 +293,7 @@ __device__ __forceinline__ void weigh_values(const bf16x8 (&kf)[KT][4], const un
       float p[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        p[x] = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mzx)) * wsc;
+        p[x] = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mzx));
         if (ZM) wsum += p[x];
       }
       bf16x8 ph, pm, pl;
@@ -329,7 +332,8 @@ __device__ __forceinline__ void contrib_tile(const DriftMfmaArgs& a, const WaveI
 #pragma unroll
     for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
   float wsum = 0.f;
-  weigh_values<KT, ZM, FULL>(kf, vb, qh, qm, ql, mz.x, mz.y, c2, vlen, lane, c, wsum);
+  weigh_values<KT, ZM, FULL>(kf, vb, qh, qm, ql, i < d.nb ? mz.x : INFINITY, c2, vlen, lane, c,
+                            wsum);
 
   // contrib rows: lanes 0-31 write 128 contiguous bytes of one query row,
   // lanes 32-63 those of the row 4 below. Raw buffer stores off a wave-uniform
@@ -499,8 +503,8 @@ __global__ __launch_bounds__(256, 2) void k_drift_dropsum(DriftMfmaArgs a, Drift
     load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
     const int vlen = block_vlen(d, j);
     // (the pipelined form of full blocks does not fit the registers left here)
-    weigh_values<KT, false, false>(kf, vb, qh, qm, ql, mz.x, drop ? mz.y : 0.f, c2, vlen, lane,
-                                   c, wsum);
+    weigh_values<KT, false, false>(kf, vb, qh, qm, ql, drop ? mz.x : INFINITY, c2, vlen, lane, c,
+                                   wsum);
   }
   // row q of the tile: [row, g, 64]; lanes 0-31 write 128 contiguous bytes
   float* prow = r.part + (((size_t)bh * d.nb + 32 * rt) * G + g) * 64;
@@ -565,7 +569,7 @@ __device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoun
   bf16x8 qh[4], qm[4], ql[4], rh[4], rm[4], rl[4];
   load_qsplit(a.qsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
   load_qsplit(r.rsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, rh, rm, rl);
-  const float2 mz = i < d.nb ? a.mz[(size_t)it.bh * d.nb + i] : make_float2(0.f, 0.f);
+  const float mzx = i < d.nb ? a.mz[(size_t)it.bh * d.nb + i].x : INFINITY;
   const float c2 = d.scale * kLog2e;
   float acc = 0.f;
 #pragma unroll
@@ -579,7 +583,7 @@ __device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoun
     const f32x16 xv = qk_tile(vf, rh, rm, rl);
 #pragma unroll
     for (int x = 0; x < 16; ++x)
-      acc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[x], c2, -mz.x)) * mz.y, xv[x], acc);
+      acc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[x], c2, -mzx)), xv[x], acc);
   }
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
                                                    false, false);
