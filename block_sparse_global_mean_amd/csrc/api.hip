@@ -323,6 +323,9 @@ int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_para
   if (params->drift_objective != BSGM_DRIFT_DROPPED_SUM)
     return fail(BSGM_E_UNSUPPORTED, "streamed drift selection takes the dropped-sum objective");
   if (params->swap_rounds < 0) return fail(BSGM_E_ARG, "swap_rounds must be >= 0");
+  if (bsgm::drift_stream_step_lds(d.nb) > bsgm::kMaxRowLds)
+    return fail(BSGM_E_UNSUPPORTED, "streamed drift selection: a row of %d blocks needs %zu bytes of LDS",
+                d.nb, bsgm::drift_stream_step_lds(d.nb));
   if (!q || !k || !v || !row_ptr || !col_idx || !ws)
     return fail(BSGM_E_ARG, "q, k, v, row_ptr, col_idx and ws must be non-NULL");
   const long long need = (long long)d.B * hb.per_batch;
@@ -475,6 +478,9 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
     if (params->restoration != BSGM_RESTORE_BEST_SWAP) {
       if (params->drift_objective != BSGM_DRIFT_DROPPED_SUM)
         return fail(BSGM_E_UNSUPPORTED, "re-rank restoration takes the dropped-sum objective");
+      if (bsgm::drift_rerank_lds(d.nb) > bsgm::kMaxRowLds)
+        return fail(BSGM_E_UNSUPPORTED, "re-rank selection: a row of %d blocks needs %zu bytes of LDS",
+                    d.nb, bsgm::drift_rerank_lds(d.nb));
       hipError_t e = bsgm::launch_select_drift_rerank(
           d, hb, params->force_frame_first_block ? 1 : 0, params->swap_rounds,
           params->restoration == BSGM_RESTORE_RERANK_TRACK_BEST ? 1 : 0, contrib, row_ptr,

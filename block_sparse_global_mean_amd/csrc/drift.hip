@@ -1424,9 +1424,12 @@ struct DriftRerankArgs {
   int32_t* set_log;   // [rows, rounds + 1, ceil(nb / 32)] or null
 };
 
+// The rank keys of the top-k search exist for rows of up to 512 blocks only.
+__host__ __device__ inline size_t rank_key_bytes(int nb) { return nb <= 512 ? (size_t)nb * 8 : 0; }
+
 __host__ __device__ inline size_t rerank_lds_bytes(int nb) {
   const size_t words = (size_t)(nb + 63) / 64 * 2;   // whole 64-block ballots
-  return align_up16((size_t)nb * 4) * 2 + (size_t)nb * 8 + 2 * words * 4;
+  return align_up16((size_t)nb * 4) * 2 + rank_key_bytes(nb) + 2 * words * 4;
 }
 
 // cur := the forced blocks plus the top k of score (ties: lower block), for one
@@ -1558,7 +1561,8 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
   float* g = reinterpret_cast<float*>(rsm + align_up16((size_t)nb * 4));      // scores
   unsigned long long* keys =
       reinterpret_cast<unsigned long long*>(rsm + 2 * align_up16((size_t)nb * 4));
-  uint32_t* cur = reinterpret_cast<uint32_t*>(keys + nb);   // kept flags, WP words
+  uint32_t* cur = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(keys) +
+                                              rank_key_bytes(nb));   // kept flags, WP words
   uint32_t* best = cur + WP;
   __shared__ __attribute__((aligned(16))) float rv[64];
   __shared__ __attribute__((aligned(16))) float tot[64];
@@ -1665,6 +1669,8 @@ __global__ __launch_bounds__(kRrThreads) void k_select_drift_rerank(DriftRerankA
   if (w == 0) rr_emit(d, a.hb, r, out, a.row_ptr, a.col_idx, lane);
 }
 
+size_t drift_rerank_lds(int nb) { return rerank_lds_bytes(nb); }
+
 hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int force, int rounds,
                                       int track_best, const float* contrib, int32_t* row_ptr,
                                       int32_t* col_idx, float* row_stat, int32_t* set_log,
@@ -1698,8 +1704,10 @@ struct DriftStepArgs {
 };
 
 __host__ __device__ inline size_t step_lds_bytes(int nb) {
-  return align_up16((size_t)nb * 4) + (size_t)nb * 8 + (size_t)(nb + 63) / 64 * 2 * 4;
+  return align_up16((size_t)nb * 4) + rank_key_bytes(nb) + (size_t)(nb + 63) / 64 * 2 * 4;
 }
+
+size_t drift_stream_step_lds(int nb) { return step_lds_bytes(nb); }
 
 __global__ __launch_bounds__(kRrThreads) void k_drift_stream_step(DriftStepArgs a, int round) {
   extern __shared__ __attribute__((aligned(16))) unsigned char ssm[];
@@ -1709,7 +1717,8 @@ __global__ __launch_bounds__(kRrThreads) void k_drift_stream_step(DriftStepArgs 
   const int k = a.hb.keep[(r / nb) % d.H];
   float* g = reinterpret_cast<float*>(ssm);
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ssm + align_up16((size_t)nb * 4));
-  uint32_t* cur = reinterpret_cast<uint32_t*>(keys + nb);
+  uint32_t* cur = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(keys) +
+                                              rank_key_bytes(nb));
   __shared__ int cnt[2][kRrThreads / 64];
   const float* nr = a.sqnorm + (size_t)r * nb;
   if (round == 0) {

@@ -80,6 +80,12 @@ hipError_t launch_select_drift(const Dims& d, const HeadBudget& hb, int force, i
                                int32_t* row_ptr, int32_t* col_idx, float* row_stat,
                                int32_t* swap_log, hipStream_t s);
 
+// Dynamic LDS of the per-row re-rank kernels (materialised and streamed); a
+// row is supported while it fits kMaxRowLds.
+constexpr size_t kMaxRowLds = 160 * 1024;
+size_t drift_rerank_lds(int nb);
+size_t drift_stream_step_lds(int nb);
+
 // Drift selection by re-rank rounds (dropped-sum objective), optionally
 // returning the least-J set seen (track_best). set_log: [rows, rounds + 1,
 // ceil(nb / 32)] kept bitmasks or null.

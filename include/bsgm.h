@@ -174,9 +174,10 @@ int bsgm_drift_scores(const bsgm_layout* layout, const void* q, const void* k, c
  *          highest g (ties: lower block), all blocks at once, for every one of the
  *          swap_rounds rounds. A round may raise J; TRACK_BEST returns the set of
  *          least J among the initial set and every round's set (ties: the
- *          earlier; [ReSS] Table S3), RERANK the last one. Rows of any number of
- *          blocks (BEST_SWAP: at most 4096; above 512 the row is read from
- *          global memory in every pass instead of held on chip).
+ *          earlier; [ReSS] Table S3), RERANK the last one. Rows of up to 19856
+ *          blocks (the row's scores and kept flags sit in LDS; BEST_SWAP: at
+ *          most 4096; above 512 the row is read from global memory in every
+ *          pass instead of held on chip).
  *   q, k       device [B,H,N,D] (TOPK, CDF; may be NULL for DRIFT)
  *   contrib    device float [B,H,Nb,Nb,D] from bsgm_drift_scores (DRIFT only)
  *   zmass      device float [B,H,Nb,Nb] from bsgm_drift_scores (RENORMALISED only)
@@ -227,7 +228,8 @@ int bsgm_select_blocks(const bsgm_layout* layout, const bsgm_select_params* para
  * Errors: BSGM_E_ARG for a NULL q, k, v, row_ptr, col_idx or ws, another mode,
  * or negative swap_rounds; BSGM_E_UNSUPPORTED for the best-swap rule or the
  * renormalised objective; BSGM_E_CAPACITY, BSGM_E_WORKSPACE as
- * bsgm_select_blocks. Rows of any number of blocks.
+ * bsgm_select_blocks, and BSGM_E_UNSUPPORTED for rows of more than 39716
+ * blocks (the row's scores and kept flags sit in LDS).
  */
 int bsgm_select_drift_streamed(const bsgm_layout* layout, const bsgm_select_params* params,
                                const void* q, const void* k, const void* v, int32_t* row_ptr,

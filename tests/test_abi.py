@@ -78,10 +78,10 @@ def test_bad_layouts_rejected(kw, code):
 
 
 def _select(lay, mode=0, keep=(2, 2), force=False, rounds=0, tau=0.9, cap=None, wsb=None,
-            q=16, k=16, contrib=None, rp=16, ci=16, objective=0, zmass=None):
+            q=16, k=16, contrib=None, rp=16, ci=16, objective=0, zmass=None, restoration=0):
     lib = bsgm.library()
     c = _lib.c_layout(lay)
-    P, arr = _lib.c_params(mode, keep, tau, force, rounds, objective)
+    P, arr = _lib.c_params(mode, keep, tau, force, rounds, objective, restoration)
     need = lib.bsgm_col_capacity(ctypes.byref(c), ctypes.byref(P))
     cap = need if cap is None else cap
     wsb = ws(lay, mode) if wsb is None else wsb
@@ -111,6 +111,8 @@ def test_select_argument_errors():
     assert _select(lay, rp=None)[0] == -1
     big = L(frames=2, frame_len=128 * 2100, frame_valid=128 * 2100)
     assert _select(big, mode=2, keep=(5, 5), contrib=16)[0] == -2      # 4200 blocks > 4096
+    wide = L(frames=2, frame_len=128 * 9930, frame_valid=128 * 9930)  # 19860 blocks
+    assert _select(wide, mode=2, keep=(5, 5), contrib=16, restoration=bsgm.RERANK)[0] == -2
 
 
 def _streamed(lay, mode=2, keep=(3, 5), force=False, rounds=2, objective=0,
@@ -150,6 +152,7 @@ def test_streamed_drift_workspace_and_errors():
     for name in ("q", "k", "v", "rp", "ci", "wsp"):
         assert _streamed(lay, **{name: None}) == -1, name
     assert _streamed(lay, cap=8 * 3 + 8 * 5 - 1) == -3
+    assert _streamed(L(frames=2, frame_len=128 * 19860, frame_valid=128 * 19860)) == -2
     assert _streamed(lay, wsb=expect - 1) == -4
 
 
