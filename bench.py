@@ -179,6 +179,9 @@ def main():
     ap.add_argument("--layer", default=None,
                     help="time only this other preset (e.g. vggt_layer_16f_drift) and print "
                          "its per-layer JSON; for profiling its kernels")
+    ap.add_argument("--drift-wide", action="store_true",
+                    help="time only the drift selection on the 100-frame layer (stored and "
+                         "streamed forms) and print its JSON; for profiling its kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -194,6 +197,10 @@ def main():
         res = side_config(bsgm, workloads, torch, dev, args.layer, args.steps)
         calibration_copy(torch, dev, args.calib_copy_mib)
         print(json.dumps({"layer": args.layer, **res}), flush=True)
+        return
+    if args.drift_wide:
+        res = drift_wide_layer(bsgm, workloads, torch, dev)
+        print(json.dumps({"drift_100_frames": res}), flush=True)
         return
     w = workloads.config("vggt_layer_32f_s75")
     lay = w.layout
