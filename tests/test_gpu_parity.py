@@ -1576,6 +1576,19 @@ def test_drift_streamed_wide_and_small_rows(dev, nb, frames, block, dtype):
                  f"streamed re-rank rows of {nb} blocks")
 
 
+def test_drift_streamed_block64_wide_forced(dev):
+    """Blocks of 64, 600 per row (wider than 512, so every round's top k comes
+    from the MSB-first priority search), ragged frames, forced frame blocks,
+    3 rounds with track-best."""
+    lay = custom_layout(25, 24 * 64, 24 * 64 - 36, 64, heads=1)
+    assert lay.nblocks == 600
+    host, vals = random_inputs(lay, 97)
+    keep = np.array([120], dtype=np.int32)
+    rows = [(0, i) for i in spread_rows(lay.nblocks, 24)]
+    run_streamed(dev, lay, host, vals, keep, 3, True, True, rows,
+                 "streamed re-rank 600 blocks of 64, forced")
+
+
 def test_drift_streamed_batch2_ragged(dev):
     """Two batch entries, two heads with different budgets, ragged frames of
     blocks of 64: every row of both batch entries of head 1."""
