@@ -22,6 +22,8 @@
 // (and, for the value sums, its V tile into a private LDS slice), then walks
 // its query tiles with no barrier, so the launches need no workgroup-wide
 // staging and the waves of a CU run independently.
+#include <algorithm>
+
 #include "device_util.h"
 
 namespace bsgm {
@@ -454,71 +456,6 @@ struct DriftRoundArgs {
   float* dot;             // [rows, nb]: <r_i, contrib_ij>
 };
 
-// Residual partial sums: one wave per (b, h, 32-row query tile, run of
-// consecutive key blocks). For each block of its run the wave stages V and K
-// as the contribution kernel does and adds W V, with the weights of the rows
-// for which the block does not count set to zero; a block no row of the tile
-// counts is skipped. A block counts where it is dropped, or with via_kept
-// where it is kept (the smaller set when fewer blocks are kept than dropped:
-// the kept sets of a tile's rows overlap, so most blocks are skipped).
-template <int BLK>
-__global__ __launch_bounds__(256, 2) void k_drift_dropsum(DriftMfmaArgs a, DriftRoundArgs r) {
-  constexpr int KT = BLK / 32, TB = BLK * 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
-  const Dims& d = a.d;
-  const int nrt = (d.nb + 31) / 32, G = r.ngroups, W = (d.nb + 31) >> 5;
-  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (gw >= d.B * d.H * nrt * G) return;
-  const int g = gw % G, rt = (gw / G) % nrt, bh = gw / (G * nrt);
-  const int j0 = (int)((long long)g * d.nb / G), j1 = (int)((long long)(g + 1) * d.nb / G);
-  const int lane = threadIdx.x & 63, n = lane & 31, hh = lane >> 5;
-  const int i = 32 * rt + n;
-  unsigned char* vb = smem + (threadIdx.x >> 6) * TB;
-  bf16x8 qh[4], qm[4], ql[4];
-  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
-  const float2 mz = i < d.nb ? a.mz[(size_t)bh * d.nb + i] : make_float2(0.f, 0.f);
-  const float c2 = d.scale * kLog2e;
-  const uint32_t* krow = r.kept + ((size_t)bh * d.nb + min(i, d.nb - 1)) * W;
-  f32x16 c[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int x = 0; x < 16; ++x) c[mt][x] = 0.f;
-  float wsum = 0.f;   // (unused)
-  // a block counts where its kept bit differs from `flip`; every block counts
-  // for the total (no kept sets)
-  const uint32_t flip = r.via_kept ? 1u : 0u;
-  uint32_t word = 0;
-  int wi = -1;
-  for (int j = j0; j < j1; ++j) {
-    if (r.kept && (j >> 5) != wi) {
-      wi = j >> 5;
-      word = krow[wi] ^ (flip ? 0u : 0xFFFFFFFFu);
-    }
-    const bool drop = i < d.nb && (!r.kept || ((word >> (j & 31)) & 1u) != 0);
-    if (__ballot(drop) == 0ull) continue;   // uniform
-    const size_t tok0 = (size_t)bh * d.N + (size_t)j * BLK;
-    stage_v<BLK>(a.v + tok0 * 64, lane, vb);
-    bf16x8 kf[KT][4];
-    load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
-    const int vlen = block_vlen(d, j);
-    // (the pipelined form of full blocks does not fit the registers left here)
-    weigh_values<KT, false, false>(kf, vb, qh, qm, ql, drop ? mz.x : INFINITY, c2, vlen, lane, c,
-                                   wsum);
-  }
-  // row q of the tile: [row, g, 64]; lanes 0-31 write 128 contiguous bytes
-  float* prow = r.part + (((size_t)bh * d.nb + 32 * rt) * G + g) * 64;
-  const size_t rs = (size_t)G * 64;
-#pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    const int q = 8 * (x >> 2) + 4 * hh + (x & 3);
-    if (32 * rt + q < d.nb) {
-      prow[q * rs + n] = c[0][x];
-      prow[q * rs + 32 + n] = c[1][x];
-    }
-  }
-}
-
 // Per row (one wave): the sum of the group partials in group order. Without
 // kept sets that is o_i, stored as such. Otherwise r (o_i minus the sum with
 // via_kept), its three bf16 terms for the dot products, and J^2 = ||r||^2;
@@ -555,59 +492,258 @@ __global__ __launch_bounds__(256) void k_drift_resid(DriftRoundArgs r, int rows,
   }
 }
 
-// <r_i, contrib_ij> of one 32-row query tile against the wave's key block:
-// X = V R^T on the matrix cores (V rows as the A operand, read from the
-// wave's LDS tile as K fragments are; r as three bf16 terms, so the products
-// are exact), then the weighted sum sum_u w_iu X_ui over the block's real
-// keys. X has the layout of S^T.
+// ---------------------------------------------------------------------------
+// The two round passes, row-stationary. A workgroup of WV waves owns WV
+// consecutive 32-row query tiles of one (b, h) (wave w takes tile WV * rg + w;
+// waves past the last tile only help to stage) and a range of key blocks. Each
+// wave keeps its tile's bf16 terms of qbar (and of r) in registers for the
+// whole range, and every key block's K and V tiles are staged once in LDS for
+// all WV waves, instead of once per wave as in the contribution kernel (whose
+// waves each own a key block and walk query tiles). Staging is double-buffered
+// through registers: the next block's global loads are issued before the
+// waves work on the current block and land in the other LDS buffer after it,
+// so one barrier per block orders both buffers. A (row, block) pair takes the
+// products of the contribution kernel in the same order, and a row's partial
+// sum adds its counted blocks in ascending order, so the results do not depend
+// on the grid.
+// ---------------------------------------------------------------------------
+constexpr int kRsMaskWords = 128;   // counted-block bitmask of a range: up to 4096 blocks
+
+// Register stage of one block's K and V tiles (BLK * 128 bytes each) over the
+// 64 * WV threads of the workgroup: thread x holds 16-byte chunks x, x + 64 WV,
+// ... of each tile. Chunk c of a tile is row c / 8, head dims 8 (c % 8) .. +7,
+// stored at the swizzled LDS place that k_frag and v_frag read.
+template <int BLK, int WV>
+struct RsStage {
+  static constexpr int TB = BLK * 128, CT = BLK * 8, NT = 64 * WV;
+  static constexpr int PT = (CT + NT - 1) / NT;
+  static constexpr bool EVEN = CT % NT == 0;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 rk[PT], rv[PT];
+  // every element is loaded (a thread past the last chunk reloads the last
+  // one), so that no element keeps a value from an earlier load
+  __device__ __forceinline__ void load(const __bf16* k, const __bf16* v, int x) {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int c = EVEN ? x + NT * p : min(x + NT * p, CT - 1);
+      rk[p] = *reinterpret_cast<const u32x4*>(k + (size_t)c * 8);
+      rv[p] = *reinterpret_cast<const u32x4*>(v + (size_t)c * 8);
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* kb, int x) const {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int c = x + NT * p, row = c >> 3, pc = c & 7;
+      if (EVEN || c < CT) {
+        const int off = row * 128 + ((pc ^ swz(row)) << 4);
+        *reinterpret_cast<u32x4*>(kb + off) = rk[p];
+        *reinterpret_cast<u32x4*>(kb + TB + off) = rv[p];
+      }
+    }
+  }
+};
+
+// First block j' >= j of [.., j1) whose bit is set in the LDS mask (word w
+// covers blocks 32 (wb + w) .. +31); j1 if none. Every thread gets the same.
+__device__ __forceinline__ int rs_next(const uint32_t* um, int wb, int j, int j1) {
+  while (j < j1) {
+    const uint32_t m = um[(j >> 5) - wb] >> (j & 31);
+    if (m) return min(j + (int)__builtin_ctz(m), j1);
+    j = (j | 31) + 1;
+  }
+  return j1;
+}
+
+// c += W V over one staged block (K tile at kb, V tile at vb), K fragments read
+// from LDS per 32-key sub-tile; the sub-tile work of weigh_values without the
+// pipelined form.
 template <int KT>
-__device__ __forceinline__ void dot_tile(const DriftMfmaArgs& a, const DriftRoundArgs& r,
-                                         const WaveItem& it, int rt, int vlen, int lane,
-                                         const bf16x8 (&kf)[KT][4], const unsigned char* vb) {
-  const Dims& d = a.d;
-  const int i = 32 * rt + (lane & 31);
-  bf16x8 qh[4], qm[4], ql[4], rh[4], rm[4], rl[4];
-  load_qsplit(a.qsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
-  load_qsplit(r.rsplit + (size_t)it.bh * d.nb * 192, d.nb, 32 * rt, lane, rh, rm, rl);
-  const float mzx = i < d.nb ? a.mz[(size_t)it.bh * d.nb + i].x : INFINITY;
-  const float c2 = d.scale * kLog2e;
-  float acc = 0.f;
+__device__ __forceinline__ void weigh_values_lds(const unsigned char* kb, const unsigned char* vb,
+                                                 const bf16x8 (&qh)[4], const bf16x8 (&qm)[4],
+                                                 const bf16x8 (&ql)[4], float mzx, float c2,
+                                                 int vlen, int lane, f32x16 (&c)[2]) {
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     if (32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
-    f32x16 s = qk_tile(kf[t], qh, qm, ql);
-    mask_padding(s, t, vlen, lane);   // weight 0 for padding keys
-    bf16x8 vf[4];
+    bf16x8 kt[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) vf[ks] = k_frag(vb, t, ks, lane);
-    const f32x16 xv = qk_tile(vf, rh, rm, rl);
+    for (int ks = 0; ks < 4; ++ks) kt[ks] = k_frag(kb, t, ks, lane);
+    f32x16 s = qk_tile(kt, qh, qm, ql);
+    mask_padding(s, t, vlen, lane);
 #pragma unroll
-    for (int x = 0; x < 16; ++x)
-      acc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[x], c2, -mzx)), xv[x], acc);
+    for (int e = 0; e < 2; ++e) {
+      float p[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) p[x] = __builtin_amdgcn_exp2f(fmaf(s[8 * e + x], c2, -mzx));
+      bf16x8 ph, pm, pl;
+      split3(p, ph, pm, pl);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 vf = v_frag(vb, 32 * t + 16 * e, mt, lane);
+        c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vf, c[mt], 0, 0, 0);
+        c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, vf, c[mt], 0, 0, 0);
+        c[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, vf, c[mt], 0, 0, 0);
+      }
+    }
   }
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
-                                                   false, false);
-  const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-  if (lane < 32 && i < d.nb) r.dot[((size_t)it.bh * d.nb + i) * d.nb + it.j] = tot;
 }
 
-// Same work split as the contributions: one wave per (b, h, key block, run of
-// query tiles), K fragments in registers, V in the wave's LDS tile.
-template <int BLK>
-__global__ __launch_bounds__(256, 2) void k_drift_dot(DriftMfmaArgs a, DriftRoundArgs r, int rtpw) {
+// Residual partial sums: workgroup (b, h, row group rg, key group g) sums W V
+// over the blocks [g nb / G, (g + 1) nb / G) that its rows count, the weights of
+// a row for which a block does not count set to zero. A block counts where it
+// is dropped, or with via_kept where it is kept (the smaller set when fewer
+// blocks are kept than dropped; the kept sets of neighbouring rows overlap).
+// A block is staged when some row of the workgroup counts it, and a wave adds
+// it when some row of its tile does. Grid: B * H * ceil(nrt / WV) * ngroups.
+template <int BLK, int WV>
+__global__ __launch_bounds__(64 * WV, 2) void k_drift_dropsum(DriftMfmaArgs a, DriftRoundArgs r) {
   constexpr int KT = BLK / 32, TB = BLK * 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TB];
+  __shared__ uint32_t umask[kRsMaskWords];
   const Dims& d = a.d;
-  WaveItem it;
-  if (!wave_item(d, rtpw, it)) return;
-  const int lane = threadIdx.x & 63;
-  unsigned char* vb = smem + (threadIdx.x >> 6) * TB;
-  const size_t tok0 = (size_t)it.bh * d.N + (size_t)it.j * BLK;
-  stage_v<BLK>(a.v + tok0 * 64, lane, vb);
-  bf16x8 kf[KT][4];
-  load_k_frags<KT>(a.k + tok0 * 64, lane, kf);
-  const int vlen = block_vlen(d, it.j);
-  for (int rt = it.rt0; rt < it.rt1; ++rt) dot_tile<KT>(a, r, it, rt, vlen, lane, kf, vb);
+  const int nrt = (d.nb + 31) / 32, ngr = (nrt + WV - 1) / WV, G = r.ngroups, W = (d.nb + 31) >> 5;
+  const int g = blockIdx.x % G, rg = (blockIdx.x / G) % ngr, bh = blockIdx.x / (G * ngr);
+  const int j0 = (int)((long long)g * d.nb / G), j1 = (int)((long long)(g + 1) * d.nb / G);
+  const int x = threadIdx.x, lane = x & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(x >> 6);
+  const int rt = rg * WV + w, i = 32 * rt + n;
+  const uint32_t inv = r.via_kept ? 0u : 0xFFFFFFFFu;   // counted: kept bits, or dropped bits
+  const int wb = j0 >> 5;
+  // the blocks that some row of the workgroup counts
+  if (r.kept) {
+    const int nw = ((j1 - 1) >> 5) - wb + 1, row0 = 32 * WV * rg;
+    const int nrows = min(32 * WV, d.nb - row0);
+    for (int y = x; y < nw; y += 64 * WV) umask[y] = 0u;
+    __syncthreads();
+    const uint32_t* kr = r.kept + ((size_t)bh * d.nb + row0) * W + wb;
+    for (int y = x; y < nrows * nw; y += 64 * WV) {
+      const int q = y / nw, wi = y - q * nw;
+      const uint32_t word = kr[(size_t)q * W + wi] ^ inv;
+      if (word) atomicOr(&umask[wi], word);
+    }
+    __syncthreads();
+  }
+  auto next = [&](int j) { return r.kept ? rs_next(umask, wb, j, j1) : j; };
+  const size_t tokb = (size_t)bh * d.N;
+  RsStage<BLK, WV> st;
+  int j = next(j0);
+  if (j < j1) {
+    st.load(a.k + (tokb + (size_t)j * BLK) * 64, a.v + (tokb + (size_t)j * BLK) * 64, x);
+    st.store(smem[0], x);
+  }
+  bf16x8 qh[4], qm[4], ql[4];
+  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  const bool live = i < d.nb;
+  const float mzx_row = live ? a.mz[(size_t)bh * d.nb + i].x : INFINITY;
+  const float c2 = d.scale * kLog2e;
+  const uint32_t* krow = r.kept ? r.kept + ((size_t)bh * d.nb + min(i, d.nb - 1)) * W : nullptr;
+  // the row's counted bits of the word holding the current block
+  uint32_t wcur = (krow && j < j1) ? krow[j >> 5] ^ inv : 0xFFFFFFFFu;
+  f32x16 c[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[mt][e] = 0.f;
+  __syncthreads();
+  int cur = 0;
+  // The stage is loaded and stored in every pass (the last block's pass
+  // reloads that block into the idle buffer), so that no stage value lives
+  // across a pass.
+  while (j < j1) {
+    const int jn = next(j + 1), jl = jn < j1 ? jn : j;
+    // the next block's word first, then its tiles: both land before the store
+    uint32_t wnext = wcur;
+    if (krow && jn < j1 && (jn >> 5) != (j >> 5)) wnext = krow[jn >> 5] ^ inv;
+    st.load(a.k + (tokb + (size_t)jl * BLK) * 64, a.v + (tokb + (size_t)jl * BLK) * 64, x);
+    const bool drop = live && ((wcur >> (j & 31)) & 1u) != 0;
+    if (__ballot(drop) != 0ull)   // uniform
+      weigh_values_lds<KT>(smem[cur], smem[cur] + TB, qh, qm, ql, drop ? mzx_row : INFINITY, c2,
+                           block_vlen(d, j), lane, c);
+    st.store(smem[cur ^ 1], x);
+    if (jn >= j1) break;
+    __syncthreads();
+    cur ^= 1;
+    j = jn;
+    wcur = wnext;
+  }
+  if (rt >= nrt) return;
+  float* prow = r.part + (((size_t)bh * d.nb + 32 * rt) * G + g) * 64;
+  const size_t rs = (size_t)G * 64;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int q = 8 * (e >> 2) + 4 * hh + (e & 3);
+    if (32 * rt + q < d.nb) {
+      prow[q * rs + n] = c[0][e];
+      prow[q * rs + 32 + n] = c[1][e];
+    }
+  }
+}
+
+// <r_i, contrib_ij> for every block of a range: workgroup (b, h, row group rg,
+// range g of ngroups equal ranges). Per block and query tile, X = V R^T on the
+// matrix cores (V rows as the A operand, read from LDS as K fragments are; r as
+// three bf16 terms, so the products are exact; X has the layout of S^T), then
+// the weighted sum sum_u w_iu X_ui over the block's real keys.
+template <int BLK, int WV>
+__global__ __launch_bounds__(64 * WV, 2) void k_drift_dot(DriftMfmaArgs a, DriftRoundArgs r) {
+  constexpr int KT = BLK / 32, TB = BLK * 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TB];
+  const Dims& d = a.d;
+  const int nrt = (d.nb + 31) / 32, ngr = (nrt + WV - 1) / WV, G = r.ngroups;
+  const int g = blockIdx.x % G, rg = (blockIdx.x / G) % ngr, bh = blockIdx.x / (G * ngr);
+  const int j0 = (int)((long long)g * d.nb / G), j1 = (int)((long long)(g + 1) * d.nb / G);
+  const int x = threadIdx.x, lane = x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(x >> 6);
+  const int rt = rg * WV + w, i = 32 * rt + (lane & 31);
+  const size_t tokb = (size_t)bh * d.N;
+  RsStage<BLK, WV> st;
+  if (j0 < j1) {
+    st.load(a.k + (tokb + (size_t)j0 * BLK) * 64, a.v + (tokb + (size_t)j0 * BLK) * 64, x);
+    st.store(smem[0], x);
+  }
+  bf16x8 qh[4], qm[4], ql[4], rh[4], rm[4], rl[4];
+  load_qsplit(a.qsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, qh, qm, ql);
+  load_qsplit(r.rsplit + (size_t)bh * d.nb * 192, d.nb, 32 * rt, lane, rh, rm, rl);
+  const float mzx = i < d.nb ? a.mz[(size_t)bh * d.nb + i].x : INFINITY;
+  const float c2 = d.scale * kLog2e;
+  float* drow = r.dot + ((size_t)bh * d.nb + min(i, d.nb - 1)) * d.nb;
+  const bool busy = rt < nrt;
+  __syncthreads();
+  int cur = 0;
+  for (int j = j0; j < j1; ++j) {
+    // loaded and stored in every pass, as in k_drift_dropsum
+    const int jl = min(j + 1, j1 - 1);
+    st.load(a.k + (tokb + (size_t)jl * BLK) * 64, a.v + (tokb + (size_t)jl * BLK) * 64, x);
+    if (busy) {
+      const unsigned char* kb = smem[cur];
+      const unsigned char* vb = smem[cur] + TB;
+      const int vlen = block_vlen(d, j);
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        if (32 * t >= vlen) break;   // uniform: the remaining sub-tiles are padding
+        bf16x8 kt[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kt[ks] = k_frag(kb, t, ks, lane);
+        f32x16 s = qk_tile(kt, qh, qm, ql);
+        mask_padding(s, t, vlen, lane);   // weight 0 for padding keys
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kt[ks] = k_frag(vb, t, ks, lane);
+        const f32x16 xv = qk_tile(kt, rh, rm, rl);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[e], c2, -mzx)), xv[e], acc);
+      }
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
+                                                       false, false);
+      const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      if (lane < 32 && i < d.nb) drow[j] = tot;
+    }
+    st.store(smem[cur ^ 1], x);
+    if (j + 1 >= j1) break;
+    __syncthreads();
+    cur ^= 1;
+  }
 }
 
 // Query tiles per wave for `slots` resident waves on the chip: among the
@@ -712,21 +848,49 @@ hipError_t launch_drift_sqnorms_bf16(const Dims& d, const float* qbar, void* qsp
 
 int drift_round_groups_max(const Dims& d) { return d.nb < 16 ? d.nb : 16; }
 
-// Groups of key blocks per query tile in the residual pass: the count of least
-// makespan at `slots` resident waves (whole rounds of waves times the blocks
-// a wave walks), the larger count among equals.
-static int drift_round_groups(const Dims& d, int slots) {
-  const long long tiles = (long long)d.B * d.H * ((d.nb + 31) / 32);
-  int best = 1;
-  long long best_span = -1;
-  for (int g = 1; g <= drift_round_groups_max(d); ++g) {
-    const long long span = ((tiles * g + slots - 1) / slots) * ((d.nb + g - 1) / g);
-    if (best_span < 0 || span <= best_span) {
-      best_span = span;
-      best = g;
-    }
-  }
-  return best;
+// Waves per workgroup of the row-stationary passes: the query tiles of a
+// (b, h) in equal groups of three or four (four, some idle, for rows of at
+// most 64 blocks: fewer waves would hold a whole block's stage each).
+static int rs_waves(const Dims& d) {
+  const int nrt = (d.nb + 31) / 32;
+  const int ngr = (nrt + 3) / 4;
+  const int wv = (nrt + ngr - 1) / ngr;
+  return wv < 3 ? 4 : wv;
+}
+
+// Least group count whose ranges fit the counted-block mask (4096 blocks,
+// less one word for a range that starts inside a word). At most
+// drift_round_groups_max for every row width the streamed selection accepts.
+static int rs_min_groups(const Dims& d) {
+  const int span = 32 * (kRsMaskWords - 1);
+  return (d.nb + span - 1) / span;
+}
+
+// Ranges of key blocks per row group in the dot pass: 16 (measured best on 176-
+// and 1100-block rows against 4 to 64), one block each on narrower rows.
+static int rs_dot_ranges(const Dims& d) { return std::min(16, d.nb); }
+
+template <bool DROPSUM, int BLK, int WV>
+static void launch_rs_k(const DriftMfmaArgs& a, const DriftRoundArgs& r, dim3 grid, hipStream_t s) {
+  if (DROPSUM)
+    hipLaunchKernelGGL((k_drift_dropsum<BLK, WV>), grid, dim3(64 * WV), 0, s, a, r);
+  else
+    hipLaunchKernelGGL((k_drift_dot<BLK, WV>), grid, dim3(64 * WV), 0, s, a, r);
+}
+
+template <bool DROPSUM, int BLK>
+static void launch_rs_b(const DriftMfmaArgs& a, const DriftRoundArgs& r, hipStream_t s) {
+  const Dims& d = a.d;
+  const int nrt = (d.nb + 31) / 32, wv = rs_waves(d), ngr = (nrt + wv - 1) / wv;
+  const dim3 grid((unsigned)((long long)d.B * d.H * ngr * r.ngroups));
+  if (wv == 3) launch_rs_k<DROPSUM, BLK, 3>(a, r, grid, s);
+  else launch_rs_k<DROPSUM, BLK, 4>(a, r, grid, s);
+}
+
+template <bool DROPSUM>
+static void launch_rs(const DriftMfmaArgs& a, const DriftRoundArgs& r, hipStream_t s) {
+  if (a.d.blk == 128) launch_rs_b<DROPSUM, 128>(a, r, s);
+  else launch_rs_b<DROPSUM, 64>(a, r, s);
 }
 
 hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const void* k,
@@ -736,14 +900,11 @@ hipError_t launch_drift_residual_bf16(const Dims& d, const void* qsplit, const v
                                       hipStream_t s) {
   DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
                   const_cast<float2*>(mz), nullptr, nullptr, nullptr};
-  const int G = drift_round_groups(d, compute_units() * 8);
+  // as many key groups as part holds (16 measured best on 176- and 1100-block rows)
+  const int G = drift_round_groups_max(d);
+  if (G < rs_min_groups(d)) return hipErrorInvalidValue;   // rows too wide for the mask
   DriftRoundArgs r{kept, via_kept, obar, part, G, (__bf16*)rsplit, nullptr};
-  const long long waves = (long long)d.B * d.H * ((d.nb + 31) / 32) * G;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (d.blk == 128)
-    hipLaunchKernelGGL(k_drift_dropsum<128>, grid, dim3(256), 0, s, a, r);
-  else
-    hipLaunchKernelGGL(k_drift_dropsum<64>, grid, dim3(256), 0, s, a, r);
+  launch_rs<true>(a, r, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_drift_resid, dim3((d.rows + 3) / 4), dim3(256), 0, s, r, d.rows,
@@ -765,13 +926,8 @@ hipError_t launch_drift_dot_bf16(const Dims& d, const void* qsplit, const void* 
                                  hipStream_t s) {
   DriftMfmaArgs a{d, nullptr, (__bf16*)qsplit, (const __bf16*)k, (const __bf16*)v, nullptr,
                   const_cast<float2*>(mz), nullptr, nullptr, nullptr};
-  DriftRoundArgs r{nullptr, 0, nullptr, nullptr, 0, (__bf16*)rsplit, dot};
-  int rt = 0;
-  const dim3 grid = wave_grid(d, compute_units() * 8, rt);
-  if (d.blk == 128)
-    hipLaunchKernelGGL(k_drift_dot<128>, grid, dim3(256), 0, s, a, r, rt);
-  else
-    hipLaunchKernelGGL(k_drift_dot<64>, grid, dim3(256), 0, s, a, r, rt);
+  DriftRoundArgs r{nullptr, 0, nullptr, nullptr, rs_dot_ranges(d), (__bf16*)rsplit, dot};
+  launch_rs<false>(a, r, s);
   return hipGetLastError();
 }
 
