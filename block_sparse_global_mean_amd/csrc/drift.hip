@@ -1689,7 +1689,8 @@ hipError_t launch_select_drift_rerank(const Dims& d, const HeadBudget& hb, int f
 // Re-rank rounds in the expanded form (no contributions kept): the same rule
 // as k_select_drift_rerank, with the scores assembled from per-(row, block)
 // scalars that the round kernels recompute, g_j = 2 <r, c_j> -/+ ||c_j||^2.
-// One workgroup per row selects the round's set into a global bitmask.
+// One workgroup per row selects the round's set into a global bitmask (rows
+// wider than 2 048 blocks; k_drift_stream_step_wave below takes the others).
 // ---------------------------------------------------------------------------
 struct DriftStepArgs {
   Dims d;
@@ -1739,6 +1740,69 @@ __global__ __launch_bounds__(kRrThreads) void k_drift_stream_step(DriftStepArgs 
   }
 }
 
+// The same step with one wave per row, for rows of up to 64 P blocks: block
+// 64 p + lane's priority sits in register p of its lane, and the MSB-first
+// search and the tie pass of rr_select count across the wave (lane counts and
+// one wave sum per step; ballots for the ties), so no barrier is needed. It selects the same set (forced blocks first, then the highest
+// g, ties to the lower block).
+template <int P>
+__global__ __launch_bounds__(256) void k_drift_stream_step_wave(DriftStepArgs a, int round) {
+  const Dims& d = a.d;
+  const int nb = d.nb, W = (nb + 31) >> 5;
+  const int r = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (r >= d.rows) return;   // wave-uniform
+  const int k = a.hb.keep[(r / nb) % d.H];
+  const float* nr = a.sqnorm + (size_t)r * nb;
+  const float* dt = round > 0 ? a.dot + (size_t)r * nb : nullptr;
+  const uint32_t* pv = round > 0 ? a.prev + (size_t)r * W : nullptr;
+  uint32_t key[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int j = 64 * p + lane;
+    key[p] = 0u;
+    if (j < nb) {
+      float g = nr[j];
+      if (round > 0) {
+        const bool in = ((pv[j >> 5] >> (j & 31)) & 1u) != 0;
+        g = 2.f * dt[j] + (in ? g : -g);
+      }
+      key[p] = (a.force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(g);
+    }
+  }
+  // blocks whose priority is at least cand: a count per lane, then one wave
+  // sum (exact in fp32 for up to 2^24 blocks)
+  auto count_ge = [&](uint32_t cand) {
+    float c = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) c += (64 * p + lane < nb && key[p] >= cand) ? 1.f : 0.f;
+    return (int)wave_allsum(c);
+  };
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (count_ge(cand) >= k) T = cand;
+  }
+  int need = k - (T == 0xFFFFFFFFu ? 0 : count_ge(T + 1u));
+  uint32_t* nx = a.next + (size_t)r * W;
+  int32_t* lg = a.set_log ? a.set_log + ((size_t)r * (a.rounds + 1) + round) * W : nullptr;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (64 * p >= nb) break;   // uniform
+    const bool valid = 64 * p + lane < nb;
+    const bool tie = valid && key[p] == T;
+    const unsigned long long tm = __ballot(tie);
+    const bool in = valid && (key[p] > T || (tie && lanes_below(tm) < need));
+    const unsigned long long m = __ballot(in);
+    if (lane < 2 && 2 * p + lane < W) {
+      const uint32_t word = lane ? (uint32_t)(m >> 32) : (uint32_t)m;
+      nx[2 * p + lane] = word;
+      if (lg) lg[2 * p + lane] = (int32_t)word;
+    }
+    need -= min(need, __popcll(tm));
+  }
+}
+
 // The CSR of the final sets (one wave per row) and, when asked, J = sqrt(jsq).
 struct DriftEmitArgs {
   Dims d;
@@ -1763,6 +1827,18 @@ hipError_t launch_drift_stream_step(const Dims& d, const HeadBudget& hb, int for
                                     const uint32_t* prev, uint32_t* next, int32_t* set_log,
                                     hipStream_t s) {
   DriftStepArgs a{d, hb, force, rounds, sqnorm, dot, prev, next, set_log};
+  if (d.nb <= 2048) {
+    const dim3 grid((d.rows + 3) / 4);
+    if (d.nb <= 256)
+      hipLaunchKernelGGL(k_drift_stream_step_wave<4>, grid, dim3(256), 0, s, a, round);
+    else if (d.nb <= 512)
+      hipLaunchKernelGGL(k_drift_stream_step_wave<8>, grid, dim3(256), 0, s, a, round);
+    else if (d.nb <= 1024)
+      hipLaunchKernelGGL(k_drift_stream_step_wave<16>, grid, dim3(256), 0, s, a, round);
+    else
+      hipLaunchKernelGGL(k_drift_stream_step_wave<32>, grid, dim3(256), 0, s, a, round);
+    return hipGetLastError();
+  }
   const size_t lds = step_lds_bytes(d.nb);
   hipError_t e = hipFuncSetAttribute((const void*)k_drift_stream_step,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -1556,14 +1556,18 @@ def test_drift_streamed_exact_ties(dev, force):
         assert got == sorted(sets[0]), (i, len(got))
 
 
-@pytest.mark.parametrize("nb,frames,block,dtype", [(1100, 100, 128, "bf16"), (61, 1, 64, "bf16"),
-                                                   (61, 1, 64, "f32"), (24, 3, 128, "f32")])
+@pytest.mark.parametrize("nb,frames,block,dtype", [(1100, 100, 128, "bf16"), (2200, 25, 64, "bf16"),
+                                                   (61, 1, 64, "bf16"), (61, 1, 64, "f32"),
+                                                   (24, 3, 128, "f32")])
 def test_drift_streamed_wide_and_small_rows(dev, nb, frames, block, dtype):
-    """Rows of 1100 key blocks (a 100-frame layer's width), a single ragged
-    frame of 61 blocks of 64 in bf16 and fp32 (the vector-ALU passes), and
-    three fp32 frames of 8 blocks of 128."""
+    """Rows of 1100 key blocks (a 100-frame layer's width; one wave per row in
+    the selection step), of 2200 blocks of 64 (one workgroup per row there), a
+    single ragged frame of 61 blocks of 64 in bf16 and fp32 (the vector-ALU
+    passes), and three fp32 frames of 8 blocks of 128."""
     if nb == 1100:
         lay = custom_layout(frames, 1408, 1374, block, heads=1)
+    elif nb == 2200:
+        lay = custom_layout(frames, 88 * 64, 88 * 64 - 30, block, heads=1)
     elif nb == 61:
         lay = custom_layout(1, 61 * 64, 61 * 64 - 40, block, heads=1, dtype=dtype)
     else:
