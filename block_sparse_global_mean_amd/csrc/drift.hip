@@ -1756,19 +1756,32 @@ __global__ __launch_bounds__(256) void k_drift_stream_step_wave(DriftStepArgs a,
   const float* nr = a.sqnorm + (size_t)r * nb;
   const float* dt = round > 0 ? a.dot + (size_t)r * nb : nullptr;
   const uint32_t* pv = round > 0 ? a.prev + (size_t)r * W : nullptr;
+  // every load unconditional (slots past the row reread its last block), so
+  // that all of them are in flight at once
+  float g[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) g[p] = nr[min(64 * p + lane, nb - 1)];
+  if (round > 0) {
+    float dv[P];
+    uint32_t pw[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int j = min(64 * p + lane, nb - 1);
+      dv[p] = dt[j];
+      pw[p] = pv[j >> 5];
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int j = 64 * p + lane;
+      const bool in = ((pw[p] >> (j & 31)) & 1u) != 0;
+      g[p] = 2.f * dv[p] + (in ? g[p] : -g[p]);
+    }
+  }
   uint32_t key[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int j = 64 * p + lane;
-    key[p] = 0u;
-    if (j < nb) {
-      float g = nr[j];
-      if (round > 0) {
-        const bool in = ((pv[j >> 5] >> (j & 31)) & 1u) != 0;
-        g = 2.f * dt[j] + (in ? g : -g);
-      }
-      key[p] = (a.force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(g);
-    }
+    key[p] = j >= nb ? 0u : (a.force && block_forced(d, j)) ? 0xFFFFFFFFu : orderable(g[p]);
   }
   // blocks whose priority is at least cand: a count per lane, then one wave
   // sum (exact in fp32 for up to 2^24 blocks)
@@ -1835,6 +1848,10 @@ hipError_t launch_drift_stream_step(const Dims& d, const HeadBudget& hb, int for
       hipLaunchKernelGGL(k_drift_stream_step_wave<8>, grid, dim3(256), 0, s, a, round);
     else if (d.nb <= 1024)
       hipLaunchKernelGGL(k_drift_stream_step_wave<16>, grid, dim3(256), 0, s, a, round);
+    else if (d.nb <= 1280)
+      hipLaunchKernelGGL(k_drift_stream_step_wave<20>, grid, dim3(256), 0, s, a, round);
+    else if (d.nb <= 1536)
+      hipLaunchKernelGGL(k_drift_stream_step_wave<24>, grid, dim3(256), 0, s, a, round);
     else
       hipLaunchKernelGGL(k_drift_stream_step_wave<32>, grid, dim3(256), 0, s, a, round);
     return hipGetLastError();
