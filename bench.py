@@ -11,7 +11,7 @@ bf16, blocks of 128, 75 % block sparsity.
 Prints one JSON line (see the keys below). `value` is the layer-effective
 throughput: algorithmic FLOP of the executed blocks (4 * 128^2 * 64 per
 executed block pair) divided by the measured time of the whole step. The
-step pools Q and K (`pool_blocks`), then selects from the pooled means
+step pools Q and K in one launch (`pool_blocks2`), then selects from the pooled means
 (`select_blocks_pooled`) while a second stream makes the fp16 copy of K
 (`attn_prepare`), so the copy's HBM stream overlaps the selection kernel
 rather than the pooling. The prepared attention call then runs the
@@ -235,8 +235,7 @@ def main():
     kbar = torch.empty_like(qbar)
 
     def pool():
-        bsgm.pool_blocks(lay, q, out=qbar)
-        bsgm.pool_blocks(lay, k, out=kbar)
+        bsgm.pool_blocks2(lay, q, k, out0=qbar, out1=kbar)
 
     def prepare_side():
         side.wait_stream(torch.cuda.current_stream())

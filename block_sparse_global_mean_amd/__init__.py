@@ -11,7 +11,8 @@ from ._lib import (  # noqa: F401
     VASC, BsgmError, EXPORTS, LIB_PATH,
     attn_prepare, attn_workspace_bytes, col_capacity, drift_scores, drift_streamed_workspace_bytes,
     fused_workspace_bytes, library,
-    NOALLOC_SCRATCH_BYTES, pool_blocks, select_blocks, select_blocks_fused, select_blocks_noalloc,
+    NOALLOC_SCRATCH_BYTES, pool_blocks, pool_blocks2, select_blocks, select_blocks_fused,
+    select_blocks_noalloc,
     select_blocks_pooled, select_drift_streamed, sparse_attn_fwd, special_rows_dense_fwd, special_rows_workspace_bytes,
     vasc_pairs, vasc_select_blocks, version, workspace_bytes,
 )

@@ -27,7 +27,7 @@ STATUS = {0: "BSGM_OK", -1: "BSGM_E_ARG", -2: "BSGM_E_UNSUPPORTED", -3: "BSGM_E_
 
 # Every symbol include/bsgm.h declares.
 EXPORTS = ("bsgm_version", "bsgm_last_error", "bsgm_workspace_bytes", "bsgm_col_capacity",
-           "bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
+           "bsgm_pool_blocks", "bsgm_pool_blocks2", "bsgm_drift_scores", "bsgm_select_blocks", "bsgm_sparse_attn_fwd",
            "bsgm_special_rows_workspace_bytes", "bsgm_special_rows_dense_fwd",
            "bsgm_vasc_select_blocks", "bsgm_attn_workspace_bytes", "bsgm_attn_prepare",
            "bsgm_sparse_attn_fwd_prepared", "bsgm_select_blocks_fused", "bsgm_fused_workspace_bytes",
@@ -75,6 +75,7 @@ def library() -> ctypes.CDLL:
         lib.bsgm_col_capacity.argtypes = [lp, pp]
         lib.bsgm_col_capacity.restype = ctypes.c_int64
         lib.bsgm_pool_blocks.argtypes = [lp, vp, vp, vp]
+        lib.bsgm_pool_blocks2.argtypes = [lp, vp, vp, vp, vp, vp]
         lib.bsgm_drift_scores.argtypes = [lp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.bsgm_select_blocks.argtypes = [lp, pp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                            vp, sz, vp]
@@ -100,7 +101,7 @@ def library() -> ctypes.CDLL:
                                                    vp, vp, sz, vp]
         lib.bsgm_drift_streamed_workspace_bytes.argtypes = [lp]
         lib.bsgm_drift_streamed_workspace_bytes.restype = sz
-        for name in ("bsgm_pool_blocks", "bsgm_drift_scores", "bsgm_select_blocks",
+        for name in ("bsgm_pool_blocks", "bsgm_pool_blocks2", "bsgm_drift_scores", "bsgm_select_blocks",
                      "bsgm_sparse_attn_fwd", "bsgm_special_rows_dense_fwd",
                      "bsgm_vasc_select_blocks", "bsgm_select_blocks_fused", "bsgm_select_blocks_pooled",
                      "bsgm_select_blocks_noalloc", "bsgm_select_drift_streamed",
@@ -216,6 +217,26 @@ def pool_blocks(layout, x: torch.Tensor, out: Optional[torch.Tensor] = None, str
     L = c_layout(layout)
     _check(library().bsgm_pool_blocks(ctypes.byref(L), _ptr(x), _ptr(out), _stream(stream)))
     return out
+
+
+def pool_blocks2(layout, x0: torch.Tensor, x1: torch.Tensor, out0: Optional[torch.Tensor] = None,
+                 out1: Optional[torch.Tensor] = None, stream=None):
+    """Block means of two tensors (e.g. Q and K) in one launch -> (out0, out1),
+    each float32 [B,H,Nb,64]; the same values as two pool_blocks calls."""
+    n, nb, _ = _dims(layout)
+    mshape = (layout.batch, layout.heads, nb, layout.head_dim)
+    outs = []
+    for x, name, out, oname in ((x0, "x0", out0, "out0"), (x1, "x1", out1, "out1")):
+        _expect(x, name, _tdtype(layout), (layout.batch, layout.heads, n, layout.head_dim))
+        _opt(out, oname, torch.float32, mshape)
+        outs.append(out if out is not None else
+                    torch.empty(mshape, dtype=torch.float32, device=x.device))
+    if outs[0].data_ptr() == outs[1].data_ptr():
+        raise ValueError("out0 and out1 must be different buffers")
+    L = c_layout(layout)
+    _check(library().bsgm_pool_blocks2(ctypes.byref(L), _ptr(x0), _ptr(outs[0]), _ptr(x1),
+                                       _ptr(outs[1]), _stream(stream)))
+    return outs[0], outs[1]
 
 
 def drift_scores(layout, q, k, v, contrib=None, score=None, workspace=None, stream=None,

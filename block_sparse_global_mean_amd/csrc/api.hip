@@ -234,7 +234,7 @@ int run_pooled_select(const bsgm::Dims& d, const bsgm::HeadBudget& hb, int dtype
 
 extern "C" {
 
-int32_t bsgm_version(void) { return 10500; }
+int32_t bsgm_version(void) { return 10600; }
 
 const char* bsgm_last_error(void) { return g_err.c_str(); }
 
@@ -265,6 +265,19 @@ int bsgm_pool_blocks(const bsgm_layout* layout, const void* x, float* mean, void
   if (st != BSGM_OK) return st;
   if (!x || !mean) return fail(BSGM_E_ARG, "x and mean must be non-NULL");
   hipError_t e = bsgm::launch_pool(d, layout->dtype, x, mean, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  return ok();
+}
+
+int bsgm_pool_blocks2(const bsgm_layout* layout, const void* x0, float* mean0, const void* x1,
+                      float* mean1, void* stream) {
+  bsgm::Dims d;
+  int st = check_layout(layout, &d);
+  if (st != BSGM_OK) return st;
+  if (!x0 || !mean0 || !x1 || !mean1) return fail(BSGM_E_ARG, "x0, mean0, x1 and mean1 must be non-NULL");
+  const void* xs[2] = {x0, x1};
+  float* means[2] = {mean0, mean1};
+  hipError_t e = bsgm::launch_pool_n(d, layout->dtype, 2, xs, means, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   return ok();
 }

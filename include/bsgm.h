@@ -128,6 +128,17 @@ int64_t bsgm_col_capacity(const bsgm_layout* layout, const bsgm_select_params* p
  */
 int bsgm_pool_blocks(const bsgm_layout* layout, const void* x, float* mean, void* stream);
 
+/* Block mean pool of two tensors of one layout in a single launch, typically
+ * the Q and K of a layer before selection from pooled means (same sources as
+ * bsgm_pool_blocks). mean0 and mean1 receive exactly what two
+ * bsgm_pool_blocks calls would write.
+ *   x0, x1       device [B,H,N,D] of layout->dtype
+ *   mean0, mean1 device float [B,H,Nb,D]; must not overlap each other or x0, x1
+ * Returns BSGM_E_ARG if any pointer is NULL.
+ */
+int bsgm_pool_blocks2(const bsgm_layout* layout, const void* x0, float* mean0, const void* x1,
+                      float* mean1, void* stream);
+
 /* Drift contributions ([ReSS] abstract, Figs. 1-3: the shift that dropping a
  * key block leaves in what attention writes into the residual stream).
  * For pooled query block i (mean of Q over its real tokens) and every real key

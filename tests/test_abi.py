@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_symbols():
     text = open(os.path.join(ROOT, "include", "bsgm.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bsgm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bsgm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = bsgm.library()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert bsgm.version() == 10500
+    assert bsgm.version() == 10600
 
 
 class L:
@@ -276,6 +276,10 @@ def test_pool_and_drift_null_arguments():
                                  None) == -1
     assert lib.bsgm_drift_scores(ctypes.byref(c), one, one, one, one, one, None, one, 10, None) == -4
     assert lib.bsgm_pool_blocks(None, one, one, None) == -1
+    two = ctypes.c_void_p(32)
+    assert lib.bsgm_pool_blocks2(ctypes.byref(c), one, two, None, two, None) == -1
+    assert lib.bsgm_pool_blocks2(ctypes.byref(c), one, None, one, two, None) == -1
+    assert lib.bsgm_pool_blocks2(None, one, two, one, two, None) == -1
 
 
 def test_attention_workspace():

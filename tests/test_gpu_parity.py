@@ -121,6 +121,31 @@ def test_pool_matches_oracle(dev, case):
     np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6 * max(1.0, np.abs(ref).max()))
 
 
+@pytest.mark.parametrize("case", ["tiny_f32", "ragged_bf16_b64", "ragged_bf16_b128_2batch"])
+def test_pool_two_tensors_one_launch(dev, case):
+    """pool_blocks2 pools two tensors in one launch: both means equal, bit for
+    bit, what two pool_blocks calls write, and match the oracle's means."""
+    say(f"pool two tensors {case}")
+    if case == "tiny_f32":
+        w, data = preset(0)
+        lay, host_in, vals = w.layout, [data["q"], data["k"]], [data["q"], data["k"]]
+    elif case == "ragged_bf16_b64":
+        lay = custom_layout(3, 192, 150, 64, heads=2)
+        host_in, vals = random_inputs(lay, 3)
+    else:
+        lay = custom_layout(2, 384, 300, 128, heads=3, batch=2)
+        host_in, vals = random_inputs(lay, 4)
+    x0, x1 = to_dev(host_in[0], dev), to_dev(host_in[1], dev)
+    m0, m1 = bsgm.pool_blocks2(lay, x0, x1)
+    s0, s1 = bsgm.pool_blocks(lay, x0), bsgm.pool_blocks(lay, x1)
+    torch.cuda.synchronize()
+    assert torch.equal(m0, s0) and torch.equal(m1, s1)
+    for got, v in ((m0, vals[0]), (m1, vals[1])):
+        ref = oracle.pool(v, lay)
+        np.testing.assert_allclose(got.cpu().numpy(), ref, rtol=0,
+                                   atol=2e-6 * max(1.0, np.abs(ref).max()))
+
+
 # --------------------------------------------------------------------------
 # pooled top-k selection
 # --------------------------------------------------------------------------
