@@ -373,7 +373,8 @@ def select_drift_streamed(layout, keep: Sequence[int], q, k, v, swap_rounds: int
 def select_blocks_pooled(layout, mode: int, keep: Sequence[int], qbar, kbar, cdf_tau: float = 0.9,
                          force: bool = False, row_ptr=None, col_idx=None, row_stat=None,
                          scores_out=None, workspace=None, want_stat: bool = True, stream=None):
-    """TOPK or CDF selection from block means already computed (pool_blocks of Q and K)."""
+    """TOPK or CDF selection from block means already computed (pool_blocks or pool_blocks2
+    of Q and K)."""
     n, nb, rows = _dims(layout)
     pshape = (layout.batch, layout.heads, nb, layout.head_dim)
     _expect(qbar, "qbar", torch.float32, pshape)
