@@ -363,11 +363,12 @@ def main():
         def vasc_select():
             bsgm.vasc_select_blocks(lay, keep, q, k, v, vmem, force=True, row_ptr=row_ptr,
                                     col_idx=col_idx, workspace=vws, want_stat=False)
-        vasc_ms = gpu_ms(torch, vasc_select, 10)
+        vasc_warm, vasc_reps = 10, 10
+        vasc_ms = gpu_ms(torch, vasc_select, vasc_reps, warm=vasc_warm)
         vasc_attn_ms = gpu_ms(torch, attend, 5)
         detail["vasc_selection"] = {
             "select_ms": round(vasc_ms, 4), "attn_ms": round(vasc_attn_ms, 4),
-            "layers_carried": 11, "max_pair_deficit": round(float(vmem.max()), 4),
+            "layers_carried": vasc_warm + vasc_reps, "max_pair_deficit": round(float(vmem.max()), 4),
             "executed_block_pairs": int(row_ptr[-1].item())}
         detail["other_layers"] = {
             name: side_config(bsgm, workloads, torch, dev, name, flush=flush)
@@ -478,11 +479,13 @@ def calibration_copy(torch, dev, mib: int):
     log(f"calibration copy of {mib} MiB done")
 
 
-def gpu_ms(torch, fn, reps: int) -> float:
+def gpu_ms(torch, fn, reps: int, warm: int = 10) -> float:
     """Average GPU time of fn over `reps` back-to-back launches on the current
-    stream (HIP events), after one untimed call."""
+    stream (HIP events), after `warm` untimed calls (the card's clock settles
+    over about ten calls of the larger kernels)."""
     stream = torch.cuda.current_stream()
-    fn()
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
