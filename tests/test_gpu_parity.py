@@ -433,6 +433,58 @@ def run_attention_case(dev, lay, host_in, vals, rows, label, workspace="auto"):
     return o, lse
 
 
+def sweep_case(seed):
+    """Seeded random layout for the end-to-end sweep: frames, frame length (whole
+    blocks), ragged valid length (padding under one block, as the library
+    requires), block 64 or 128, fp32 or bf16, batch, heads, per-head budgets
+    (at least the forced blocks, as the library requires), forced blocks, TOPK
+    or CDF."""
+    rng = np.random.default_rng(1000 + seed)
+    block = (64, 128)[seed % 2]
+    dtype = "f32" if seed % 3 == 0 else "bf16"
+    mode = bsgm.CDF if seed % 4 == 3 else bsgm.TOPK
+    frames = int(rng.integers(2, 11))
+    frame_len = block * int(rng.integers(1, 7))
+    frame_valid = frame_len - int(rng.integers(0, block))   # padding under a block (no empty blocks)
+    heads = int(rng.integers(1, 4))
+    batch = 1 if mode == bsgm.CDF else int(rng.integers(1, 3))
+    lay = custom_layout(frames, frame_len, frame_valid, block, heads=heads, dtype=dtype, batch=batch)
+    force = bool(rng.integers(0, 2))
+    lo = max(1, len(oracle.forced_blocks(lay, force)))   # the budget covers the forced blocks
+    keep = np.array([int(rng.integers(lo, lay.nblocks + 1)) for _ in range(heads)], dtype=np.int32)
+    tau = float(rng.uniform(0.5, 0.97))
+    return lay, mode, force, keep, tau
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_end_to_end_random_layouts(dev, seed):
+    """Selection then attention on seeded random layouts (see sweep_case): every
+    row's list is a valid answer of its rule against the oracle's pooled scores,
+    and every output row equals the oracle's attention over the GPU's own list."""
+    lay, mode, force, keep, tau = sweep_case(seed)
+    say(f"sweep seed {seed}: frames {lay.frames}x{lay.frame_len} ({lay.frame_valid} real), block "
+        f"{lay.block}, {lay.dtype}, batch {lay.batch}, heads {lay.heads}, "
+        f"{'CDF' if mode == bsgm.CDF else 'TOPK'}, keep {keep.tolist()}, force {force}")
+    host_in, vals = random_inputs(lay, 2000 + seed)
+    q, k, v = (to_dev(x, dev) for x in host_in)
+    nb = lay.nblocks
+    if mode == bsgm.TOPK:
+        scores = torch.empty((lay.batch, lay.heads, nb, nb), dtype=torch.float32, device=dev)
+        rp, ci, st = bsgm.select_blocks(lay, bsgm.TOPK, keep, q=q, k=k, force=force,
+                                        scores_out=scores)
+        torch.cuda.synchronize()
+        check_topk(lay, vals, keep, force, rp.cpu().numpy(), ci.cpu().numpy(),
+                   scores.cpu().numpy(), st.cpu().numpy())
+    else:
+        rp, ci, st = bsgm.select_blocks(lay, bsgm.CDF, keep, q=q, k=k, cdf_tau=tau, force=force)
+        torch.cuda.synchronize()
+        check_cdf(lay, vals, keep, tau, force, rp.cpu().numpy(), ci.cpu().numpy(),
+                  st.cpu().numpy())
+    rows = parity.csr_rows(rp.cpu().numpy(), ci.cpu().numpy())
+    run_attention_case(dev, lay, host_in, vals, rows, f"sweep seed {seed}",
+                       workspace="auto" if seed % 2 == 0 else None)
+
+
 def test_binding_rejects_bad_buffers(dev):
     """Host, mistyped or misshaped buffers are refused before anything is enqueued."""
     w, data = preset(0)
