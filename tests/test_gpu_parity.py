@@ -1587,6 +1587,78 @@ def test_drift_streamed_layer16(dev, rounds, track_best, force):
     assert torch.equal(st.view(torch.int32), st2.view(torch.int32))
 
 
+DRIFT_SWEEP_RULES = ("best-swap dropped sum", "best-swap renormalised", "re-rank", "streamed re-rank")
+
+
+def drift_sweep_case(seed):
+    """Seeded random layout and rule for the drift sweep: frames, frame length
+    (whole blocks), padding under one block, block 64 or 128, fp32 or bf16,
+    heads, batch (the re-rank rules), budgets covering the forced blocks,
+    rounds, track-best."""
+    rng = np.random.default_rng(3000 + seed)
+    rule = seed % 4
+    block = (64, 128)[(seed // 4) % 2]
+    dtype = "f32" if seed % 3 == 0 else "bf16"
+    frames = int(rng.integers(2, 9))
+    frame_len = block * int(rng.integers(1, 6))
+    frame_valid = frame_len - int(rng.integers(0, block))
+    heads = int(rng.integers(1, 3))
+    batch = 1 if rule < 2 else int(rng.integers(1, 3))
+    lay = custom_layout(frames, frame_len, frame_valid, block, heads=heads, dtype=dtype, batch=batch)
+    force = bool(rng.integers(0, 2))
+    nb = lay.nblocks
+    lo = max(1, len(oracle.forced_blocks(lay, force)))
+    keep = np.array([int(rng.integers(lo, max(lo, nb - 1) + 1)) for _ in range(heads)],
+                    dtype=np.int32)
+    rounds = int(rng.integers(0, 5)) if rule < 2 else int(rng.integers(0, 7))
+    track_best = bool(rng.integers(0, 2))
+    return lay, rule, force, keep, rounds, track_best
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_drift_random_layouts(dev, seed):
+    """Drift selection on seeded random layouts (see drift_sweep_case), each
+    rule in turn: every row's contributions against the oracle's, and its list
+    replayed under the rule on the oracle's contributions; then attention over
+    the selected lists against the oracle on every row."""
+    lay, rule, force, keep, rounds, track_best = drift_sweep_case(seed)
+    nb = lay.nblocks
+    label = (f"drift sweep seed {seed}: {DRIFT_SWEEP_RULES[rule]}, frames {lay.frames}x"
+             f"{lay.frame_len} ({lay.frame_valid} real), block {lay.block}, {lay.dtype}, batch "
+             f"{lay.batch}, heads {lay.heads}, keep {keep.tolist()}, rounds {rounds}, "
+             f"track-best {track_best}, force {force}")
+    say(label)
+    host, vals = random_inputs(lay, 4000 + seed)
+    q, k, v = (to_dev(x, dev) for x in host)
+    if rule < 2:
+        renorm = rule == 1
+        zmass = (torch.full((1, lay.heads, nb, nb), -1.0, dtype=torch.float32, device=dev)
+                 if renorm else None)
+        contrib, score = bsgm.drift_scores(lay, q, k, v, zmass=zmass)
+        log = torch.full((lay.heads * nb, max(rounds, 1), 2), -7, dtype=torch.int32, device=dev)
+        rp, ci, st = bsgm.select_blocks(
+            lay, bsgm.DRIFT, keep, contrib=contrib, swap_rounds=rounds, force=force, swap_log=log,
+            objective=bsgm.RENORMALISED if renorm else bsgm.DROPPED_SUM, zmass=zmass)
+        torch.cuda.synchronize()
+        rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+        parity.check_csr_wellformed(rpn, cin, nb)
+        rows = [(h, i) for h in range(lay.heads) for i in range(nb)]
+        check_drift(lay, vals, keep, rounds, force, contrib.cpu().numpy(), score.cpu().numpy(),
+                    rpn, cin, st.cpu().numpy(), log.cpu().numpy(), rows,
+                    objective=oracle.RENORM if renorm else oracle.RAW,
+                    zmass_g=zmass.cpu().numpy() if renorm else None)
+    else:
+        rows = [(b, h, i) for b in range(lay.batch) for h in range(lay.heads) for i in range(nb)]
+        if rule == 2:
+            rp, ci = run_rerank(dev, lay, host, vals, keep, rounds, track_best, force, rows, label)
+        else:
+            rp, ci, _, _ = run_streamed(dev, lay, host, vals, keep, rounds, track_best, force,
+                                        rows, label, min_same=0.5)
+        rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    run_attention_case(dev, lay, host, vals, parity.csr_rows(rpn, cin), f"drift sweep seed {seed}",
+                       workspace="auto" if seed % 2 == 0 else None)
+
+
 def test_drift_streamed_more_kept_than_dropped(dev):
     """Keep 120 of 176 blocks (more kept than dropped, so the rounds sum the
     dropped blocks directly rather than the total minus the kept ones), with a
