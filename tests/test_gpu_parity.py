@@ -1919,6 +1919,32 @@ def test_vasc_small_layouts_three_layers(dev, dtype, block, force):
     run_vasc_layers(dev, lay, host, vals, keep, force, 3, label="small")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_vasc_random_layouts(dev, seed):
+    """Value-aware selection with pair memory on seeded random layouts (frames,
+    frame length in whole blocks, padding under one block, block 64 or 128,
+    fp32 or bf16, batch, heads, budgets covering the forced blocks, odd and
+    even block counts), two to four layers carrying the memory: every row and
+    every pair against the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    block = (64, 128)[seed % 2]
+    dtype = "f32" if seed % 3 == 0 else "bf16"
+    frames = int(rng.integers(2, 9))
+    frame_len = block * int(rng.integers(1, 6))
+    lay = custom_layout(frames, frame_len, frame_len - int(rng.integers(0, block)), block,
+                        heads=int(rng.integers(1, 3)), dtype=dtype, batch=int(rng.integers(1, 3)))
+    force = bool(rng.integers(0, 2))
+    lo = max(1, len(oracle.forced_blocks(lay, force)))
+    keep = np.array([int(rng.integers(lo, max(lo, lay.nblocks - 1) + 1))
+                     for _ in range(lay.heads)], dtype=np.int32)
+    layers = int(rng.integers(2, 5))
+    say(f"vasc sweep seed {seed}: frames {lay.frames}x{lay.frame_len} ({lay.frame_valid} real), "
+        f"block {block}, {dtype}, batch {lay.batch}, heads {lay.heads}, nb {lay.nblocks}, "
+        f"keep {keep.tolist()}, force {force}, layers {layers}")
+    host, vals = random_inputs(lay, 6000 + seed)
+    run_vasc_layers(dev, lay, host, vals, keep, force, layers, label=f"sweep seed {seed}")
+
+
 def test_vasc_layer32_full_size_sampled(dev):
     """The 32-frame layer (16 heads, 352 blocks, 88 kept with the 32 forced
     special blocks): two layers, sampled rows, every pair's memory."""
